@@ -1,0 +1,339 @@
+"""Benchmark of the PQ2_0 ternary GEMM path on one MI355X.
+
+A step is one pass of the hot path over one batch: pq2_quantize_act on the
+activations, then pq2_gemm against the next weight matrix of a rotating set
+(the set is larger than the 256 MB Infinity Cache, so weights stream from
+HBM). Inputs are resident in HBM before the timed region starts.
+
+Default workload: decode GEMV, M = 1, N = 5120, K = 6144, 64 rotating
+matrices. ``--workload`` selects another configuration; ``--sweep`` prints
+one line per configuration (small-batch, prefill, 64-layer decode step).
+
+Printed JSON line: metric/value/unit (algorithmic HBM GB/s of the whole step,
+or int8 TOP/s for prefill), the roofline of the dominant kernel measured with
+HIP events around each of its launches, and the CPU oracle timed on a bounded
+sample of the same workload on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published
+GROUP = 128
+METRIC = "PQ2 GEMM: HBM GB/s (% peak) at M=1..16; int8 TOPS (% peak) prefill"
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def gemm_bytes(M, N, K):
+    """codes + fp16 group scales + plane-order q + s and t + y (float32)."""
+    G = K // GROUP
+    return N * K // 4 + 2 * N * G + M * K + 8 * M * G + 4 * M * N
+
+
+def quant_bytes(M, K):
+    G = K // GROUP
+    return 4 * M * K + M * K + 8 * M * G
+
+
+def gemm_ops(M, N, K):
+    return 2 * M * N * K
+
+
+# ---------------------------------------------------------------- workloads
+
+def workload_list():
+    import pq2_synth as synth
+    out = {"decode": ("gemm", synth.decode_gemv())}
+    for m in synth.SMALL_MS:
+        for n, k in synth.SMALL_SHAPES:
+            w = synth.small_batch(m, n, k)
+            out[w.name] = ("gemm", w)
+    for m in synth.PREFILL_MS:
+        for n, k in synth.PREFILL_SHAPES:
+            w = synth.prefill(m, n, k)
+            out[w.name] = ("gemm", w)
+    for m in (1, 16):
+        out[f"layer64_m{m}"] = ("layers", m)
+    return out
+
+
+def make_weight_set(wl, torch, dev):
+    """Rotating set of distinct matrices, generated on the host (numpy PCG64)."""
+    import pq2_synth as synth
+    codes, scales = [], []
+    for i in range(wl.rotate):
+        w = synth.weights(wl.n, wl.k, synth.matrix_seed(i), wl.probs)
+        codes.append(torch.from_numpy(w.codes).to(dev))
+        scales.append(torch.from_numpy(w.wscale_bits.view(np.int16)).to(dev))
+    return codes, scales
+
+
+def make_layer_set(torch, dev, n_layers, gen):
+    """64 synthetic layers x 5 projections; generated on the device from a seeded
+    torch generator (5.6 GB of packed weights would take minutes with numpy).
+    Each packed byte is one of the 81 bytes whose four 2-bit fields are codes
+    0..2, drawn uniformly, i.e. four iid uniform codes."""
+    import pq2_synth as synth
+    table = torch.from_numpy(synth._VALID_BYTES).to(dev)
+    layers = []
+    for _ in range(n_layers):
+        projs = []
+        for (n, k) in synth.LAYER_SHAPES:
+            idx = torch.randint(0, 81, (n, k // 4), generator=gen, device=dev)
+            codes = table[idx]
+            ws = (torch.rand((n, k // GROUP), generator=gen, device=dev) * 0.09 + 0.01)
+            projs.append((codes, ws.to(torch.float16).view(torch.int16), n, k))
+        layers.append(projs)
+    return layers
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, budget_s=10.0):
+    """The oracle (as is) on a bounded sample of the workload, all host cores."""
+    import oracle
+    import pq2_synth as synth
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    x = synth.activations(wl.m, wl.k, 0, wl.outlier_frac)
+    n_mats = min(wl.rotate, 4)
+    mats = [synth.weights(wl.n, wl.k, synth.matrix_seed(i), wl.probs) for i in range(n_mats)]
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        w = mats[calls % n_mats]
+        oracle.forward(x, w.codes, w.wscale, threads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_call = el / calls
+    step_bytes = gemm_bytes(wl.m, wl.n, wl.k) + quant_bytes(wl.m, wl.k)
+    return {
+        "value": step_bytes / per_call / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{calls} full calls (quantise + all {wl.m}x{wl.n} outputs) over {n_mats} "
+                  f"of the workload's matrices, {el:.1f} s, {per_call * 1e3:.1f} ms/call",
+    }
+
+
+def cpu_baseline_prefill(wl, budget_s=10.0):
+    import oracle
+    import pq2_synth as synth
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    x = synth.activations(wl.m, wl.k, 0)
+    w = synth.weights(wl.n, wl.k, synth.matrix_seed(0), wl.probs)
+    q, s, t = oracle.quantize(x)
+    rng = np.random.default_rng(0)
+    P = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        mm = rng.integers(0, wl.m, 4096)
+        nn = rng.integers(0, wl.n, 4096)
+        oracle.gemm_f64_sampled(q, s, w.codes, w.wscale, mm, nn, threads=threads)
+        P += 4096
+    el = time.perf_counter() - t0
+    return {"value": 2 * P * wl.k / el / 1e12, "unit": "TOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{P} sampled outputs of the {wl.m}x{wl.n} product, {el:.1f} s"}
+
+
+# ---------------------------------------------------------------- GPU timing
+
+def traffic_record(kernel_tag):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    rec = json.load(open(path))
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_gemm(args, wl, torch, pq2):
+    dev = torch.device("cuda:0")
+    import pq2_synth as synth
+    codes, scales = make_weight_set(wl, torch, dev)
+    x = torch.from_numpy(synth.activations(wl.m, wl.k, 0, wl.outlier_frac)).to(dev)
+    M, N, K = wl.m, wl.n, wl.k
+    G = K // GROUP
+    q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s = torch.empty((M, G), dtype=torch.float32, device=dev)
+    t = torch.empty((M, G), dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    R = len(codes)
+
+    def step(i):
+        pq2.pq2_quantize_act(x, q, s, t)
+        pq2.pq2_gemm(q, s, t, codes[i % R], scales[i % R], y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record()
+    for i in range(args.steps):
+        pq2.pq2_quantize_act(x, q, s, t)
+        ev[i][0].record()
+        pq2.pq2_gemm(q, s, t, codes[i % R], scales[i % R], y)
+        ev[i][1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_step = total_ms / args.steps
+    return dict(ms_step=ms_step, gemm_ms=gemm_ms, wall=wall, M=M, N=N, K=K)
+
+
+def report_gemm(args, wl, r, torch):
+    M, N, K = r["M"], r["N"], r["K"]
+    step_bytes = gemm_bytes(M, N, K) + quant_bytes(M, K)
+    prefill = M > 16
+    path = "gemv_m1" if M == 1 else ("small_mfma" if M <= 16 else "prefill_mfma")
+    if prefill:
+        value = gemm_ops(M, N, K) / (r["ms_step"] * 1e-3) / 1e12
+        unit = "TOP/s"
+        achieved = gemm_ops(M, N, K) / (r["gemm_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOP/s",
+                "frac": achieved / I8_PEAK_TOPS}
+    else:
+        value = step_bytes / (r["ms_step"] * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = gemm_bytes(M, N, K) / (r["gemm_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    roof["kernel"] = path
+    roof["kernel_us"] = r["gemm_ms"] * 1e3
+    roof["traffic"] = traffic_record(f"{path}_{wl.name}")
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "N": N, "K": K, "rotating_matrices": wl.rotate,
+                   "step": "pq2_quantize_act + pq2_gemm",
+                   "algorithmic_bytes_per_step": step_bytes,
+                   "gemm_bytes_per_call": gemm_bytes(M, N, K),
+                   "gemm_int_ops_per_call": gemm_ops(M, N, K)},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = (cpu_baseline_prefill(wl, args.cpu_seconds) if prefill
+                                else cpu_baseline(wl, args.cpu_seconds))
+    return line
+
+
+def run_layers(args, m, torch, pq2):
+    """64-layer synthetic decode step: 5 PQ2_0 projections per layer, back to back."""
+    import pq2_synth as synth
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    layers = make_layer_set(torch, dev, synth.N_LAYERS, gen)
+    xs = {}
+    bufs = {}
+    for (n, k) in synth.LAYER_SHAPES:
+        if k not in xs:
+            xs[k] = torch.from_numpy(synth.activations(m, k, 0)).to(dev)
+            bufs[k] = (torch.empty((m, k), dtype=torch.int8, device=dev),
+                       torch.empty((m, k // GROUP), dtype=torch.float32, device=dev),
+                       torch.empty((m, k // GROUP), dtype=torch.int32, device=dev))
+    ys = {n: torch.empty((m, n), dtype=torch.float32, device=dev) for (n, _) in synth.LAYER_SHAPES}
+
+    def step():
+        for projs in layers:
+            for (codes, ws, n, k) in projs:
+                q, s, t = bufs[k]
+                pq2.pq2_quantize_act(xs[k], q, s, t)
+                pq2.pq2_gemm(q, s, t, codes, ws, ys[n])
+
+    for _ in range(max(1, args.warmup // 10)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 10)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    total = 0
+    for (n, k) in synth.LAYER_SHAPES:
+        total += gemm_bytes(m, n, k) + quant_bytes(m, k)
+    total *= synth.N_LAYERS
+    gbs = total / (ms * 1e-3) / 1e9
+    return {"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps,
+            "warmup": max(1, args.warmup // 10), "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+            "config": {"workload": f"layer64_m{m}", "M": m, "layers": synth.N_LAYERS,
+                       "gemms_per_step": 5 * synth.N_LAYERS,
+                       "algorithmic_bytes_per_step": total},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "note": "whole step incl. launch gaps (stream time)"}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--sweep", action="store_true", help="one line per configuration")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the PQ2_0 path is measured on a "
+              "single MI355X (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import gemm_pq2_w2a8_amd as pq2
+
+    wls = workload_list()
+    names = list(wls) if args.sweep else [args.workload]
+    for name in names:
+        kind, wl = wls[name]
+        print(f"# running {name}", file=sys.stderr, flush=True)
+        if kind == "gemm":
+            r = run_gemm(args, wl, torch, pq2)
+            line = report_gemm(args, wl, r, torch)
+        else:
+            line = run_layers(args, wl, torch, pq2)
+        print(json.dumps(line), flush=True)
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

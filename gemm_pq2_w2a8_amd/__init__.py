@@ -1,0 +1,156 @@
+"""Thin Python binding of the PQ2_0 C ABI (include/pq2.h), for PyTorch tensors.
+
+Argument marshalling only: tensors are checked for dtype, shape, device and
+contiguity, their device pointers and the current HIP stream are passed to
+``libpq2.so``, and a non-zero status raises :class:`PQ2Error`. Every step of
+the computation runs in the library's gfx950 kernels; there is no fallback.
+Importing this package raises if ``libpq2.so`` has not been built
+(``python -m gemm_pq2_w2a8_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpq2.so")
+
+GROUP = 128
+PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_PREFILL = 0, 1, 2, 3
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gemm_pq2_w2a8_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+lib.pq2_abi_version.restype = ctypes.c_int
+lib.pq2_abi_version.argtypes = []
+lib.pq2_status_str.restype = ctypes.c_char_p
+lib.pq2_status_str.argtypes = [ctypes.c_int]
+lib.pq2_quantize_act.restype = ctypes.c_int
+lib.pq2_quantize_act.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+lib.pq2_gemm.restype = ctypes.c_int
+lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.pq2_gemm_group_dots.restype = ctypes.c_int
+lib.pq2_gemm_group_dots.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
+
+# Every extern "C" symbol declared in include/pq2.h.
+ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_gemm",
+               "pq2_gemm_group_dots")
+
+
+class PQ2Error(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(lib.pq2_status_str(status).decode())
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise PQ2Error(status)
+
+
+def abi_version() -> int:
+    return int(lib.pq2_abi_version())
+
+
+def _stream(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mk(x: torch.Tensor) -> Tuple[int, int]:
+    if x.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def pq2_quantize_act(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, t: torch.Tensor,
+                     stream=None) -> None:
+    """x float32 [M][K] -> q int8 [M][K] (plane order), s float32 [M][G], t int32 [M][G]."""
+    M, K = _mk(x)
+    G = K // GROUP
+    _need(x, "x", torch.float32, (M, K))
+    _need(q, "q", torch.int8, (M, K))
+    _need(s, "s", torch.float32, (M, G))
+    _need(t, "t", torch.int32, (M, G))
+    _check(lib.pq2_quantize_act(x.data_ptr(), q.data_ptr(), s.data_ptr(), t.data_ptr(), M, K,
+                                _stream(x, stream)))
+
+
+def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
+             wscale: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """y float32 [M][N] = PQ2_0 product of plane-order q/s/t and codes/wscale."""
+    M, K = _mk(q)
+    N = int(codes.shape[0])
+    G = K // GROUP
+    _need(q, "q", torch.int8, (M, K))
+    _need(s, "s", torch.float32, (M, G))
+    _need(t, "t", torch.int32, (M, G))
+    _need(codes, "codes", torch.uint8, (N, K // 4))
+    if wscale.dtype == torch.float16:
+        wscale = wscale.view(torch.int16)
+    _need(wscale, "wscale", torch.int16, (N, G))
+    _need(y, "y", torch.float32, (M, N))
+    _check(lib.pq2_gemm(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
+                        wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
+
+
+def pq2_gemm_group_dots(q: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
+                        d: torch.Tensor, path: int = PATH_AUTO, stream=None) -> None:
+    """d int32 [M][N][G] = exact group dots through the selected kernel path."""
+    M, K = _mk(q)
+    N = int(codes.shape[0])
+    G = K // GROUP
+    _need(q, "q", torch.int8, (M, K))
+    _need(t, "t", torch.int32, (M, G))
+    _need(codes, "codes", torch.uint8, (N, K // 4))
+    _need(d, "d", torch.int32, (M, N, G))
+    _check(lib.pq2_gemm_group_dots(q.data_ptr(), t.data_ptr(), codes.data_ptr(), d.data_ptr(),
+                                   M, N, K, int(path), _stream(q, stream)))
+
+
+# ---------------------------------------------------------------- allocating helpers
+
+def quantize_act(x: torch.Tensor, stream=None):
+    """Allocate q/s/t with torch and run pq2_quantize_act."""
+    M, K = _mk(x)
+    G = K // GROUP
+    q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    t = torch.empty((M, G), dtype=torch.int32, device=x.device)
+    pq2_quantize_act(x, q, s, t, stream)
+    return q, s, t
+
+
+def linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor,
+           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Whole path: quantise x, then the PQ2_0 product; returns y float32 [M][N]."""
+    q, s, t = quantize_act(x, stream)
+    M = int(x.shape[0])
+    N = int(codes.shape[0])
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    pq2_gemm(q, s, t, codes, wscale, y, stream)
+    return y

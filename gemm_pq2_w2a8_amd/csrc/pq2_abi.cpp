@@ -1,0 +1,100 @@
+// pq2_abi.cpp -- the C ABI declared in include/pq2.h: host-side argument
+// validation and dispatch to the gfx950 kernels. Validation happens before
+// anything is enqueued; the library keeps no mutable state.
+#include "../../include/pq2.h"
+
+#include <hip/hip_runtime.h>
+
+#include "pq2_launch.hpp"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+pq2_status check_mnk(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || K < PQ2_GROUP || K % PQ2_GROUP != 0) return PQ2_ERR_SHAPE;
+    if (M > PQ2_MAX_DIM || N > PQ2_MAX_DIM || K > PQ2_MAX_DIM) return PQ2_ERR_SHAPE;
+    return PQ2_OK;
+}
+
+pq2_status from_hip(hipError_t e) { return e == hipSuccess ? PQ2_OK : PQ2_ERR_HIP; }
+
+pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *codes,
+                    const pq2::GemmOut &out, int64_t M, int64_t N, int64_t K,
+                    hipStream_t stream) {
+    switch (path) {
+        case PQ2_PATH_GEMV:
+            return from_hip(pq2::launch_gemv_m1(q, t, codes, out, N, K, stream));
+        case PQ2_PATH_SMALL:
+            return from_hip(pq2::launch_small(q, t, codes, out, M, N, K, stream));
+        case PQ2_PATH_PREFILL:
+            return from_hip(pq2::launch_prefill(q, t, codes, out, M, N, K, stream));
+        default:
+            return PQ2_ERR_ARG;
+    }
+}
+
+int auto_path(int64_t M) {
+    if (M == 1) return PQ2_PATH_GEMV;
+    if (M <= 16) return PQ2_PATH_SMALL;
+    return PQ2_PATH_PREFILL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pq2_abi_version(void) { return PQ2_ABI_VERSION; }
+
+const char *pq2_status_str(int status) {
+    switch (status) {
+        case PQ2_OK: return "PQ2_OK";
+        case PQ2_ERR_NULL: return "PQ2_ERR_NULL: a required pointer is NULL";
+        case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128";
+        case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
+        case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
+        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M";
+        default: return "PQ2 unknown status";
+    }
+}
+
+pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t, int64_t M,
+                            int64_t K, void *hip_stream) {
+    if (!x || !q || !s || !t) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, 1, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(t, 4))
+        return PQ2_ERR_ALIGN;
+    return from_hip(pq2::launch_quantize(x, q, s, t, M, K, static_cast<hipStream_t>(hip_stream)));
+}
+
+pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
+                    const uint16_t *wscale, float *y, int64_t M, int64_t N, int64_t K,
+                    void *hip_stream) {
+    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, N, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
+        !aligned(wscale, 2) || !aligned(y, 4))
+        return PQ2_ERR_ALIGN;
+    const pq2::GemmOut out{y, nullptr, s, wscale};
+    return run_path(auto_path(M), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+}
+
+pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                               int32_t *d, int64_t M, int64_t N, int64_t K, int path,
+                               void *hip_stream) {
+    if (!q || !t || !codes || !d) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, N, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(t, 4) || !aligned(d, 4))
+        return PQ2_ERR_ALIGN;
+    if (path == PQ2_PATH_AUTO) path = auto_path(M);
+    if (path == PQ2_PATH_GEMV && M != 1) return PQ2_ERR_ARG;
+    if (path == PQ2_PATH_SMALL && M > 16) return PQ2_ERR_ARG;
+    if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PREFILL) return PQ2_ERR_ARG;
+    const pq2::GemmOut out{nullptr, d, nullptr, nullptr};
+    return run_path(path, q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// pq2_launch.hpp -- host-side launchers of the PQ2_0 kernels. Arguments are
+// validated by the C ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pq2 {
+
+// Epilogue of a GEMM launch: the float32 scale epilogue into y, or the exact
+// int32 group dots into d (test and diagnostic path).
+struct GemmOut {
+    float *y;        // [M][N] or nullptr
+    int32_t *d;      // [M][N][G] or nullptr
+    const float *s;  // [M][G], unused when d is set
+    const uint16_t *ws;  // [N][G], unused when d is set
+};
+
+hipError_t launch_quantize(const float *x, int8_t *q, float *s, int32_t *t, int64_t M,
+                           int64_t K, hipStream_t stream);
+
+hipError_t launch_gemv_m1(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                          const GemmOut &out, int64_t N, int64_t K, hipStream_t stream);
+
+hipError_t launch_small(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                        const GemmOut &out, int64_t M, int64_t N, int64_t K,
+                        hipStream_t stream);
+
+hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                          const GemmOut &out, int64_t M, int64_t N, int64_t K,
+                          hipStream_t stream);
+
+}  // namespace pq2

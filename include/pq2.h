@@ -1,0 +1,126 @@
+/*
+ * pq2.h -- C ABI of the PQ2_0 ternary-weight x int8-activation GEMM for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Making a ternary reasoning model fast in vLLM -- from
+ * CUDA to Triton and Gluon", section "One token at a time: plain Triton is
+ * enough"; per-call buffers from section "Prompt processing: check
+ * configuration and launch costs"):
+ *
+ *   x float32 [M][K]  --pq2_quantize_act-->  q int8 [M][K] (plane order),
+ *                                            s float32 [M][G], t int32 [M][G]
+ *   q, s, t + codes + wscale  --pq2_gemm-->  y float32 [M][N]
+ *
+ *   y[m][n] = sum_g  s[m][g] * wscale[n][g] * D[m][n][g]
+ *   D[m][n][g] = sum_{k in group g} code[n][k] * q[m][k]  -  t[m][g]
+ *              = sum_{k in group g} (code[n][k] - 1) * q[m][k]
+ *
+ * G = K / 128. All arrays are dense and row-major, in device memory, owned
+ * by the caller. The library never allocates, frees or synchronises; every
+ * call only enqueues kernels on the given stream (NULL = the null stream).
+ * Inputs must not overlap outputs. Calls are thread-safe: the library keeps
+ * no mutable global state.
+ *
+ * LAYOUTS (fixed):
+ *  codes   uint8 [N][K/4]. The 2-bit code of weight k of row n (code c means
+ *          the weight c-1; codes are 0, 1, 2) sits in byte n*K/4 + k/4 at
+ *          bits 2*(k%4) .. 2*(k%4)+1. Viewed as little-endian 32-bit words,
+ *          group g of a row is words 8g .. 8g+7. Base 16-byte aligned.
+ *  wscale  IEEE binary16 bit patterns [N][G], one scale per (row, group).
+ *          Base 2-byte aligned.
+ *  x       float32 [M][K]. Base 16-byte aligned.
+ *  q       int8 [M][K] in plane order: inside group g (bytes 128g..128g+127
+ *          of a row), the activation of weight 4*b+s (b = 0..31, s = 0..3)
+ *          is stored at byte 128g + 32*s + b. Base 16-byte aligned.
+ *  s       float32 [M][G]; t int32 [M][G]. Base 4-byte aligned.
+ *  y       float32 [M][N], overwritten. Base 4-byte aligned.
+ *
+ * ERRORS: arguments are validated on the host before anything is enqueued:
+ *  PQ2_ERR_NULL  a required pointer is NULL;
+ *  PQ2_ERR_SHAPE M < 1, N < 1, K < 128, K % 128 != 0, or a dimension above
+ *                PQ2_MAX_DIM;
+ *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above;
+ *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots);
+ *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
+ * Nothing is enqueued when a status other than PQ2_OK is returned, except for
+ * PQ2_ERR_HIP. A fault during execution surfaces at the caller's next
+ * synchronisation, as for any HIP kernel. No C++ exception crosses the ABI.
+ */
+#ifndef PQ2_H
+#define PQ2_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQ2_ABI_VERSION 1
+#define PQ2_GROUP 128
+#define PQ2_MAX_DIM (1LL << 30)
+
+typedef enum {
+    PQ2_OK = 0,
+    PQ2_ERR_NULL = 1,
+    PQ2_ERR_SHAPE = 2,
+    PQ2_ERR_ALIGN = 3,
+    PQ2_ERR_HIP = 4,
+    PQ2_ERR_ARG = 5
+} pq2_status;
+
+/* Kernel path selectors for pq2_gemm_group_dots. */
+enum {
+    PQ2_PATH_AUTO = 0,      /* same choice as pq2_gemm */
+    PQ2_PATH_GEMV = 1,      /* M == 1 only: the v_dot4 GEMV */
+    PQ2_PATH_SMALL = 2,     /* M <= 16 only: the small-batch MFMA kernel */
+    PQ2_PATH_PREFILL = 3    /* any M: the tiled MFMA GEMM */
+};
+
+/* Returns PQ2_ABI_VERSION of the loaded library. */
+int pq2_abi_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+const char *pq2_status_str(int status);
+
+/*
+ * Per-128-group int8 quantisation of activations, fused with the plane-order
+ * permutation (page 1, sections "One token at a time" for the layout and
+ * "Prompt processing" for the q/s/t buffers). For each row m and group g:
+ *   amax = max |x|;  s = amax / 127 (float32, correctly rounded division);
+ *   q = clamp(round_half_even(x / s), -127, 127) (float32 division);
+ *   t = sum of the group's q.   A group with s == 0 gets q = 0, t = 0.
+ * x must be finite. Writes q (plane order), s and t.
+ */
+pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
+                            int64_t M, int64_t K, void *hip_stream);
+
+/*
+ * y = the PQ2_0 product defined above. The kernel depends on M:
+ *   M == 1        -> GEMV streaming code words into v_dot4 (2-bit planes
+ *                    masked out of each 32-bit word, no decode step);
+ *   2 <= M <= 16  -> small-batch kernel on int8 MFMA, tokens padded to 16;
+ *   M >= 17       -> tiled int8 MFMA GEMM (prefill).
+ * Group dots are exact int32; the float32 epilogue sums the G terms in an
+ * order that differs from a sequential sum only by float32 rounding.
+ */
+pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
+                    const uint8_t *codes, const uint16_t *wscale, float *y,
+                    int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/*
+ * Test and diagnostic entry: runs the main loop of the selected kernel path
+ * but stores the exact per-group dots instead of the float epilogue:
+ *   d int32 [M][N][G],  d[m][n][g] = D[m][n][g] as defined above.
+ * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M == 1 and
+ * PQ2_PATH_SMALL requires M <= 16 (else PQ2_ERR_ARG).
+ */
+pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t,
+                               const uint8_t *codes, int32_t *d,
+                               int64_t M, int64_t N, int64_t K,
+                               int path, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ2_H */

@@ -1,0 +1,89 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pq2.h")
+
+pq2 = pytest.importorskip("gemm_pq2_w2a8_amd")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_HIP, ERR_ARG = 0, 1, 2, 3, 4, 5
+P = 0x100000  # a fake, 256-byte-aligned non-null address; never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pq2_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert set(names) == set(pq2.ABI_SYMBOLS)
+    for name in names:
+        assert hasattr(pq2.lib, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define\s+PQ2_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert pq2.abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for st in range(6):
+        s = pq2.lib.pq2_status_str(st)
+        assert s and s.startswith(b"PQ2_")
+    assert pq2.lib.pq2_status_str(99)
+
+
+def test_quantize_validation():
+    f = pq2.lib.pq2_quantize_act
+    assert f(None, P, P, P, 1, 128, None) == ERR_NULL
+    assert f(P, P, P, None, 1, 128, None) == ERR_NULL
+    assert f(P, P, P, P, 0, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, 64, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, 200, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, -128, None) == ERR_SHAPE
+    assert f(P, P, P, P, (1 << 30) + 1, 128, None) == ERR_SHAPE
+    assert f(P + 4, P, P, P, 1, 128, None) == ERR_ALIGN     # x needs 16 B
+    assert f(P, P + 8, P, P, 1, 128, None) == ERR_ALIGN     # q needs 16 B
+    assert f(P, P, P + 2, P, 1, 128, None) == ERR_ALIGN     # s needs 4 B
+    assert f(P, P, P, P + 1, 1, 128, None) == ERR_ALIGN     # t needs 4 B
+
+
+def test_gemm_validation():
+    f = pq2.lib.pq2_gemm
+    assert f(None, P, P, P, P, P, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, None, P, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 0, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 0, 8, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
+    assert f(P, P, P, P, P + 1, P, 1, 8, 128, None) == ERR_ALIGN   # wscale needs 2 B
+    assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
+
+
+def test_group_dots_validation():
+    f = pq2.lib.pq2_gemm_group_dots
+    assert f(P, P, P, None, 1, 8, 128, 0, None) == ERR_NULL
+    assert f(P, P, P, P, 1, 8, 100, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, 2, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG
+    assert f(P, P, P, P, 17, 8, 128, pq2.PATH_SMALL, None) == ERR_ARG
+    assert f(P, P, P, P, 1, 8, 128, 7, None) == ERR_ARG
+    assert f(P, P, P, P, 1, 8, 128, -1, None) == ERR_ARG
+    assert f(P, P, P + 8, P, 1, 8, 128, 0, None) == ERR_ALIGN   # codes needs 16 B
+    assert f(P + 8, P, P, P, 1, 8, 128, 0, None) == ERR_ALIGN   # q needs 16 B
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 128)
+    with pytest.raises(ValueError):
+        pq2.quantize_act(x)

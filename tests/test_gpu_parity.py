@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Integer work (q, s bits, t, per-group dots) must match bit for bit. The float32
+output y must satisfy max |y - y*| / sum_g |term_g| < 1e-5, with y* the
+oracle's float64 result; with unit or one-hot scales every partial sum is an
+integer below 2^24, so y must then match exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pq2_synth as synth
+
+pytestmark = pytest.mark.gpu
+
+G = 128
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def pq2():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gemm_pq2_w2a8_amd as lib   # raises if libpq2.so is missing
+    return lib
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def plane(q):
+    """Natural -> plane order (position 32*s+b <- element 4*b+s), numpy reshape."""
+    M, K = q.shape
+    return np.ascontiguousarray(q.reshape(M, K // G, 32, 4).transpose(0, 1, 3, 2).reshape(M, K))
+
+
+def rand_q(M, K, rng):
+    q = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    t = q.reshape(M, -1, G).astype(np.int32).sum(-1).astype(np.int32)
+    return q, t
+
+
+def gpu_dots(pq2, qn, t, codes, path):
+    M, K = qn.shape
+    N = codes.shape[0]
+    d = torch.empty((M, N, K // G), dtype=torch.int32, device="cuda")
+    pq2.pq2_gemm_group_dots(dev(plane(qn)), dev(t), dev(codes), d, path=path)
+    return host(d)
+
+
+def gpu_gemm(pq2, qp, s, t, codes, ws):
+    M = qp.shape[0]
+    N = codes.shape[0]
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(dev(qp), dev(s), dev(t), dev(codes), dev(ws.view(np.int16)), y)
+    return host(y)
+
+
+# ---------------------------------------------------------------- K1 quantise
+
+def edge_rows():
+    x = np.zeros((4, 640), np.float32)
+    x[0, 0:10] = [0.5, 1.5, 2.5, -2.5, 126.5, -0.5, 3.5, 127.0, -126.5, 0.49999997]   # s = 1
+    x[0, 128] = 1.4e-45                      # underflowing scale -> zeros
+    x[0, 256:384] = np.float32(3e-39)        # subnormal scale
+    x[0, 300] = -np.float32(1e-39)
+    sv = 1070.0 / 1024.0                     # division vs reciprocal ties
+    x[1, 0] = 127 * sv
+    x[1, 1:128] = ((np.arange(127) + 0.5) * sv).astype(np.float32)
+    x[1, 128:256] = -x[1, 0:128]
+    x[2, :] = np.float32(3.0e38) * np.sign(np.sin(np.arange(640)))
+    x[3, 128:256] = 1e-20 * np.arange(128, dtype=np.float32)
+    return x
+
+
+QUANT_CASES = {
+    "tiny": lambda: synth.activations(1, 512, 0),
+    "decode": lambda: synth.activations(1, 6144, 0),
+    "small_outliers": lambda: synth.activations(16, 17408, 0, outlier_frac=0.01),
+    "ragged": lambda: synth.activations(3, 640, 5, outlier_frac=0.01),
+    "prefill": lambda: synth.activations(4096, 5120, 0),
+    "edge": edge_rows,
+}
+
+
+@pytest.mark.parametrize("case", list(QUANT_CASES))
+def test_quantize_bitexact(pq2, case):
+    x = QUANT_CASES[case]()
+    print(f"quantize case={case} shape={x.shape}", flush=True)
+    q, s, t = pq2.quantize_act(dev(x))
+    qo, so, to = oracle.quantize(x)
+    np.testing.assert_array_equal(host(q), oracle.plane_order(qo))
+    np.testing.assert_array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    np.testing.assert_array_equal(host(t), to)
+
+
+# ---------------------------------------------------------------- exact group dots
+
+GEMV_SHAPES = [(1, 128), (7, 384), (64, 512), (300, 640), (33, 2048), (130, 5120), (257, 6144),
+               (65, 8192)]
+
+
+@pytest.mark.parametrize("N,K", GEMV_SHAPES)
+def test_group_dots_gemv(pq2, N, K):
+    print(f"dots gemv N={N} K={K}", flush=True)
+    rng = np.random.default_rng(N * 7 + K)
+    qn, t = rand_q(1, K, rng)
+    codes = synth.draw_codes(N, K, rng)
+    np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, pq2.PATH_GEMV),
+                                  oracle.group_dots(qn, codes))
+
+
+SMALL_SHAPES = [(M, N, K) for M in (1, 2, 3, 8, 16) for (N, K) in ((1, 128), (17, 640), (100, 5120))]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_SHAPES)
+def test_group_dots_small(pq2, M, N, K):
+    print(f"dots small M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 1000 + N + K)
+    qn, t = rand_q(M, K, rng)
+    codes = synth.draw_codes(N, K, rng, synth.PREFILL_CODES)
+    np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, pq2.PATH_SMALL),
+                                  oracle.group_dots(qn, codes))
+
+
+PREFILL_SHAPES = [(1, 1, 128), (17, 129, 384), (130, 300, 1024), (257, 129, 640), (128, 128, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
+def test_group_dots_prefill(pq2, M, N, K):
+    print(f"dots prefill M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 1000 + N + K + 1)
+    qn, t = rand_q(M, K, rng)
+    codes = synth.draw_codes(N, K, rng, synth.PREFILL_CODES)
+    np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, pq2.PATH_PREFILL),
+                                  oracle.group_dots(qn, codes))
+
+
+@pytest.mark.parametrize("path,M", [(1, 1), (2, 5), (3, 20)])
+def test_code3_is_plus_two(pq2, path, M):
+    """Code 3 is not a PQ2_0 code; both sides decode it as +2."""
+    rng = np.random.default_rng(path)
+    N, K = 40, 256
+    qn, t = rand_q(M, K, rng)
+    c = rng.integers(0, 4, size=(N, K)).astype(np.uint8)
+    codes = synth.pack_codes(c)
+    np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, path), oracle.group_dots(qn, codes))
+
+
+@pytest.mark.parametrize("path,M", [(1, 1), (2, 16), (3, 130)])
+def test_extreme_dots(pq2, path, M):
+    """q = +-127 everywhere with codes 2 or 0: |D| = 16256, the int32 extreme of a group."""
+    N, K = 20, 384
+    qn = np.full((M, K), 127, np.int8)
+    qn[::2] = -127
+    t = qn.reshape(M, -1, G).astype(np.int32).sum(-1).astype(np.int32)
+    c = np.zeros((N, K), np.uint8)
+    c[::2] = 2
+    codes = synth.pack_codes(c)
+    d = gpu_dots(pq2, qn, t, codes, path)
+    np.testing.assert_array_equal(d, oracle.group_dots(qn, codes))
+    assert np.abs(d).max() == 16256
+
+
+# ---------------------------------------------------------------- float32 output
+
+Y_SHAPES = [(1, 256, 512), (1, 100, 640), (2, 300, 1024), (5, 129, 384), (16, 64, 5120),
+            (17, 200, 640), (128, 256, 1024), (200, 130, 384)]
+
+
+@pytest.mark.parametrize("M,N,K", Y_SHAPES)
+def test_gemm_y_within_tolerance(pq2, M, N, K):
+    print(f"gemm y M={M} N={N} K={K}", flush=True)
+    x = synth.activations(M, K, M + N, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(N + K))
+    y = host(pq2.linear(dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))))
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(y, yo, tabs) < TOL
+
+
+def test_tiny_workload(pq2):
+    wl = synth.tiny()
+    w = synth.weights(wl.n, wl.k, 0)
+    x = synth.activations(wl.m, wl.k, 0)
+    y = host(pq2.linear(dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))))
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(y, yo, tabs) < TOL
+    # scale of the error relative to the output, for the record
+    print("tiny: max|y-y*|/max|y*| =", np.abs(y - yo).max() / np.abs(yo).max())
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 33])
+def test_one_hot_scales_give_exact_dots(pq2, M):
+    """s = 1 and ws[n][g] = [g == g0]: y equals the group dot exactly."""
+    rng = np.random.default_rng(M)
+    N, K = 70, 640
+    qn, t = rand_q(M, K, rng)
+    codes = synth.draw_codes(N, K, rng)
+    D = oracle.group_dots(qn, codes)
+    s = np.ones((M, K // G), np.float32)
+    for g0 in (0, K // G - 1):
+        ws = np.zeros((N, K // G), np.float16)
+        ws[:, g0] = 1.0
+        y = gpu_gemm(pq2, plane(qn), s, t, codes, ws)
+        np.testing.assert_array_equal(y, D[:, :, g0].astype(np.float32))
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 40])
+def test_degenerate_inputs(pq2, M):
+    """All-zero activations and all-zero-weight codes give exactly zero."""
+    N, K = 33, 384
+    w = synth.weights(N, K, 3)
+    y = host(pq2.linear(torch.zeros((M, K), device="cuda"), dev(w.codes),
+                        dev(w.wscale_bits.view(np.int16))))
+    assert (y == 0).all()
+    x = synth.activations(M, K, 4)
+    zero_codes = synth.pack_codes(np.ones((N, K), np.uint8))
+    y = host(pq2.linear(dev(x), dev(zero_codes), dev(w.wscale_bits.view(np.int16))))
+    assert (y == 0).all()
+
+
+def test_smallest_problem(pq2):
+    x = synth.activations(1, 128, 9)
+    w = synth.weights(1, 128, 9)
+    y = host(pq2.linear(dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))))
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(y, yo, tabs) < TOL
+
+
+# ---------------------------------------------------------------- full workload sizes
+
+FULL = [
+    ("decode_gemv", 1, 5120, 6144, synth.UNIFORM_CODES, 0.0),
+    ("layer_qkv", 1, 6144, 5120, synth.UNIFORM_CODES, 0.0),
+    ("small_m2_oproj", 2, 5120, 6144, synth.UNIFORM_CODES, 0.01),
+    ("small_m16_up", 16, 17408, 5120, synth.UNIFORM_CODES, 0.01),
+    ("small_m8_down", 8, 5120, 17408, synth.UNIFORM_CODES, 0.01),
+    ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
+    ("prefill_m4096_up", 4096, 17408, 5120, synth.PREFILL_CODES, 0.0),
+]
+
+
+@pytest.mark.parametrize("name,M,N,K,probs,outl", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
+    print(f"full {name} M={M} N={N} K={K}", flush=True)
+    x = synth.activations(M, K, 0, outlier_frac=outl)
+    w = synth.weights(N, K, synth.matrix_seed(0), probs)
+    xd, cd, wd = dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    q, s, t = pq2.quantize_act(xd)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(q, s, t, cd, wd, y)
+    yh = host(y)
+    qo, so, to = oracle.quantize(x)
+    np.testing.assert_array_equal(host(q), oracle.plane_order(qo))
+    rng = np.random.default_rng(1)
+    P = 384
+    mm = np.concatenate([rng.integers(0, M, P - 2), [0, M - 1]])
+    nn = np.concatenate([rng.integers(0, N, P - 2), [N - 1, 0]])
+    ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
+    assert oracle.rel_err(yh[mm, nn], ys, ts) < TOL
+    # unit scales: y = sum_g D, an integer below 2^24, exact in any order
+    ones_s = torch.ones_like(s)
+    ones_w = torch.full((N, K // G), 0x3C00, dtype=torch.int16, device="cuda")
+    pq2.pq2_gemm(q, ones_s, t, cd, ones_w, y)
+    yu = host(y)
+    Ds = oracle.group_dots_sampled(qo, w.codes, mm, nn)
+    np.testing.assert_array_equal(yu[mm, nn], Ds.sum(-1).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K,path", [(1, 5120, 6144, 1), (16, 5120, 6144, 2),
+                                        (16, 2048, 17408, 2), (256, 1024, 5120, 3)])
+def test_full_row_dots(pq2, M, N, K, path):
+    """Exact per-group dots over whole decode-size weight matrices."""
+    print(f"full dots M={M} N={N} K={K} path={path}", flush=True)
+    x = synth.activations(M, K, 0, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(1))
+    qo, so, to = oracle.quantize(x)
+    np.testing.assert_array_equal(gpu_dots(pq2, qo, to, w.codes, path),
+                                  oracle.group_dots(qo, w.codes))
