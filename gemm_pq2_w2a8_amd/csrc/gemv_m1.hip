@@ -6,20 +6,30 @@
 // its four bytes -- lines up with four consecutive activation bytes and one
 // int8 dot4 consumes them with no decode step; the -1 offset of the ternary
 // code is one subtraction of sum(q) per 128-weight group; the group dot is
-// then scaled by s[g] * ws[n][g] in float32 and summed over groups.
+// then scaled by s[g] * ws[n][g] in float32 and summed over groups. The page
+// also found independent dot4 accumulators and a one-stage loop best for one
+// token (page "Chasing llama.cpp at batch one", section "The win: a program
+// just for one token").
 //
 // gfx950 mapping:
 //  * A "chunk" is 16 bytes of one row = 4 code words = half a group. A wave
 //    splits into RL = 64/CL row slots of CL lanes; lane cs of a slot handles
 //    chunks cs, cs+CL, cs+2CL, ... of RP rows. CL = gcd(K/64, 64), so every
 //    lane is busy on every iteration and each load instruction covers RL
-//    contiguous segments of CL*16 bytes (coalesced HBM streaming).
-//  * The 16 plane-order q words of a chunk are loaded once per iteration and
-//    reused for the RP rows; q is K bytes and stays in cache.
-//  * Planes 0 and 2 are masked to bits 0..1 (after one shift by 4 for plane
-//    2); planes 1 and 3 are masked in place at bits 2..3, which is 4 * code.
-//    They go to a second accumulator that is divided by 4 (exactly) before
-//    the two are added: five bit operations and four v_dot4 per code word.
+//    contiguous runs of CL*16 bytes (coalesced HBM streaming).
+//  * K is processed in LDS windows of up to 32768 activations (one window
+//    for every K up to that). Per window the block stages q into LDS
+//    chunk-major by plane ([plane][chunk] of 16 bytes, so the CL lanes of a
+//    slot read consecutive 16-byte words), with s and t.
+//  * Memory-level parallelism: a lane issues the code loads (and the weight
+//    scale of each chunk's group) of IB chunk iterations x RP rows at once
+//    (one batch) and the next batch is in flight while the current one is
+//    computed. A window's first batch and all of its staging loads are
+//    issued before the first wait: one memory round trip before compute.
+//  * Planes 0 and 2 are masked to bits 0..1 (plane 2 after one shift by 4);
+//    planes 1 and 3 are masked in place at bits 2..3, which is 4 * code, and
+//    go to a second accumulator divided by 4 (exactly) before the two are
+//    added: five bit operations and four v_dot4 per code word.
 //  * The even lane of a chunk pair seeds its accumulator with -t[g]; the two
 //    half-group sums meet through a DPP lane swap, giving the exact group dot
 //    on both lanes. The even lane applies the float32 epilogue.
@@ -33,83 +43,180 @@ namespace {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
+constexpr int kLoadsPerBatch = 8;                 // uint4 code loads per lane per batch
+constexpr int64_t kMaxWindow = 32768;             // activations per LDS window
+constexpr int kQStagePer = kMaxWindow / 16 / kGemvThreads;   // q chunks per thread
+
+template <int LOG_CL, int RP>
+struct GemvShape {
+    static constexpr int CL = 1 << LOG_CL;
+    static constexpr int RL = kWave / CL;
+    static constexpr int ROWS_PER_WAVE = RL * RP;
+    static constexpr int ROWS_PER_BLOCK = kGemvWaves * ROWS_PER_WAVE;
+    static constexpr int IB = kLoadsPerBatch / RP;    // chunk iterations per batch
+};
+
+// LDS bytes per group of a window: q (128), s (4), t (4).
+constexpr int64_t kLdsPerGroup = kGroup + 8;
 
 template <int LOG_CL, int RP, bool DOTS>
 __global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, int64_t N, int64_t K) {
-    constexpr int CL = 1 << LOG_CL;
-    constexpr int RL = kWave / CL;
-    constexpr int ROWS_PER_WAVE = RL * RP;
+    int32_t *__restrict__ d, int64_t N, int64_t K, int64_t window) {
+    using S = GemvShape<LOG_CL, RP>;
+    constexpr int CL = S::CL, RL = S::RL, IB = S::IB;
+    extern __shared__ uint4 smem[];
+
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int cs = lane & (CL - 1);
     const int rs = lane >> LOG_CL;
-    const int h = cs & 1;                       // half of the group this lane holds
+    const int h = cs & 1;                         // half of the group this lane holds
     const int64_t G = K / kGroup;
-    const int64_t row_bytes = K / 4;
-    const int64_t iters = (K / 64) / CL;
-    const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + wave) * ROWS_PER_WAVE + rs;
+    const int64_t block_row0 = (int64_t)blockIdx.x * S::ROWS_PER_BLOCK;
+    const int local0 = wave * S::ROWS_PER_WAVE + rs;     // first local row of this lane
+    const int64_t row0 = block_row0 + local0;
 
-    const uint8_t *rowp[RP];
-    int64_t rowc[RP];
+    const uint4 *rowp[RP];
+    const uint16_t *wsp[RP];
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
         const int64_t row = row0 + (int64_t)r * RL;
-        rowc[r] = row < N ? row : N - 1;
-        rowp[r] = codes + rowc[r] * row_bytes;
+        const int64_t rc = row < N ? row : N - 1;
+        rowp[r] = reinterpret_cast<const uint4 *>(codes + rc * (K / 4));
+        wsp[r] = ws + rc * G;
     }
 
     float facc[RP];
 #pragma unroll
     for (int r = 0; r < RP; ++r) facc[r] = 0.0f;
 
-    for (int64_t it = 0; it < iters; ++it) {
-        const int64_t c = cs + (int64_t)CL * it;
-        const int64_t g = c >> 1;
-        // plane-order activations of this half group: plane p at +32p bytes
-        const uint4 *qp = reinterpret_cast<const uint4 *>(q + kGroup * g + 16 * h);
-        const uint4 q0 = qp[0], q1 = qp[2], q2 = qp[4], q3 = qp[6];
-        const int tg = t[g];
-        float sg = 0.0f;
-        if (!DOTS) sg = s[g];
+    for (int64_t k0 = 0; k0 < K; k0 += window) {
+        // window extent; all wave-uniform, kept in scalar registers
+        const int wk = __builtin_amdgcn_readfirstlane((int)((K - k0 < window) ? K - k0 : window));
+        const int wg = wk / kGroup;                   // groups in window
+        const int wchunks = wk / 64;
+        const int iters = wchunks / CL;
+        const int64_t g0 = k0 / kGroup;
+        const uint4 *wrow[RP];                        // this lane's first chunk of the window
+        const uint16_t *wsrow[RP];                    // the rows' scales of the window
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            wrow[r] = rowp[r] + k0 / 64 + cs;
+            wsrow[r] = wsp[r] + g0;
+        }
 
-        uint4 w[RP];
-        uint16_t wsv[RP];
+        // Loads are never predicated (a chunk past the window re-reads the
+        // window's last chunk and is not used), so each batch is a fixed
+        // number of loads and the compiler's wait counts stay exact.
+        uint4 bufa[IB][RP], bufb[IB][RP];
+        uint16_t wsa[IB][RP], wsb[IB][RP];
+        auto load_batch = [&](uint4 (&buf)[IB][RP], uint16_t (&wsv)[IB][RP], int it0) {
 #pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            w[r] = reinterpret_cast<const uint4 *>(rowp[r])[c];
-            if (!DOTS) wsv[r] = ws[rowc[r] * G + g];
-        }
+            for (int b = 0; b < IB; ++b) {
+                const int it = min(it0 + b, iters - 1);
 #pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            int da = h ? 0 : -tg;   // planes 0 and 2, and the -sum(q) offset
-            int db = 0;             // planes 1 and 3, in place: 4 * (their dot)
-            const uint32_t wr[4] = {w[r].x, w[r].y, w[r].z, w[r].w};
-            const uint32_t p0[4] = {q0.x, q0.y, q0.z, q0.w};
-            const uint32_t p1[4] = {q1.x, q1.y, q1.z, q1.w};
-            const uint32_t p2[4] = {q2.x, q2.y, q2.z, q2.w};
-            const uint32_t p3[4] = {q3.x, q3.y, q3.z, q3.w};
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const uint32_t wd = wr[jj];
-                const uint32_t hi = wd >> 4;
-                da = dot4(wd & kPlaneMask, p0[jj], da);
-                db = dot4(wd & kPlaneMaskX4, p1[jj], db);
-                da = dot4(hi & kPlaneMask, p2[jj], da);
-                db = dot4(hi & kPlaneMaskX4, p3[jj], db);
+                for (int r = 0; r < RP; ++r) {
+                    buf[b][r] = wrow[r][CL * it];
+                    if (!DOTS) wsv[b][r] = wsrow[r][(cs + CL * it) >> 1];
+                }
             }
-            const int half_dot = da + (db >> 2);          // db is a multiple of 4
-            const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
-            if (DOTS) {
-                const int64_t row = row0 + (int64_t)r * RL;
-                if (!h && row < N) d[row * G + g] = dot;
-            } else {
-                const float coef = h ? 0.0f : sg * half_bits_to_float(wsv[r]);
-                facc[r] = fmaf((float)dot, coef, facc[r]);
+        };
+        load_batch(bufa, wsa, 0);
+
+        // stage the window: q [plane][chunk], s [g], t [g]; all loads of the
+        // staging are issued (clamped, unpredicated) before any LDS store, so
+        // they share one memory round trip with the first code batch
+        float *s_l = reinterpret_cast<float *>(smem + 4 * wchunks);
+        int32_t *t_l = reinterpret_cast<int32_t *>(s_l + wg);
+        {
+            const uint4 *qg = reinterpret_cast<const uint4 *>(q + k0);
+            const int nq = wk / 16;
+            uint4 qs[kQStagePer];
+#pragma unroll
+            for (int i = 0; i < kQStagePer; ++i)
+                qs[i] = qg[min((int)threadIdx.x + i * kGemvThreads, nq - 1)];
+            const int gi = min((int)threadIdx.x, wg - 1);
+            float sv = 0.0f;
+            if (!DOTS) sv = s[g0 + gi];
+            const int32_t tv = t[g0 + gi];
+#pragma unroll
+            for (int i = 0; i < kQStagePer; ++i) {
+                const int u = threadIdx.x + i * kGemvThreads;
+                if (u < nq) {
+                    const int g = u >> 3, p = (u >> 1) & 3, hh = u & 1;
+                    smem[p * wchunks + 2 * g + hh] = qs[i];
+                }
+            }
+            if ((int)threadIdx.x < wg) {
+                if (!DOTS) s_l[threadIdx.x] = sv;
+                t_l[threadIdx.x] = tv;
             }
         }
+        __syncthreads();
+
+        auto compute_batch = [&](const uint4 (&buf)[IB][RP], const uint16_t (&wsv)[IB][RP],
+                                 int it0) {
+#pragma unroll
+            for (int b = 0; b < IB; ++b) {
+                if (it0 + b >= iters) break;
+                const int c = cs + CL * (it0 + b);    // chunk within window
+                const int g = c >> 1;                 // group within window
+                uint4 qv[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) qv[p] = smem[p * wchunks + c];
+                const int tg = t_l[g];
+                float sg = 0.0f;
+                if (!DOTS) sg = s_l[g];
+#pragma unroll
+                for (int r = 0; r < RP; ++r) {
+                    const uint4 w = buf[b][r];
+                    const uint32_t wr[4] = {w.x, w.y, w.z, w.w};
+                    const uint32_t p0[4] = {qv[0].x, qv[0].y, qv[0].z, qv[0].w};
+                    const uint32_t p1[4] = {qv[1].x, qv[1].y, qv[1].z, qv[1].w};
+                    const uint32_t p2[4] = {qv[2].x, qv[2].y, qv[2].z, qv[2].w};
+                    const uint32_t p3[4] = {qv[3].x, qv[3].y, qv[3].z, qv[3].w};
+                    int da = h ? 0 : -tg;   // planes 0 and 2, and the -sum(q) offset
+                    int db = 0;             // planes 1 and 3, in place: 4 * (their dot)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const uint32_t wd = wr[jj];
+                        const uint32_t hi = wd >> 4;
+                        da = dot4(wd & kPlaneMask, p0[jj], da);
+                        db = dot4(wd & kPlaneMaskX4, p1[jj], db);
+                        da = dot4(hi & kPlaneMask, p2[jj], da);
+                        db = dot4(hi & kPlaneMaskX4, p3[jj], db);
+                    }
+                    const int half_dot = da + (db >> 2);            // db is a multiple of 4
+                    const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
+                    if (DOTS) {
+                        const int64_t row = row0 + (int64_t)r * RL;
+                        if (!h && row < N) d[row * G + g0 + g] = dot;
+                    } else {
+                        const float cf = sg * half_bits_to_float(wsv[b][r]);
+                        facc[r] = fmaf((float)dot, h ? 0.0f : cf, facc[r]);
+                    }
+                }
+            }
+        };
+
+        // ping-pong: the other buffer's loads are in flight during each
+        // compute. Prefetches are unconditional (clamped), so the wait counts
+        // inside the loop are static.
+        if (iters <= IB) {
+            compute_batch(bufa, wsa, 0);
+        } else {
+            for (int it0 = 0;; it0 += 2 * IB) {
+                load_batch(bufb, wsb, it0 + IB);
+                compute_batch(bufa, wsa, it0);
+                if (it0 + IB >= iters) break;
+                load_batch(bufa, wsa, it0 + 2 * IB);
+                compute_batch(bufb, wsb, it0 + IB);
+                if (it0 + 2 * IB >= iters) break;
+            }
+        }
+        if (k0 + window < K) __syncthreads();    // window buffer is reused
     }
 
     if (!DOTS) {
@@ -125,27 +232,30 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
 template <int LOG_CL, int RP>
 hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
                       const GemmOut &out, int64_t N, int64_t K, hipStream_t stream) {
-    constexpr int rows_per_block = kGemvWaves * (kWave >> LOG_CL) * RP;
-    const int64_t blocks = (N + rows_per_block - 1) / rows_per_block;
-    if (out.d) {
+    using S = GemvShape<LOG_CL, RP>;
+    const int64_t blocks = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
+    const bool dots = out.d != nullptr;
+    const int64_t window = K < kMaxWindow ? K : kMaxWindow;
+    const size_t lds = (size_t)((window / kGroup) * kLdsPerGroup);
+    if (dots) {
         hipLaunchKernelGGL((gemv_m1_kernel<LOG_CL, RP, true>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), 0, stream, q, nullptr, t, codes, nullptr,
-                           nullptr, out.d, N, K);
+                           dim3(kGemvThreads), lds, stream, q, nullptr, t, codes, nullptr,
+                           nullptr, out.d, N, K, window);
     } else {
         hipLaunchKernelGGL((gemv_m1_kernel<LOG_CL, RP, false>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), 0, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, N, K);
+                           dim3(kGemvThreads), lds, stream, q, out.s, t, codes, out.ws, out.y,
+                           nullptr, N, K, window);
     }
     return hipGetLastError();
 }
 
+// Two rows per lane when a row slot is wide (CL >= 32): each wave then still
+// covers four rows, and every q word read from LDS serves both rows.
 template <int LOG_CL>
-hipError_t launch_rp(const int8_t *q, const int32_t *t, const uint8_t *codes,
+hipError_t launch_cl(const int8_t *q, const int32_t *t, const uint8_t *codes,
                      const GemmOut &out, int64_t N, int64_t K, hipStream_t stream) {
-    // Two rows per lane once the grid has enough waves to keep every CU busy.
-    const int64_t waves_rp1 = (N + (kWave >> LOG_CL) - 1) / (kWave >> LOG_CL);
-    if (waves_rp1 >= 4096) return launch_cfg<LOG_CL, 2>(q, t, codes, out, N, K, stream);
-    return launch_cfg<LOG_CL, 1>(q, t, codes, out, N, K, stream);
+    constexpr int RP = (LOG_CL >= 5) ? 2 : 1;
+    return launch_cfg<LOG_CL, RP>(q, t, codes, out, N, K, stream);
 }
 
 }  // namespace
@@ -157,12 +267,12 @@ hipError_t launch_gemv_m1(const int8_t *q, const int32_t *t, const uint8_t *code
     int64_t cl = chunks & -chunks;
     if (cl > 64) cl = 64;
     switch (cl) {
-        case 2: return launch_rp<1>(q, t, codes, out, N, K, stream);
-        case 4: return launch_rp<2>(q, t, codes, out, N, K, stream);
-        case 8: return launch_rp<3>(q, t, codes, out, N, K, stream);
-        case 16: return launch_rp<4>(q, t, codes, out, N, K, stream);
-        case 32: return launch_rp<5>(q, t, codes, out, N, K, stream);
-        default: return launch_rp<6>(q, t, codes, out, N, K, stream);
+        case 2: return launch_cl<1>(q, t, codes, out, N, K, stream);
+        case 4: return launch_cl<2>(q, t, codes, out, N, K, stream);
+        case 8: return launch_cl<3>(q, t, codes, out, N, K, stream);
+        case 16: return launch_cl<4>(q, t, codes, out, N, K, stream);
+        case 32: return launch_cl<5>(q, t, codes, out, N, K, stream);
+        default: return launch_cl<6>(q, t, codes, out, N, K, stream);
     }
 }
 

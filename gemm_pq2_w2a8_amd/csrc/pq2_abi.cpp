@@ -34,9 +34,9 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
     }
 }
 
-int auto_path(int64_t M) {
+int auto_path(int64_t M, int64_t K) {
     if (M == 1) return PQ2_PATH_GEMV;
-    if (M <= 16) return PQ2_PATH_SMALL;
+    if (M <= 16 && K <= pq2::kSmallMaxK) return PQ2_PATH_SMALL;
     return PQ2_PATH_PREFILL;
 }
 
@@ -78,7 +78,7 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uin
         !aligned(wscale, 2) || !aligned(y, 4))
         return PQ2_ERR_ALIGN;
     const pq2::GemmOut out{y, nullptr, s, wscale};
-    return run_path(auto_path(M), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+    return run_path(auto_path(M, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,
@@ -89,9 +89,9 @@ pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t 
     if (st != PQ2_OK) return st;
     if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(t, 4) || !aligned(d, 4))
         return PQ2_ERR_ALIGN;
-    if (path == PQ2_PATH_AUTO) path = auto_path(M);
+    if (path == PQ2_PATH_AUTO) path = auto_path(M, K);
     if (path == PQ2_PATH_GEMV && M != 1) return PQ2_ERR_ARG;
-    if (path == PQ2_PATH_SMALL && M > 16) return PQ2_ERR_ARG;
+    if (path == PQ2_PATH_SMALL && (M > 16 || K > pq2::kSmallMaxK)) return PQ2_ERR_ARG;
     if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PREFILL) return PQ2_ERR_ARG;
     const pq2::GemmOut out{nullptr, d, nullptr, nullptr};
     return run_path(path, q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));

@@ -72,7 +72,7 @@ typedef enum {
 enum {
     PQ2_PATH_AUTO = 0,      /* same choice as pq2_gemm */
     PQ2_PATH_GEMV = 1,      /* M == 1 only: the v_dot4 GEMV */
-    PQ2_PATH_SMALL = 2,     /* M <= 16 only: the small-batch MFMA kernel */
+    PQ2_PATH_SMALL = 2,     /* M <= 16, K <= 32768: the small-batch MFMA kernel */
     PQ2_PATH_PREFILL = 3    /* any M: the tiled MFMA GEMM */
 };
 
@@ -98,7 +98,8 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
  * y = the PQ2_0 product defined above. The kernel depends on M:
  *   M == 1        -> GEMV streaming code words into v_dot4 (2-bit planes
  *                    masked out of each 32-bit word, no decode step);
- *   2 <= M <= 16  -> small-batch kernel on int8 MFMA, tokens padded to 16;
+ *   2 <= M <= 16  -> small-batch kernel on int8 MFMA, tokens padded to 16
+ *                    (K <= 32768; larger K takes the tiled kernel);
  *   M >= 17       -> tiled int8 MFMA GEMM (prefill).
  * Group dots are exact int32; the float32 epilogue sums the G terms in an
  * order that differs from a sequential sum only by float32 rounding.
@@ -112,7 +113,7 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
  * but stores the exact per-group dots instead of the float epilogue:
  *   d int32 [M][N][G],  d[m][n][g] = D[m][n][g] as defined above.
  * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M == 1 and
- * PQ2_PATH_SMALL requires M <= 16 (else PQ2_ERR_ARG).
+ * PQ2_PATH_SMALL requires M <= 16 and K <= 32768 (else PQ2_ERR_ARG).
  */
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t,
                                const uint8_t *codes, int32_t *d,

@@ -285,3 +285,22 @@ def test_full_row_dots(pq2, M, N, K, path):
     qo, so, to = oracle.quantize(x)
     np.testing.assert_array_equal(gpu_dots(pq2, qo, to, w.codes, path),
                                   oracle.group_dots(qo, w.codes))
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 4100, 5120), (16, 4160, 640), (8, 4160, 17408),
+                                   (16, 4096, 16384)])
+def test_small_multi_tile_blocks(pq2, M, N, K):
+    """Small-batch blocks of 64 (K <= 16384) or 32 weight rows (larger K), with ragged
+    last blocks: exact group dots and float outputs."""
+    print(f"small multi-tile M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M + N + K)
+    x = synth.draw_x(M, K, rng, outlier_frac=0.01)
+    w = synth.weights(N, K, 7)
+    qo, so, to = oracle.quantize(x)
+    np.testing.assert_array_equal(gpu_dots(pq2, qo, to, w.codes, pq2.PATH_SMALL),
+                                  oracle.group_dots(qo, w.codes))
+    y = gpu_gemm(pq2, oracle.plane_order(qo), so, to, w.codes, w.wscale)
+    mm = np.repeat(np.arange(M), 40)
+    nn = np.concatenate([rng.integers(0, N, 38), [0, N - 1]] * M)
+    ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
+    assert oracle.rel_err(y[mm, nn], ys, ts) < TOL
