@@ -84,8 +84,9 @@ const char *pq2_status_str(int status);
 
 /*
  * Per-128-group int8 quantisation of activations, fused with the plane-order
- * permutation (page 1, sections "One token at a time" for the layout and
- * "Prompt processing" for the q/s/t buffers). For each row m and group g:
+ * permutation (page "Making a ternary reasoning model fast in vLLM -- from
+ * CUDA to Triton and Gluon": section "One token at a time" for the layout,
+ * section "Prompt processing" for the q/s/t buffers). For each row m and group g:
  *   amax = max |x|;  s = amax / 127 (float32, correctly rounded division);
  *   q = clamp(round_half_even(x / s), -127, 127) (float32 division);
  *   t = sum of the group's q.   A group with s == 0 gets q = 0, t = 0.
