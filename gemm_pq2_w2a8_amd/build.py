@@ -33,6 +33,9 @@ CFLAGS = [
     # the quantiser needs IEEE division and float32 denormals
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
+    # MFMA sources and results in ordinary VGPRs: the kernels' epilogues read
+    # every MFMA result with VALU instructions, which cannot read AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", INCLUDE,
 ]
 

@@ -13,7 +13,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 pq2_status check_mnk(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || K < PQ2_GROUP || K % PQ2_GROUP != 0) return PQ2_ERR_SHAPE;
-    if (M > PQ2_MAX_DIM || N > PQ2_MAX_DIM || K > PQ2_MAX_DIM) return PQ2_ERR_SHAPE;
+    if (M > PQ2_MAX_DIM || N > PQ2_MAX_DIM || K > PQ2_MAX_K) return PQ2_ERR_SHAPE;
     return PQ2_OK;
 }
 
@@ -50,7 +50,7 @@ const char *pq2_status_str(int status) {
     switch (status) {
         case PQ2_OK: return "PQ2_OK";
         case PQ2_ERR_NULL: return "PQ2_ERR_NULL: a required pointer is NULL";
-        case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128";
+        case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128, K <= 2^24";
         case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
         case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
         case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M";

@@ -20,9 +20,19 @@
 //    (one 16-byte LDS read). The accumulator is seeded with -t, so the two
 //    MFMAs give the exact group dot; the float32 epilogue
 //    acc += D * (s[m] * ws[n]) follows per group.
-//  * Per group the block stages codes, activations and the group's scales
-//    in LDS, double buffered: the global loads of group g+1 are in flight
-//    while group g is computed, with one barrier per group.
+//  * The float epilogue (convert, scale product, FMA per output and group)
+//    is the VALU work that bounds this kernel, so everything else is kept
+//    off the VALU: MFMA results stay in VGPRs (no accumulator-register
+//    copies), global addresses are a uniform 64-bit base plus a fixed 32-bit
+//    per-lane offset, and a lane's A operands are formed once per group and
+//    reused across its WM token tiles.
+//  * Scales are staged in LDS eight groups at a time (double buffered).
+//  * Staging runs through two LDS stages with one barrier per group. With
+//    DEPTH = 2 the global loads of group g+2 are issued into one of two
+//    register sets while group g is computed and group g+1 is written from
+//    the other set into the second stage; with DEPTH = 1 (large tiles, whose
+//    accumulators leave no room for a second set) the loads of group g+1 are
+//    in flight while group g is computed.
 //  * Tiles are numbered so that each XCD (blocks are dealt round-robin over
 //    the 8 XCDs) gets a contiguous run of tiles along N for the same token
 //    panel, which then stays in that XCD's L2.
@@ -33,9 +43,17 @@ namespace pq2 {
 
 namespace {
 
+#ifndef PREFILL_TUNE_OVERRIDE
+#define PREFILL_TUNE_OVERRIDE
+#endif
+
 constexpr int kCodeStride = 48;          // LDS bytes per code row (32 + pad)
 constexpr int kQStride = 144;            // LDS bytes per token row (128 + pad)
 constexpr int kNumXcd = 8;
+// Scales are staged kScaleChunk groups at a time: lanes walk along the group
+// dimension of the [rows][G] scale arrays, so one load instruction touches a
+// few cache lines instead of one line per lane.
+constexpr int kScaleChunk = 8;
 
 // Bijection from dispatch order to tile order: dispatch slot b runs on XCD
 // b % 8; XCD x receives the x-th contiguous run of tile numbers.
@@ -57,28 +75,149 @@ struct PfCfg {
     struct __align__(16) Stage {
         uint8_t codes[BN * kCodeStride];
         int8_t q[BM * kQStride];
-        uint16_t ws[BN];
-        float s[BM];
-        int32_t t[BM];
+    };
+    // Scales of kScaleChunk consecutive groups, group-major: ws[j][row],
+    // s[j][token], t[j][token] for group kScaleChunk * c + j.
+    static constexpr int kWsElems = kScaleChunk * BN;
+    static constexpr int kStElems = kScaleChunk * BM;
+    static constexpr int kWsPer = (kWsElems + kThreads - 1) / kThreads;
+    static constexpr int kStPer = (kStElems + kThreads - 1) / kThreads;
+    struct __align__(16) Scales {
+        uint16_t ws[kScaleChunk][BN];
+        float s[kScaleChunk][BM];
+        int32_t t[kScaleChunk][BM];
     };
 };
 
-template <int WN, int WM, int WAVES_N, int WAVES_M, bool DOTS>
+// Buffer resource over [base, base + bytes) (bytes clamped to 32 bits; every
+// offset used is in range by construction, the hardware range check is a
+// second guard). Word 3 selects 32-bit raw data, as for all gfx9 buffers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes >= 0xffffffffLL ? (int)0xffffffffu : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+// 16-byte staging chunks: global -> registers (buffer loads: fixed per-lane
+// offset plus a uniform group offset), registers -> LDS. Native vector
+// types: copies of the HIP uint4 struct become memcpys that can leave the
+// staging registers in scratch memory.
+template <int P>
+__device__ __forceinline__ void load_chunks(v4i (&dst)[P], __amdgpu_buffer_rsrc_t rs,
+                                            const uint32_t (&off)[P], uint32_t goff) {
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off[i], (int)goff, 0);
+}
+
+template <int CHUNKS, int THREADS, int P>
+__device__ __forceinline__ void store_chunks(const v4i (&src)[P], uint8_t *lds,
+                                             const int (&dst)[P], int tid) {
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (CHUNKS % THREADS == 0 || tid + i * THREADS < CHUNKS)
+            *reinterpret_cast<v4i *>(lds + dst[i]) = src[i];
+}
+
+// Per-lane constants of the compute step.
+struct LaneCtx {
+    int row_base, tok_base, r, lg, half, sh0, G;
+    int64_t m0, n0, M, N;
+    int32_t *d;
+};
+
+// One group from an LDS stage and the group's scale tables (ws_g, s_g, t_g:
+// row / token-indexed LDS rows). Every LDS read of the group (code words and
+// weight scales of the wave's WN row tiles, activations and token scales of
+// its WM token tiles) is issued first, so their latency is paid once per
+// group; then per token tile the 2 * WN MFMAs are issued before their
+// epilogue (or the exact dots).
+template <int WN, int WM, bool DOTS, class Stage>
+__device__ __forceinline__ void compute_group(const Stage &cur, const uint16_t *ws_g,
+                                              const float *s_g, const int32_t *t_g,
+                                              float (&acc)[WN][WM][4], const LaneCtx &c_, int g) {
+    v4i w[WN], b0[WM], b1[WM];
+    uint2 wsw[WN];
+    int tt[WM];
+    float sv[WM];
+#pragma unroll
+    for (int a = 0; a < WN; ++a) {
+        w[a] = *reinterpret_cast<const v4i *>(
+            cur.codes + (c_.row_base + 16 * a + c_.r) * kCodeStride + 16 * c_.half);
+        if (!DOTS)
+            wsw[a] = *reinterpret_cast<const uint2 *>(ws_g + c_.row_base + 16 * a + 4 * c_.lg);
+    }
+#pragma unroll
+    for (int b = 0; b < WM; ++b) {
+        const int tok = c_.tok_base + 16 * b + c_.r;
+        const int8_t *qrow = cur.q + tok * kQStride + 16 * c_.lg;
+        b0[b] = *reinterpret_cast<const v4i *>(qrow);
+        b1[b] = *reinterpret_cast<const v4i *>(qrow + 64);
+        tt[b] = t_g[tok];
+        sv[b] = DOTS ? 0.0f : s_g[tok];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4i a0[WN], a1[WN];
+    float wsf[WN][4];
+#pragma unroll
+    for (int a = 0; a < WN; ++a) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t sh = (uint32_t)w[a][j] >> c_.sh0;
+            a0[a][j] = (int)(sh & kPlaneMask);
+            a1[a][j] = (int)((sh >> 4) & kPlaneMask);
+        }
+        if (!DOTS) {
+            wsf[a][0] = half_bits_to_float((uint16_t)(wsw[a].x & 0xffff));
+            wsf[a][1] = half_bits_to_float((uint16_t)(wsw[a].x >> 16));
+            wsf[a][2] = half_bits_to_float((uint16_t)(wsw[a].y & 0xffff));
+            wsf[a][3] = half_bits_to_float((uint16_t)(wsw[a].y >> 16));
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < WM; ++b) {
+        const v4i seed = {-tt[b], -tt[b], -tt[b], -tt[b]};
+        v4i c[WN];
+#pragma unroll
+        for (int a = 0; a < WN; ++a) c[a] = mfma16x16x64(a0[a], b0[b], seed);
+#pragma unroll
+        for (int a = 0; a < WN; ++a) c[a] = mfma16x16x64(a1[a], b1[b], c[a]);
+#pragma unroll
+        for (int a = 0; a < WN; ++a) {
+            if (DOTS) {
+                const int64_t m = c_.m0 + c_.tok_base + 16 * b + c_.r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t n = c_.n0 + c_.row_base + 16 * a + 4 * c_.lg + i;
+                    if (m < c_.M && n < c_.N) c_.d[(m * c_.N + n) * c_.G + g] = c[a][i];
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[a][b][i] = fmaf((float)c[a][i], sv[b] * wsf[a][i], acc[a][b][i]);
+            }
+        }
+    }
+}
+
+template <int WN, int WM, int WAVES_N, int WAVES_M, int DEPTH, bool DOTS>
 __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
     int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
     using C = PfCfg<WN, WM, WAVES_N, WAVES_M>;
     using Stage = typename C::Stage;
+    using Scales = typename C::Scales;
     __shared__ Stage stage[2];
+    __shared__ Scales scl[2];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wn = wave % WAVES_N, wm = wave / WAVES_N;
     const int r = lane & 15, lg = lane >> 4;
     const int half = lg & 1;
     const int sh0 = 2 * (lg >> 1);
     const int G = (int)(K / kGroup);
+    const int64_t KB = K / 4;                // code bytes per row
 
     const int64_t tiles_n = (N + C::BN - 1) / C::BN;
     const int64_t tiles_m = (M + C::BM - 1) / C::BM;
@@ -86,67 +225,112 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
     const int64_t n0 = (tile % tiles_n) * C::BN;
     const int64_t m0 = (tile / tiles_n) * C::BM;
 
-    // staging assignment: chunk c of codes is (row c/2, half c%2); chunk c of q
-    // is (token c/8, 16-byte piece c%8)
-    const uint4 *code_src[C::kCodePer];
+    // Buffer resources based at the block's first row and token; per-lane
+    // 32-bit offsets (the host bounds K so that BN * K / 4 and BM * K fit in
+    // 32 bits) and a uniform offset per group.
+    const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(codes + n0 * KB, (N - n0) * KB);
+    const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + m0 * K, (M - m0) * K);
+    const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(t + m0 * G, (M - m0) * G * 4);
+    const __amdgpu_buffer_rsrc_t rs_ws = make_rsrc(DOTS ? nullptr : ws + n0 * G, DOTS ? 0 : (N - n0) * G * 2);
+    const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(DOTS ? nullptr : s + m0 * G, DOTS ? 0 : (M - m0) * G * 4);
+
+    // staging assignment: chunk c of codes is (row c/2, half c%2); chunk c of
+    // q is (token c/8, 16-byte piece c%8). Rows and tokens past the end are
+    // clamped to the last one (their results are never stored).
+    uint32_t code_off[C::kCodePer];
     int code_dst[C::kCodePer];
 #pragma unroll
     for (int i = 0; i < C::kCodePer; ++i) {
         int c = tid + i * C::kThreads;
         if (c >= C::kCodeChunks) c = C::kCodeChunks - 1;
         const int row = c >> 1, hh = c & 1;
-        const int64_t gn = (n0 + row < N) ? n0 + row : N - 1;
-        code_src[i] = reinterpret_cast<const uint4 *>(codes + gn * (K / 4) + 16 * hh);
+        const int64_t rel = (n0 + row < N) ? row : N - 1 - n0;
+        code_off[i] = (uint32_t)(rel * KB + 16 * hh);
         code_dst[i] = row * kCodeStride + 16 * hh;
     }
-    const uint4 *q_src[C::kQPer];
+    uint32_t q_off[C::kQPer];
     int q_dst[C::kQPer];
 #pragma unroll
     for (int i = 0; i < C::kQPer; ++i) {
         int c = tid + i * C::kThreads;
         if (c >= C::kQChunks) c = C::kQChunks - 1;
         const int tok = c >> 3, piece = c & 7;
-        const int64_t gm = (m0 + tok < M) ? m0 + tok : M - 1;
-        q_src[i] = reinterpret_cast<const uint4 *>(q + gm * K + 16 * piece);
+        const int64_t rel = (m0 + tok < M) ? tok : M - 1 - m0;
+        q_off[i] = (uint32_t)(rel * K + 16 * piece);
         q_dst[i] = tok * kQStride + 16 * piece;
     }
-
-    // Staging loads and LDS writes are never predicated on g (the step after
-    // the last group re-reads the last group into the idle buffer), which
-    // keeps the staging registers out of scratch memory.
-    constexpr bool kCodeRagged = (C::kCodeChunks % C::kThreads) != 0;
-    constexpr bool kQRagged = (C::kQChunks % C::kThreads) != 0;
-    const int64_t sn = (n0 + tid < N) ? n0 + tid : N - 1;     // ws row of this thread
-    const int64_t sm = (m0 + tid < M) ? m0 + tid : M - 1;     // s/t token of this thread
-#define PQ2_PF_FETCH(g)                                                             \
-    do {                                                                          \
-        _Pragma("unroll") for (int i = 0; i < C::kCodePer; ++i) rc[i] = code_src[i][2 * (g)]; \
-        _Pragma("unroll") for (int i = 0; i < C::kQPer; ++i) rq[i] = q_src[i][8 * (g)];       \
-        if (!DOTS && tid < C::BN) rws = ws[sn * G + (g)];                         \
-        if (tid < C::BM) {                                                        \
-            rt = t[sm * G + (g)];                                                 \
-            if (!DOTS) rs_ = s[sm * G + (g)];                                     \
-        }                                                                         \
+    // scale-chunk assignment: element e = tid + i * kThreads is (row or token
+    // e / kScaleChunk, group offset e % kScaleChunk); kThreads is a multiple
+    // of kScaleChunk, so a thread's group offset sc_j is the same for all i
+    // and its rows step by kThreads / kScaleChunk.
+    static_assert(C::kThreads % kScaleChunk == 0, "scale chunk layout");
+    constexpr int kRowStep = C::kThreads / kScaleChunk;
+    const int sc_j = tid % kScaleChunk, sc_row = tid / kScaleChunk;
+    // Staging loads are never predicated (groups past the end are clamped to
+    // the last group), which keeps their registers out of scratch memory and
+    // the wait counts exact; only the LDS writes of ragged chunk counts are.
+#define PQ2_PF_FETCH(gg, RC, RQ)                                                      \
+    do {                                                                            \
+        const uint32_t g_ = (uint32_t)((gg) < G ? (gg) : G - 1);                    \
+        load_chunks(RC, rs_codes, code_off, 32u * g_);                              \
+        load_chunks(RQ, rs_q, q_off, (uint32_t)kGroup * g_);                        \
+        __builtin_amdgcn_sched_barrier(0);                                          \
     } while (0)
-#define PQ2_PF_COMMIT(st)                                                           \
-    do {                                                                          \
-        _Pragma("unroll") for (int i = 0; i < C::kCodePer; ++i)                   \
-            if (!kCodeRagged || tid + i * C::kThreads < C::kCodeChunks)           \
-                *reinterpret_cast<uint4 *>((st).codes + code_dst[i]) = rc[i];     \
-        _Pragma("unroll") for (int i = 0; i < C::kQPer; ++i)                      \
-            if (!kQRagged || tid + i * C::kThreads < C::kQChunks)                 \
-                *reinterpret_cast<uint4 *>((st).q + q_dst[i]) = rq[i];            \
-        if (!DOTS && tid < C::BN) (st).ws[tid] = rws;                             \
-        if (tid < C::BM) {                                                        \
-            (st).t[tid] = rt;                                                     \
-            if (!DOTS) (st).s[tid] = rs_;                                         \
-        }                                                                         \
+#define PQ2_PF_COMMIT(st, RC, RQ)                                                     \
+    do {                                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                          \
+        store_chunks<C::kCodeChunks, C::kThreads>(RC, (st).codes, code_dst, tid);   \
+        store_chunks<C::kQChunks, C::kThreads>(RQ, (uint8_t *)(st).q, q_dst, tid);  \
     } while (0)
-
-    uint4 rc[C::kCodePer], rq[C::kQPer];
-    uint16_t rws = 0;
-    float rs_ = 0.0f;
-    int32_t rt = 0;
+    // scale chunk cc: group kScaleChunk * cc + j, clamped to the last group
+#define PQ2_PF_SCALE_FETCH(cc)                                                        \
+    do {                                                                            \
+        const int gi_ = kScaleChunk * (cc) + sc_j < G ? kScaleChunk * (cc) + sc_j : G - 1; \
+        if (!DOTS) {                                                                \
+            _Pragma("unroll") for (int i = 0; i < C::kWsPer; ++i) {                 \
+                int row = sc_row + i * kRowStep;                                    \
+                row = row < C::BN ? row : C::BN - 1;                                \
+                row = n0 + row < N ? row : (int)(N - 1 - n0);                       \
+                rws[i] = __builtin_amdgcn_raw_buffer_load_b16(                      \
+                    rs_ws, (int)(2u * ((uint32_t)row * (uint32_t)G + (uint32_t)gi_)), 0, 0); \
+            }                                                                       \
+        }                                                                           \
+        _Pragma("unroll") for (int i = 0; i < C::kStPer; ++i) {                     \
+            int tok = sc_row + i * kRowStep;                                        \
+            tok = tok < C::BM ? tok : C::BM - 1;                                    \
+            tok = m0 + tok < M ? tok : (int)(M - 1 - m0);                           \
+            const int off = (int)(4u * ((uint32_t)tok * (uint32_t)G + (uint32_t)gi_)); \
+            if (!DOTS) rss[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, off, 0, 0); \
+            rts[i] = __builtin_amdgcn_raw_buffer_load_b32(rs_t, off, 0, 0);         \
+        }                                                                           \
+    } while (0)
+#define PQ2_PF_SCALE_COMMIT(buf)                                                      \
+    do {                                                                            \
+        if (!DOTS) {                                                                \
+            _Pragma("unroll") for (int i = 0; i < C::kWsPer; ++i)                   \
+                if (C::kWsElems % C::kThreads == 0 || tid + i * C::kThreads < C::kWsElems) \
+                    (buf).ws[sc_j][sc_row + i * kRowStep] = rws[i];                 \
+        }                                                                           \
+        _Pragma("unroll") for (int i = 0; i < C::kStPer; ++i)                       \
+            if (C::kStElems % C::kThreads == 0 || tid + i * C::kThreads < C::kStElems) { \
+                if (!DOTS) (buf).s[sc_j][sc_row + i * kRowStep] = __builtin_bit_cast(float, rss[i]); \
+                (buf).t[sc_j][sc_row + i * kRowStep] = (int32_t)rts[i];             \
+            }                                                                       \
+    } while (0)
+    // one group: scale chunk loads every kScaleChunk groups (committed in the
+    // same iteration, into the buffer the previous chunk used)
+#define PQ2_PF_STEP(gg, CUR, NXT, RC_F, RQ_F, RC_C, RQ_C, FETCH_G)                     \
+    do {                                                                            \
+        const int cc_ = (gg) / kScaleChunk, jj_ = (gg) % kScaleChunk;               \
+        const bool sc_ = jj_ == 0 && (gg) + kScaleChunk < G;                        \
+        if (sc_) PQ2_PF_SCALE_FETCH(cc_ + 1);                                       \
+        PQ2_PF_FETCH(FETCH_G, RC_F, RQ_F);                                          \
+        const Scales &sb_ = scl[cc_ & 1];                                           \
+        compute_group<WN, WM, DOTS>(CUR, sb_.ws[jj_], sb_.s[jj_], sb_.t[jj_], acc, ctx, (gg)); \
+        PQ2_PF_COMMIT(NXT, RC_C, RQ_C);                                             \
+        if (sc_) PQ2_PF_SCALE_COMMIT(scl[(cc_ + 1) & 1]);                           \
+        __syncthreads();                                                            \
+    } while (0)
 
     float acc[WN][WM][4];
 #pragma unroll
@@ -156,82 +340,67 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
 
-    PQ2_PF_FETCH(0);
-    PQ2_PF_COMMIT(stage[0]);
-    __syncthreads();
+    LaneCtx ctx;
+    ctx.row_base = 16 * WN * wn;    // wave's first row within the block tile
+    ctx.tok_base = 16 * WM * wm;    // wave's first token within the block tile
+    ctx.r = r;
+    ctx.lg = lg;
+    ctx.half = half;
+    ctx.sh0 = sh0;
+    ctx.m0 = m0;
+    ctx.n0 = n0;
+    ctx.M = M;
+    ctx.N = N;
+    ctx.G = G;
+    ctx.d = d;
 
-    const int row_base = 16 * WN * wn;     // wave's first row within the block tile
-    const int tok_base = 16 * WM * wm;     // wave's first token within the block tile
-    for (int g = 0; g < G; ++g) {
-        const Stage &cur = stage[g & 1];
-        const int gn1 = g + 1 < G ? g + 1 : g;
-        PQ2_PF_FETCH(gn1);
+    uint16_t rws[C::kWsPer];
+    uint32_t rss[C::kStPer], rts[C::kStPer];
+#pragma unroll
+    for (int i = 0; i < C::kWsPer; ++i) rws[i] = 0;
+#pragma unroll
+    for (int i = 0; i < C::kStPer; ++i) rss[i] = rts[i] = 0;
+    PQ2_PF_SCALE_FETCH(0);
+    PQ2_PF_SCALE_COMMIT(scl[0]);
 
-        // A operands (and weight scales) of the wave's WN row tiles
-        v4i a0[WN], a1[WN];
-        float wsf[WN][4];
-#pragma unroll
-        for (int a = 0; a < WN; ++a) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(
-                cur.codes + (row_base + 16 * a + r) * kCodeStride + 16 * half);
-            const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t sh = wv[j] >> sh0;
-                a0[a][j] = (int)(sh & kPlaneMask);
-                a1[a][j] = (int)((sh >> 4) & kPlaneMask);
-            }
-            if (!DOTS) {
-                const uint2 wsw = *reinterpret_cast<const uint2 *>(cur.ws + row_base + 16 * a + 4 * lg);
-                wsf[a][0] = half_bits_to_float((uint16_t)(wsw.x & 0xffff));
-                wsf[a][1] = half_bits_to_float((uint16_t)(wsw.x >> 16));
-                wsf[a][2] = half_bits_to_float((uint16_t)(wsw.y & 0xffff));
-                wsf[a][3] = half_bits_to_float((uint16_t)(wsw.y >> 16));
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < WM; ++b) {
-            const int tok = tok_base + 16 * b + r;
-            const int8_t *qrow = cur.q + tok * kQStride + 16 * half + 16 * sh0;
-            const uint4 q0 = *reinterpret_cast<const uint4 *>(qrow);
-            const uint4 q1 = *reinterpret_cast<const uint4 *>(qrow + 64);
-            const v4i b0 = {(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w};
-            const v4i b1 = {(int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
-            const int tneg = -cur.t[tok];
-            const float sv = cur.s[tok];
-#pragma unroll
-            for (int a = 0; a < WN; ++a) {
-                v4i c = {tneg, tneg, tneg, tneg};
-                c = mfma16x16x64(a0[a], b0, c);
-                c = mfma16x16x64(a1[a], b1, c);
-                if (DOTS) {
-                    const int64_t m = m0 + tok;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int64_t n = n0 + row_base + 16 * a + 4 * lg + i;
-                        if (m < M && n < N) d[(m * N + n) * G + g] = c[i];
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[a][b][i] = fmaf((float)c[i], sv * wsf[a][i], acc[a][b][i]);
-                }
-            }
-        }
-
-        PQ2_PF_COMMIT(stage[(g + 1) & 1]);
+    v4i rcA[C::kCodePer], rqA[C::kQPer];
+    int g = 0;
+    if constexpr (DEPTH == 2) {
+        v4i rcB[C::kCodePer], rqB[C::kQPer];
+        PQ2_PF_FETCH(0, rcA, rqA);
+        PQ2_PF_FETCH(1, rcB, rqB);
+        PQ2_PF_COMMIT(stage[0], rcA, rqA);
         __syncthreads();
+        for (; g + 1 < G; g += 2) {
+            // stage 0 holds group g, set B carries group g+1, set A fetches g+2
+            PQ2_PF_STEP(g, stage[0], stage[1], rcA, rqA, rcB, rqB, g + 2);
+            // stage 1 holds group g+1, set A carries group g+2, set B fetches g+3
+            PQ2_PF_STEP(g + 1, stage[1], stage[0], rcB, rqB, rcA, rqA, g + 3);
+        }
+        if (g < G) {   // odd G: the last group is in stage 0
+            const Scales &sb = scl[(g / kScaleChunk) & 1];
+            const int jj = g % kScaleChunk;
+            compute_group<WN, WM, DOTS>(stage[0], sb.ws[jj], sb.s[jj], sb.t[jj], acc, ctx, g);
+        }
+    } else {
+        PQ2_PF_FETCH(0, rcA, rqA);
+        PQ2_PF_COMMIT(stage[0], rcA, rqA);
+        __syncthreads();
+        for (; g < G; ++g) PQ2_PF_STEP(g, stage[g & 1], stage[(g + 1) & 1], rcA, rqA, rcA, rqA, g + 1);
     }
 #undef PQ2_PF_FETCH
 #undef PQ2_PF_COMMIT
+#undef PQ2_PF_SCALE_FETCH
+#undef PQ2_PF_SCALE_COMMIT
+#undef PQ2_PF_STEP
 
     if (!DOTS) {
 #pragma unroll
         for (int b = 0; b < WM; ++b) {
-            const int64_t m = m0 + tok_base + 16 * b + r;
+            const int64_t m = m0 + ctx.tok_base + 16 * b + r;
 #pragma unroll
             for (int a = 0; a < WN; ++a) {
-                const int64_t nb = n0 + row_base + 16 * a + 4 * lg;
+                const int64_t nb = n0 + ctx.row_base + 16 * a + 4 * lg;
                 if (m < M) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -242,18 +411,18 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
     }
 }
 
-template <int WN, int WM, int WAVES_N, int WAVES_M>
+template <int WN, int WM, int WAVES_N, int WAVES_M, int DEPTH>
 hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
                       const GemmOut &out, int64_t M, int64_t N, int64_t K,
                       hipStream_t stream) {
     using C = PfCfg<WN, WM, WAVES_N, WAVES_M>;
     const int64_t blocks = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
     if (out.d) {
-        hipLaunchKernelGGL((prefill_mfma_kernel<WN, WM, WAVES_N, WAVES_M, true>),
+        hipLaunchKernelGGL((prefill_mfma_kernel<WN, WM, WAVES_N, WAVES_M, DEPTH, true>),
                            dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, q, nullptr, t,
                            codes, nullptr, nullptr, out.d, M, N, K);
     } else {
-        hipLaunchKernelGGL((prefill_mfma_kernel<WN, WM, WAVES_N, WAVES_M, false>),
+        hipLaunchKernelGGL((prefill_mfma_kernel<WN, WM, WAVES_N, WAVES_M, DEPTH, false>),
                            dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, q, out.s, t,
                            codes, out.ws, out.y, nullptr, M, N, K);
     }
@@ -262,17 +431,29 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 
 }  // namespace
 
+// Tile configurations (rows x tokens, waves, prefetch depth):
+//   0: 128 x 128, 2 x 2 waves of 64 x 64, depth 1
+//   1: 128 x 128, 4 x 1 waves of 32 x 128, depth 1
+//   2: 128 x 128, 2 x 2 waves of 64 x 64, depth 2
+//   3:  64 x 128, 2 x 2 waves of 32 x 64, depth 2
+//   4:  32 x 128, 2 x 2 waves of 16 x 64, depth 2
+//   5: 128 x 64,  2 x 2 waves of 64 x 32, depth 2
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
     // Largest tile that still gives every CU at least one block.
     auto tiles = [&](int64_t bn, int64_t bm) { return ((N + bn - 1) / bn) * ((M + bm - 1) / bm); };
     constexpr int64_t kCUs = 256;
-    if (tiles(128, 128) >= kCUs)
-        return launch_cfg<4, 4, 2, 2>(q, t, codes, out, M, N, K, stream);   // 128 x 128
-    if (tiles(64, 128) >= kCUs)
-        return launch_cfg<2, 4, 2, 2>(q, t, codes, out, M, N, K, stream);   // 64 x 128
-    return launch_cfg<1, 4, 2, 2>(q, t, codes, out, M, N, K, stream);       // 32 x 128
+    int cfg = tiles(128, 128) >= kCUs ? 0 : tiles(64, 128) >= kCUs ? 3 : 4;
+    PREFILL_TUNE_OVERRIDE
+    switch (cfg) {
+        case 1: return launch_cfg<2, 8, 4, 1, 1>(q, t, codes, out, M, N, K, stream);
+        case 2: return launch_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 3: return launch_cfg<2, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 4: return launch_cfg<1, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 5: return launch_cfg<4, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        default: return launch_cfg<4, 4, 2, 2, 1>(q, t, codes, out, M, N, K, stream);
+    }
 }
 
 }  // namespace pq2

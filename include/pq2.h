@@ -37,8 +37,9 @@
  *
  * ERRORS: arguments are validated on the host before anything is enqueued:
  *  PQ2_ERR_NULL  a required pointer is NULL;
- *  PQ2_ERR_SHAPE M < 1, N < 1, K < 128, K % 128 != 0, or a dimension above
- *                PQ2_MAX_DIM;
+ *  PQ2_ERR_SHAPE M < 1, N < 1, K < 128, K % 128 != 0, M or N above
+ *                PQ2_MAX_DIM, or K above PQ2_MAX_K (the kernels address a
+ *                block's rows with 32-bit offsets);
  *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above;
  *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots);
  *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
@@ -58,6 +59,7 @@ extern "C" {
 #define PQ2_ABI_VERSION 1
 #define PQ2_GROUP 128
 #define PQ2_MAX_DIM (1LL << 30)
+#define PQ2_MAX_K (1LL << 24)
 
 typedef enum {
     PQ2_OK = 0,

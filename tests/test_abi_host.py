@@ -51,6 +51,7 @@ def test_quantize_validation():
     assert f(P, P, P, P, 1, 0, None) == ERR_SHAPE
     assert f(P, P, P, P, 1, -128, None) == ERR_SHAPE
     assert f(P, P, P, P, (1 << 30) + 1, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, (1 << 24) + 128, None) == ERR_SHAPE   # K above PQ2_MAX_K
     assert f(P + 4, P, P, P, 1, 128, None) == ERR_ALIGN     # x needs 16 B
     assert f(P, P + 8, P, P, 1, 128, None) == ERR_ALIGN     # q needs 16 B
     assert f(P, P, P + 2, P, 1, 128, None) == ERR_ALIGN     # s needs 4 B
@@ -65,6 +66,8 @@ def test_gemm_validation():
     assert f(P, P, P, P, P, P, 1, 0, 128, None) == ERR_SHAPE
     assert f(P, P, P, P, P, P, 0, 8, 128, None) == ERR_SHAPE
     assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1, 8, (1 << 24) + 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1, (1 << 30) + 1, 128, None) == ERR_SHAPE
     assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
     assert f(P, P, P, P, P + 1, P, 1, 8, 128, None) == ERR_ALIGN   # wscale needs 2 B
     assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
