@@ -253,7 +253,7 @@ def report_gemm(args, wl, r, torch):
     M, N, K = r["M"], r["N"], r["K"]
     step_bytes = gemm_bytes(M, N, K) + quant_bytes(M, K)
     prefill = M > 16
-    path = "gemv_m1" if M == 1 else ("small_mfma" if M <= 16 else "prefill_mfma")
+    path = "gemv_dot4" if M <= 2 else ("small_mfma" if M <= 16 else "prefill_mfma")
     if prefill:
         value = gemm_ops(M, N, K) / (r["ms_step"] * 1e-3) / 1e12
         unit = "TOP/s"

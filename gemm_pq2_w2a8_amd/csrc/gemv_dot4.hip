@@ -1,4 +1,4 @@
-// gemv_m1.hip -- K2: the M = 1 PQ2_0 GEMV on v_dot4.
+// gemv_dot4.hip -- K2: the PQ2_0 GEMV on v_dot4 for 1 to 4 token rows.
 //
 // Algorithm (page "Making a ternary reasoning model fast in vLLM", section
 // "One token at a time: plain Triton is enough"): activations are in plane
@@ -9,7 +9,11 @@
 // then scaled by s[g] * ws[n][g] in float32 and summed over groups. The page
 // also found independent dot4 accumulators and a one-stage loop best for one
 // token (page "Chasing llama.cpp at batch one", section "The win: a program
-// just for one token").
+// just for one token"). The same page series notes that plane dot products
+// turn arithmetic-bound from about three tokens (section "One token at a
+// time", last paragraph); on gfx950 the per-word bit work is shared by the
+// tokens and the dot4 rate leaves room for up to four, so MT = 1, 2 or 4
+// token rows run here and larger batches take the MFMA kernel.
 //
 // gfx950 mapping:
 //  * A "chunk" is 16 bytes of one row = 4 code words = half a group. A wave
@@ -17,10 +21,11 @@
 //    chunks cs, cs+CL, cs+2CL, ... of RP rows. CL = gcd(K/64, 64), so every
 //    lane is busy on every iteration and each load instruction covers RL
 //    contiguous runs of CL*16 bytes (coalesced HBM streaming).
-//  * K is processed in LDS windows of up to 32768 activations (one window
-//    for every K up to that). Per window the block stages q into LDS
-//    chunk-major by plane ([plane][chunk] of 16 bytes, so the CL lanes of a
-//    slot read consecutive 16-byte words), with s and t.
+//  * K is processed in LDS windows of up to 32768/MT activations per token
+//    (one window for every K up to that). Per window the block stages the
+//    MT token rows of q into LDS chunk-major by plane ([token][plane][chunk]
+//    of 16 bytes, so the CL lanes of a slot read consecutive 16-byte words),
+//    with s and t.
 //  * Memory-level parallelism: a lane issues the code loads (and the weight
 //    scale of each chunk's group) of IB chunk iterations x RP rows at once
 //    (one batch) and the next batch is in flight while the current one is
@@ -29,11 +34,14 @@
 //  * Planes 0 and 2 are masked to bits 0..1 (plane 2 after one shift by 4);
 //    planes 1 and 3 are masked in place at bits 2..3, which is 4 * code, and
 //    go to a second accumulator divided by 4 (exactly) before the two are
-//    added: five bit operations and four v_dot4 per code word.
-//  * The even lane of a chunk pair seeds its accumulator with -t[g]; the two
-//    half-group sums meet through a DPP lane swap, giving the exact group dot
-//    on both lanes. The even lane applies the float32 epilogue.
+//    added: five bit operations per code word shared by all tokens, and four
+//    v_dot4 per code word and token.
+//  * The even lane of a chunk pair seeds its accumulators with -t[m][g]; the
+//    two half-group sums meet through a DPP lane swap, giving the exact group
+//    dot on both lanes. The even lane applies the float32 epilogue.
 //  * Rows are reduced over their CL lanes with a fixed butterfly at the end.
+//  * Token rows past M (M = 3 runs as MT = 4) read token M-1 and are never
+//    stored.
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
@@ -41,11 +49,20 @@ namespace pq2 {
 
 namespace {
 
+// u / n for 0 <= u < MT * n, without a division: MT - 1 comparisons.
+template <int MT>
+__device__ __forceinline__ int token_of(int u, int n) {
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < MT; ++i) m += u >= i * n ? 1 : 0;
+    return m;
+}
+
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kLoadsPerBatch = 8;                 // uint4 code loads per lane per batch
-constexpr int64_t kMaxWindow = 32768;             // activations per LDS window
-constexpr int kQStagePer = kMaxWindow / 16 / kGemvThreads;   // q chunks per thread
+constexpr int64_t kMaxStage = 32768;              // activations staged per window (all tokens)
+constexpr int kQStagePer = kMaxStage / 16 / kGemvThreads;   // q chunks per thread
 
 template <int LOG_CL, int RP>
 struct GemvShape {
@@ -56,14 +73,14 @@ struct GemvShape {
     static constexpr int IB = kLoadsPerBatch / RP;    // chunk iterations per batch
 };
 
-// LDS bytes per group of a window: q (128), s (4), t (4).
+// LDS bytes per group and token of a window: q (128), s (4), t (4).
 constexpr int64_t kLdsPerGroup = kGroup + 8;
 
-template <int LOG_CL, int RP, bool DOTS>
-__global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
+template <int LOG_CL, int RP, int MT, bool DOTS>
+__global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, int64_t N, int64_t K, int64_t window) {
+    int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K, int64_t window) {
     using S = GemvShape<LOG_CL, RP>;
     constexpr int CL = S::CL, RL = S::RL, IB = S::IB;
     extern __shared__ uint4 smem[];
@@ -88,9 +105,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
         wsp[r] = ws + rc * G;
     }
 
-    float facc[RP];
+    float facc[RP][MT];
 #pragma unroll
-    for (int r = 0; r < RP; ++r) facc[r] = 0.0f;
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) facc[r][m] = 0.0f;
 
     for (int64_t k0 = 0; k0 < K; k0 += window) {
         // window extent; all wave-uniform, kept in scalar registers
@@ -125,31 +144,43 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
         };
         load_batch(bufa, wsa, 0);
 
-        // stage the window: q [plane][chunk], s [g], t [g]; all loads of the
-        // staging are issued (clamped, unpredicated) before any LDS store, so
-        // they share one memory round trip with the first code batch
-        float *s_l = reinterpret_cast<float *>(smem + 4 * wchunks);
-        int32_t *t_l = reinterpret_cast<int32_t *>(s_l + wg);
+        // stage the window: q [token][plane][chunk], s [token][g],
+        // t [token][g]; all loads of the staging are issued (clamped,
+        // unpredicated) before any LDS store, so they share one memory round
+        // trip with the first code batch
+        float *s_l = reinterpret_cast<float *>(smem + 4 * MT * wchunks);
+        int32_t *t_l = reinterpret_cast<int32_t *>(s_l + MT * wg);
         {
-            const uint4 *qg = reinterpret_cast<const uint4 *>(q + k0);
-            const int nq = wk / 16;
+            const int nq = wk / 16;                   // 16-byte q chunks per token
             uint4 qs[kQStagePer];
 #pragma unroll
-            for (int i = 0; i < kQStagePer; ++i)
-                qs[i] = qg[min((int)threadIdx.x + i * kGemvThreads, nq - 1)];
-            const int gi = min((int)threadIdx.x, wg - 1);
+            for (int i = 0; i < kQStagePer; ++i) {
+                int u = (int)threadIdx.x + i * kGemvThreads;
+                u = u < MT * nq ? u : MT * nq - 1;
+                const int m = token_of<MT>(u, nq), uu = u - m * nq;
+                const int64_t mc = m < M ? m : M - 1;
+                qs[i] = reinterpret_cast<const uint4 *>(q + mc * K + k0)[uu];
+            }
             float sv = 0.0f;
-            if (!DOTS) sv = s[g0 + gi];
-            const int32_t tv = t[g0 + gi];
+            int32_t tv = 0;
+            {
+                int e = (int)threadIdx.x;
+                e = e < MT * wg ? e : MT * wg - 1;
+                const int m = token_of<MT>(e, wg), gi = e - m * wg;
+                const int64_t mc = m < M ? m : M - 1;
+                if (!DOTS) sv = s[mc * G + g0 + gi];
+                tv = t[mc * G + g0 + gi];
+            }
 #pragma unroll
             for (int i = 0; i < kQStagePer; ++i) {
                 const int u = threadIdx.x + i * kGemvThreads;
-                if (u < nq) {
-                    const int g = u >> 3, p = (u >> 1) & 3, hh = u & 1;
-                    smem[p * wchunks + 2 * g + hh] = qs[i];
+                if (u < MT * nq) {
+                    const int m = token_of<MT>(u, nq), uu = u - m * nq;
+                    const int g = uu >> 3, p = (uu >> 1) & 3, hh = uu & 1;
+                    smem[(m * 4 + p) * wchunks + 2 * g + hh] = qs[i];
                 }
             }
-            if ((int)threadIdx.x < wg) {
+            if ((int)threadIdx.x < MT * wg) {
                 if (!DOTS) s_l[threadIdx.x] = sv;
                 t_l[threadIdx.x] = tv;
             }
@@ -163,39 +194,58 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
                 if (it0 + b >= iters) break;
                 const int c = cs + CL * (it0 + b);    // chunk within window
                 const int g = c >> 1;                 // group within window
-                uint4 qv[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) qv[p] = smem[p * wchunks + c];
-                const int tg = t_l[g];
-                float sg = 0.0f;
-                if (!DOTS) sg = s_l[g];
+                // the planes of every code word of the RP rows, shared by the tokens
+                uint32_t pa0[RP][4], pa1[RP][4], pa2[RP][4], pa3[RP][4];
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
                     const uint4 w = buf[b][r];
                     const uint32_t wr[4] = {w.x, w.y, w.z, w.w};
-                    const uint32_t p0[4] = {qv[0].x, qv[0].y, qv[0].z, qv[0].w};
-                    const uint32_t p1[4] = {qv[1].x, qv[1].y, qv[1].z, qv[1].w};
-                    const uint32_t p2[4] = {qv[2].x, qv[2].y, qv[2].z, qv[2].w};
-                    const uint32_t p3[4] = {qv[3].x, qv[3].y, qv[3].z, qv[3].w};
-                    int da = h ? 0 : -tg;   // planes 0 and 2, and the -sum(q) offset
-                    int db = 0;             // planes 1 and 3, in place: 4 * (their dot)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const uint32_t wd = wr[jj];
                         const uint32_t hi = wd >> 4;
-                        da = dot4(wd & kPlaneMask, p0[jj], da);
-                        db = dot4(wd & kPlaneMaskX4, p1[jj], db);
-                        da = dot4(hi & kPlaneMask, p2[jj], da);
-                        db = dot4(hi & kPlaneMaskX4, p3[jj], db);
+                        pa0[r][jj] = wd & kPlaneMask;
+                        pa1[r][jj] = wd & kPlaneMaskX4;
+                        pa2[r][jj] = hi & kPlaneMask;
+                        pa3[r][jj] = hi & kPlaneMaskX4;
                     }
-                    const int half_dot = da + (db >> 2);            // db is a multiple of 4
-                    const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
-                    if (DOTS) {
-                        const int64_t row = row0 + (int64_t)r * RL;
-                        if (!h && row < N) d[row * G + g0 + g] = dot;
-                    } else {
-                        const float cf = sg * half_bits_to_float(wsv[b][r]);
-                        facc[r] = fmaf((float)dot, h ? 0.0f : cf, facc[r]);
+                }
+                float cw[RP];
+                if (!DOTS) {
+#pragma unroll
+                    for (int r = 0; r < RP; ++r) cw[r] = half_bits_to_float(wsv[b][r]);
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    uint4 qv[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) qv[p] = smem[(m * 4 + p) * wchunks + c];
+                    const int tg = t_l[m * wg + g];
+                    float sg = 0.0f;
+                    if (!DOTS) sg = s_l[m * wg + g];
+                    const uint32_t p0[4] = {qv[0].x, qv[0].y, qv[0].z, qv[0].w};
+                    const uint32_t p1[4] = {qv[1].x, qv[1].y, qv[1].z, qv[1].w};
+                    const uint32_t p2[4] = {qv[2].x, qv[2].y, qv[2].z, qv[2].w};
+                    const uint32_t p3[4] = {qv[3].x, qv[3].y, qv[3].z, qv[3].w};
+#pragma unroll
+                    for (int r = 0; r < RP; ++r) {
+                        int da = h ? 0 : -tg;   // planes 0 and 2, and the -sum(q) offset
+                        int db = 0;             // planes 1 and 3, in place: 4 * (their dot)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            da = dot4(pa0[r][jj], p0[jj], da);
+                            db = dot4(pa1[r][jj], p1[jj], db);
+                            da = dot4(pa2[r][jj], p2[jj], da);
+                            db = dot4(pa3[r][jj], p3[jj], db);
+                        }
+                        const int half_dot = da + (db >> 2);            // db is a multiple of 4
+                        const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
+                        if (DOTS) {
+                            const int64_t row = row0 + (int64_t)r * RL;
+                            if (!h && m < M && row < N) d[(m * N + row) * G + g0 + g] = dot;
+                        } else {
+                            facc[r][m] = fmaf((float)dot, h ? 0.0f : sg * cw[r], facc[r][m]);
+                        }
                     }
                 }
             }
@@ -222,29 +272,33 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_m1_kernel(
     if (!DOTS) {
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-            const float v = segment_sum<CL>(facc[r]);
             const int64_t row = row0 + (int64_t)r * RL;
-            if (cs == 0 && row < N) y[row] = v;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float v = segment_sum<CL>(facc[r][m]);
+                if (cs == 0 && m < M && row < N) y[m * N + row] = v;
+            }
         }
     }
 }
 
-template <int LOG_CL, int RP>
+template <int LOG_CL, int RP, int MT>
 hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                      const GemmOut &out, int64_t N, int64_t K, hipStream_t stream) {
+                      const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     using S = GemvShape<LOG_CL, RP>;
     const int64_t blocks = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
     const bool dots = out.d != nullptr;
-    const int64_t window = K < kMaxWindow ? K : kMaxWindow;
-    const size_t lds = (size_t)((window / kGroup) * kLdsPerGroup);
+    constexpr int64_t kWindow = kMaxStage / MT;       // a multiple of 64 * CL for every CL
+    const int64_t window = K < kWindow ? K : kWindow;
+    const size_t lds = (size_t)(MT * (window / kGroup) * kLdsPerGroup);
     if (dots) {
-        hipLaunchKernelGGL((gemv_m1_kernel<LOG_CL, RP, true>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true>), dim3((unsigned)blocks),
                            dim3(kGemvThreads), lds, stream, q, nullptr, t, codes, nullptr,
-                           nullptr, out.d, N, K, window);
+                           nullptr, out.d, M, N, K, window);
     } else {
-        hipLaunchKernelGGL((gemv_m1_kernel<LOG_CL, RP, false>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false>), dim3((unsigned)blocks),
                            dim3(kGemvThreads), lds, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, N, K, window);
+                           nullptr, M, N, K, window);
     }
     return hipGetLastError();
 }
@@ -253,26 +307,28 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 // covers four rows, and every q word read from LDS serves both rows.
 template <int LOG_CL>
 hipError_t launch_cl(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                     const GemmOut &out, int64_t N, int64_t K, hipStream_t stream) {
+                     const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     constexpr int RP = (LOG_CL >= 5) ? 2 : 1;
-    return launch_cfg<LOG_CL, RP>(q, t, codes, out, N, K, stream);
+    if (M == 1) return launch_cfg<LOG_CL, RP, 1>(q, t, codes, out, M, N, K, stream);
+    if (M == 2) return launch_cfg<LOG_CL, RP, 2>(q, t, codes, out, M, N, K, stream);
+    return launch_cfg<LOG_CL, RP, 4>(q, t, codes, out, M, N, K, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemv_m1(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                          const GemmOut &out, int64_t N, int64_t K, hipStream_t stream) {
+hipError_t launch_gemv(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                       const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     // chunk lanes per row: the largest power of two <= 64 dividing K/64
     const int64_t chunks = K / 64;
     int64_t cl = chunks & -chunks;
     if (cl > 64) cl = 64;
     switch (cl) {
-        case 2: return launch_cl<1>(q, t, codes, out, N, K, stream);
-        case 4: return launch_cl<2>(q, t, codes, out, N, K, stream);
-        case 8: return launch_cl<3>(q, t, codes, out, N, K, stream);
-        case 16: return launch_cl<4>(q, t, codes, out, N, K, stream);
-        case 32: return launch_cl<5>(q, t, codes, out, N, K, stream);
-        default: return launch_cl<6>(q, t, codes, out, N, K, stream);
+        case 2: return launch_cl<1>(q, t, codes, out, M, N, K, stream);
+        case 4: return launch_cl<2>(q, t, codes, out, M, N, K, stream);
+        case 8: return launch_cl<3>(q, t, codes, out, M, N, K, stream);
+        case 16: return launch_cl<4>(q, t, codes, out, M, N, K, stream);
+        case 32: return launch_cl<5>(q, t, codes, out, M, N, K, stream);
+        default: return launch_cl<6>(q, t, codes, out, M, N, K, stream);
     }
 }
 

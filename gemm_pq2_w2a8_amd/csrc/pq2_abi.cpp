@@ -24,7 +24,7 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
                     hipStream_t stream) {
     switch (path) {
         case PQ2_PATH_GEMV:
-            return from_hip(pq2::launch_gemv_m1(q, t, codes, out, N, K, stream));
+            return from_hip(pq2::launch_gemv(q, t, codes, out, M, N, K, stream));
         case PQ2_PATH_SMALL:
             return from_hip(pq2::launch_small(q, t, codes, out, M, N, K, stream));
         case PQ2_PATH_PREFILL:
@@ -34,8 +34,12 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
     }
 }
 
+#ifndef PQ2_GEMV_AUTO_M
+#define PQ2_GEMV_AUTO_M 2   // largest M that pq2_gemm sends to the dot4 GEMV
+#endif
+
 int auto_path(int64_t M, int64_t K) {
-    if (M == 1) return PQ2_PATH_GEMV;
+    if (M <= PQ2_GEMV_AUTO_M) return PQ2_PATH_GEMV;
     if (M <= 16 && K <= pq2::kSmallMaxK) return PQ2_PATH_SMALL;
     return PQ2_PATH_PREFILL;
 }
@@ -90,7 +94,7 @@ pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t 
     if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(t, 4) || !aligned(d, 4))
         return PQ2_ERR_ALIGN;
     if (path == PQ2_PATH_AUTO) path = auto_path(M, K);
-    if (path == PQ2_PATH_GEMV && M != 1) return PQ2_ERR_ARG;
+    if (path == PQ2_PATH_GEMV && M > pq2::kGemvMaxM) return PQ2_ERR_ARG;
     if (path == PQ2_PATH_SMALL && (M > 16 || K > pq2::kSmallMaxK)) return PQ2_ERR_ARG;
     if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PREFILL) return PQ2_ERR_ARG;
     const pq2::GemmOut out{nullptr, d, nullptr, nullptr};

@@ -19,8 +19,11 @@ struct GemmOut {
 hipError_t launch_quantize(const float *x, int8_t *q, float *s, int32_t *t, int64_t M,
                            int64_t K, hipStream_t stream);
 
-hipError_t launch_gemv_m1(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                          const GemmOut &out, int64_t N, int64_t K, hipStream_t stream);
+// The dot4 GEMV runs 1 to kGemvMaxM token rows.
+constexpr int64_t kGemvMaxM = 4;
+
+hipError_t launch_gemv(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                       const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // The small-batch kernel stages 3 * 16 * (G + 1) words of scales in LDS.
 constexpr int64_t kSmallMaxK = 32768;

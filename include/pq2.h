@@ -73,7 +73,7 @@ typedef enum {
 /* Kernel path selectors for pq2_gemm_group_dots. */
 enum {
     PQ2_PATH_AUTO = 0,      /* same choice as pq2_gemm */
-    PQ2_PATH_GEMV = 1,      /* M == 1 only: the v_dot4 GEMV */
+    PQ2_PATH_GEMV = 1,      /* M <= 4 only: the v_dot4 GEMV */
     PQ2_PATH_SMALL = 2,     /* M <= 16, K <= 32768: the small-batch MFMA kernel */
     PQ2_PATH_PREFILL = 3    /* any M: the tiled MFMA GEMM */
 };
@@ -99,9 +99,10 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
 
 /*
  * y = the PQ2_0 product defined above. The kernel depends on M:
- *   M == 1        -> GEMV streaming code words into v_dot4 (2-bit planes
- *                    masked out of each 32-bit word, no decode step);
- *   2 <= M <= 16  -> small-batch kernel on int8 MFMA, tokens padded to 16
+ *   1 <= M <= 2   -> GEMV streaming code words into v_dot4 (2-bit planes
+ *                    masked out of each 32-bit word, no decode step; each
+ *                    word serves every token row);
+ *   3 <= M <= 16  -> small-batch kernel on int8 MFMA, tokens padded to 16
  *                    (K <= 32768; larger K takes the tiled kernel);
  *   M >= 17       -> tiled int8 MFMA GEMM (prefill).
  * Group dots are exact int32; the float32 epilogue sums the G terms in an
@@ -115,7 +116,7 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
  * Test and diagnostic entry: runs the main loop of the selected kernel path
  * but stores the exact per-group dots instead of the float epilogue:
  *   d int32 [M][N][G],  d[m][n][g] = D[m][n][g] as defined above.
- * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M == 1 and
+ * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M <= 4 and
  * PQ2_PATH_SMALL requires M <= 16 and K <= 32768 (else PQ2_ERR_ARG).
  */
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t,

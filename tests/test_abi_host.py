@@ -77,7 +77,7 @@ def test_group_dots_validation():
     f = pq2.lib.pq2_gemm_group_dots
     assert f(P, P, P, None, 1, 8, 128, 0, None) == ERR_NULL
     assert f(P, P, P, P, 1, 8, 100, 0, None) == ERR_SHAPE
-    assert f(P, P, P, P, 2, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG
+    assert f(P, P, P, P, 5, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG   # GEMV: M <= 4
     assert f(P, P, P, P, 17, 8, 128, pq2.PATH_SMALL, None) == ERR_ARG
     assert f(P, P, P, P, 16, 8, 32768 + 128, pq2.PATH_SMALL, None) == ERR_ARG
     assert f(P, P, P, P, 1, 8, 128, 7, None) == ERR_ARG

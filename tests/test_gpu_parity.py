@@ -118,6 +118,23 @@ def test_group_dots_gemv(pq2, N, K):
                                   oracle.group_dots(qn, codes))
 
 
+GEMV_TOKEN_SHAPES = [(M, N, K) for M in (2, 3, 4)
+                     for (N, K) in ((1, 128), (7, 384), (300, 640), (130, 5120), (257, 6144),
+                                    (65, 8320), (33, 17408))]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_TOKEN_SHAPES)
+def test_group_dots_gemv_tokens(pq2, M, N, K):
+    """The dot4 GEMV with 2 to 4 token rows (M = 3 runs as 4 with a padded row);
+    K = 8320 and 17408 span several LDS windows."""
+    print(f"dots gemv M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 100 + N * 7 + K)
+    qn, t = rand_q(M, K, rng)
+    codes = synth.draw_codes(N, K, rng)
+    np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, pq2.PATH_GEMV),
+                                  oracle.group_dots(qn, codes))
+
+
 SMALL_SHAPES = [(M, N, K) for M in (1, 2, 3, 8, 16) for (N, K) in ((1, 128), (17, 640), (100, 5120))]
 
 
@@ -144,7 +161,7 @@ def test_group_dots_prefill(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
-@pytest.mark.parametrize("path,M", [(1, 1), (2, 5), (3, 20)])
+@pytest.mark.parametrize("path,M", [(1, 1), (1, 4), (2, 5), (3, 20)])
 def test_code3_is_plus_two(pq2, path, M):
     """Code 3 is not a PQ2_0 code; both sides decode it as +2."""
     rng = np.random.default_rng(path)
@@ -155,7 +172,7 @@ def test_code3_is_plus_two(pq2, path, M):
     np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, path), oracle.group_dots(qn, codes))
 
 
-@pytest.mark.parametrize("path,M", [(1, 1), (2, 16), (3, 130)])
+@pytest.mark.parametrize("path,M", [(1, 1), (1, 3), (2, 16), (3, 130)])
 def test_extreme_dots(pq2, path, M):
     """q = +-127 everywhere with codes 2 or 0: |D| = 16256, the int32 extreme of a group."""
     N, K = 20, 384
@@ -172,7 +189,8 @@ def test_extreme_dots(pq2, path, M):
 
 # ---------------------------------------------------------------- float32 output
 
-Y_SHAPES = [(1, 256, 512), (1, 100, 640), (2, 300, 1024), (5, 129, 384), (16, 64, 5120),
+Y_SHAPES = [(1, 256, 512), (1, 100, 640), (2, 300, 1024), (3, 300, 1024), (4, 257, 6144),
+            (4, 33, 17408), (5, 129, 384), (16, 64, 5120),
             (17, 200, 640), (128, 256, 1024), (200, 130, 384)]
 
 
@@ -241,6 +259,8 @@ FULL = [
     ("decode_gemv", 1, 5120, 6144, synth.UNIFORM_CODES, 0.0),
     ("layer_qkv", 1, 6144, 5120, synth.UNIFORM_CODES, 0.0),
     ("small_m2_oproj", 2, 5120, 6144, synth.UNIFORM_CODES, 0.01),
+    ("small_m4_up", 4, 17408, 5120, synth.UNIFORM_CODES, 0.01),
+    ("small_m3_down", 3, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("small_m16_up", 16, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("small_m8_down", 8, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
@@ -275,7 +295,8 @@ def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
     np.testing.assert_array_equal(yu[mm, nn], Ds.sum(-1).astype(np.float32))
 
 
-@pytest.mark.parametrize("M,N,K,path", [(1, 5120, 6144, 1), (16, 5120, 6144, 2),
+@pytest.mark.parametrize("M,N,K,path", [(1, 5120, 6144, 1), (4, 5120, 6144, 1),
+                                        (2, 2048, 17408, 1), (16, 5120, 6144, 2),
                                         (16, 2048, 17408, 2), (256, 1024, 5120, 3)])
 def test_full_row_dots(pq2, M, N, K, path):
     """Exact per-group dots over whole decode-size weight matrices."""
