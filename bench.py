@@ -3,7 +3,9 @@
 A step is one pass of the hot path over one batch: pq2_quantize_act on the
 activations, then pq2_gemm against the next weight matrix of a rotating set
 (the set is larger than the 256 MB Infinity Cache, so weights stream from
-HBM). Inputs are resident in HBM before the timed region starts.
+HBM). Inputs are resident in HBM before the timed region starts. For
+M <= 4 the single-launch pq2_linear (quantisation inside the GEMV) is timed
+too and reported in the config (fused_step_us).
 
 Default workload: decode GEMV, M = 1, N = 5120, K = 6144, 64 rotating
 matrices. ``--workload`` selects another configuration; ``--sweep`` prints
@@ -42,6 +44,14 @@ def gemm_bytes(M, N, K):
 def quant_bytes(M, K):
     G = K // GROUP
     return 4 * M * K + M * K + 8 * M * G
+
+
+LINEAR_MAX_M = 4   # PQ2_LINEAR_MAX_M
+
+
+def step_bytes(M, N, K):
+    """Algorithmic HBM bytes of quantise + GEMM (q, s, t written and read back)."""
+    return gemm_bytes(M, N, K) + quant_bytes(M, K)
 
 
 def gemm_ops(M, N, K):
@@ -117,9 +127,8 @@ def cpu_baseline(wl, budget_s=10.0):
         if el >= budget_s:
             break
     per_call = el / calls
-    step_bytes = gemm_bytes(wl.m, wl.n, wl.k) + quant_bytes(wl.m, wl.k)
     return {
-        "value": step_bytes / per_call / 1e9,
+        "value": step_bytes(wl.m, wl.n, wl.k) / per_call / 1e9,
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
@@ -204,16 +213,25 @@ def run_gemm(args, wl, torch, pq2):
     xp, qp, sp, tp, yp = x.data_ptr(), q.data_ptr(), s.data_ptr(), t.data_ptr(), y.data_ptr()
     cps = [c.data_ptr() for c in codes]
     wps = [w.data_ptr() for w in scales]
-    quant, gemm = lib.pq2_quantize_act, lib.pq2_gemm
+    quant, gemm, linear = lib.pq2_quantize_act, lib.pq2_gemm, lib.pq2_linear
+    fused = M <= LINEAR_MAX_M
 
-    def step(i):
+    def step_unfused(i):
         st1 = quant(xp, qp, sp, tp, M, K, stream)
         st2 = gemm(qp, sp, tp, cps[i % R], wps[i % R], yp, M, N, K, stream)
         if st1 or st2:
             raise pq2.PQ2Error(st1 or st2)
 
+    def step_fused(i):
+        st = linear(xp, cps[i % R], wps[i % R], yp, M, N, K, stream)
+        if st:
+            raise pq2.PQ2Error(st)
+
+    step = step_unfused
     for i in range(args.warmup):
         step(i)
+        if fused:
+            step_fused(i)
     torch.cuda.synchronize()
     cyc_per_ms = spin_cycles_per_ms(torch)
 
@@ -238,36 +256,42 @@ def run_gemm(args, wl, torch, pq2):
         torch.cuda.synchronize()
         return a.elapsed_time(b), enq_ms, host_ms
 
-    # the whole step: quantise + GEMM
+    # the whole step
     wall0 = time.perf_counter()
     total_ms, enq_ms, _ = timed(step)
     wall = time.perf_counter() - wall0
-    # the GEMM kernel alone, back to back on the same stream (average launch
-    # duration including the dispatch gap between launches)
+    # pq2_gemm alone, back to back on the same stream (average launch duration
+    # including the dispatch gap between launches)
     gemm_total, _, _ = timed(lambda i: gemm(qp, sp, tp, cps[i % R], wps[i % R], yp, M, N, K, stream))
-    return dict(ms_step=total_ms / args.steps, gemm_ms=gemm_total / args.steps, wall=wall,
-                M=M, N=N, K=K, host_enqueue_ms=enq_ms, gpu_ms=total_ms)
+    out = dict(ms_step=total_ms / args.steps, gemm_ms=gemm_total / args.steps, wall=wall,
+               M=M, N=N, K=K, host_enqueue_ms=enq_ms, gpu_ms=total_ms, fused=fused)
+    out["kernel_ms"] = out["gemm_ms"]
+    if fused:
+        fus_total, _, _ = timed(step_fused)
+        out["fused_ms_step"] = fus_total / args.steps
+    return out
 
 
 def report_gemm(args, wl, r, torch):
     M, N, K = r["M"], r["N"], r["K"]
-    step_bytes = gemm_bytes(M, N, K) + quant_bytes(M, K)
+    sbytes = step_bytes(M, N, K)
     prefill = M > 16
+    fused = r["fused"]
     path = "gemv_dot4" if M <= 2 else ("small_mfma" if M <= 16 else "prefill_mfma")
     if prefill:
         value = gemm_ops(M, N, K) / (r["ms_step"] * 1e-3) / 1e12
         unit = "TOP/s"
-        achieved = gemm_ops(M, N, K) / (r["gemm_ms"] * 1e-3) / 1e12
+        achieved = gemm_ops(M, N, K) / (r["kernel_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TOP/s",
                 "frac": achieved / I8_PEAK_TOPS}
     else:
-        value = step_bytes / (r["ms_step"] * 1e-3) / 1e9
+        value = sbytes / (r["ms_step"] * 1e-3) / 1e9
         unit = "GB/s"
-        achieved = gemm_bytes(M, N, K) / (r["gemm_ms"] * 1e-3) / 1e9
+        achieved = gemm_bytes(M, N, K) / (r["kernel_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     roof["kernel"] = path
-    roof["kernel_us"] = r["gemm_ms"] * 1e3
+    roof["kernel_us"] = r["kernel_ms"] * 1e3
     roof["timing"] = ("HIP events around K back-to-back pq2_gemm launches (rotating weights); the "
                       "stream is held by a spin kernel while the host enqueues, so the events see "
                       "GPU time; includes the dispatch gap between launches")
@@ -278,12 +302,15 @@ def report_gemm(args, wl, r, torch):
         "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": wl.name, "M": M, "N": N, "K": K, "rotating_matrices": wl.rotate,
                    "step": "pq2_quantize_act + pq2_gemm",
-                   "algorithmic_bytes_per_step": step_bytes,
+                   "algorithmic_bytes_per_step": sbytes,
                    "gemm_bytes_per_call": gemm_bytes(M, N, K),
                    "gemm_int_ops_per_call": gemm_ops(M, N, K),
-                   "host_enqueue_ms": r["host_enqueue_ms"], "gpu_ms": r["gpu_ms"]},
+                   "host_enqueue_ms": r["host_enqueue_ms"], "gpu_ms": r["gpu_ms"],
+                   "pq2_gemm_us": r["gemm_ms"] * 1e3},
         "roofline": roof,
     }
+    if fused:
+        line["config"]["fused_step_us"] = r["fused_ms_step"] * 1e3
     if not args.no_cpu:
         line["cpu_baseline"] = (cpu_baseline_prefill(wl, args.cpu_seconds) if prefill
                                 else cpu_baseline(wl, args.cpu_seconds))
@@ -340,7 +367,7 @@ def run_layers(args, m, torch, pq2):
     ms = a.elapsed_time(b) / steps
     total = 0
     for (n, k) in synth.LAYER_SHAPES:
-        total += gemm_bytes(m, n, k) + quant_bytes(m, k)
+        total += step_bytes(m, n, k)
     total *= synth.N_LAYERS
     gbs = total / (ms * 1e-3) / 1e9
     return {"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps,
@@ -348,6 +375,7 @@ def run_layers(args, m, torch, pq2):
             "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
             "config": {"workload": f"layer64_m{m}", "M": m, "layers": synth.N_LAYERS,
                        "gemms_per_step": 5 * synth.N_LAYERS,
+                       "projection": "pq2_quantize_act + pq2_gemm",
                        "algorithmic_bytes_per_step": total},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,

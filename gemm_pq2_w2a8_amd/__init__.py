@@ -5,7 +5,7 @@ contiguity, their device pointers and the current HIP stream are passed to
 ``libpq2.so``, and a non-zero status raises :class:`PQ2Error`. Every step of
 the computation runs in the library's gfx950 kernels; there is no fallback.
 Importing this package raises if ``libpq2.so`` has not been built
-(``python -m gemm_pq2_w2a8_amd.build``).
+(``python gemm_pq2_w2a8_amd/build.py``).
 """
 
 from __future__ import annotations
@@ -23,7 +23,7 @@ GROUP = 128
 PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_PREFILL = 0, 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gemm_pq2_w2a8_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python gemm_pq2_w2a8_amd/build.py`")
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -39,10 +39,14 @@ lib.pq2_gemm.restype = ctypes.c_int
 lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.pq2_gemm_group_dots.restype = ctypes.c_int
 lib.pq2_gemm_group_dots.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
+lib.pq2_linear.restype = ctypes.c_int
+lib.pq2_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
+
+LINEAR_MAX_M = 4    # PQ2_LINEAR_MAX_M
 
 # Every extern "C" symbol declared in include/pq2.h.
 ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_gemm",
-               "pq2_gemm_group_dots")
+               "pq2_linear", "pq2_gemm_group_dots")
 
 
 class PQ2Error(RuntimeError):
@@ -118,6 +122,22 @@ def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Ten
                         wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
 
 
+def pq2_linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor, y: torch.Tensor,
+               stream=None) -> None:
+    """y float32 [M][N] from float32 x [M][K] in one launch (M <= LINEAR_MAX_M)."""
+    M, K = _mk(x)
+    N = int(codes.shape[0])
+    G = K // GROUP
+    _need(x, "x", torch.float32, (M, K))
+    _need(codes, "codes", torch.uint8, (N, K // 4))
+    if wscale.dtype == torch.float16:
+        wscale = wscale.view(torch.int16)
+    _need(wscale, "wscale", torch.int16, (N, G))
+    _need(y, "y", torch.float32, (M, N))
+    _check(lib.pq2_linear(x.data_ptr(), codes.data_ptr(), wscale.data_ptr(), y.data_ptr(),
+                          M, N, K, _stream(x, stream)))
+
+
 def pq2_gemm_group_dots(q: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
                         d: torch.Tensor, path: int = PATH_AUTO, stream=None) -> None:
     """d int32 [M][N][G] = exact group dots through the selected kernel path."""
@@ -147,10 +167,14 @@ def quantize_act(x: torch.Tensor, stream=None):
 
 def linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor,
            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Whole path: quantise x, then the PQ2_0 product; returns y float32 [M][N]."""
-    q, s, t = quantize_act(x, stream)
+    """Whole path, y float32 [M][N]: one pq2_linear launch for M <= LINEAR_MAX_M,
+    else pq2_quantize_act into torch-allocated q/s/t followed by pq2_gemm."""
     M = int(x.shape[0])
     N = int(codes.shape[0])
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if M <= LINEAR_MAX_M:
+        pq2_linear(x, codes, wscale, y, stream)
+        return y
+    q, s, t = quantize_act(x, stream)
     pq2_gemm(q, s, t, codes, wscale, y, stream)
     return y

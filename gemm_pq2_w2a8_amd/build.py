@@ -1,6 +1,7 @@
 """Build ``libpq2.so`` (the C-ABI library of include/pq2.h) for gfx950 with hipcc.
 
-Run ``python -m gemm_pq2_w2a8_amd.build`` (or call :func:`build`). Objects go to
+Run ``python gemm_pq2_w2a8_amd/build.py`` (or call :func:`build`); as a script it
+does not import the package, which needs a built library. Objects go to
 ``gemm_pq2_w2a8_amd/_build/``; the library is written next to this file.
 """
 

@@ -42,6 +42,10 @@
 //  * Rows are reduced over their CL lanes with a fixed butterfly at the end.
 //  * Token rows past M (M = 3 runs as MT = 4) read token M-1 and are never
 //    stored.
+//  * The fused variant (pq2_linear) reads float32 x instead of q, s, t: each
+//    block quantises its window in LDS with the quantiser's own arithmetic
+//    (quantize_groups32) while its first batch of code loads is in flight,
+//    which saves the separate quantise launch of a decode step.
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
@@ -76,11 +80,16 @@ struct GemvShape {
 // LDS bytes per group and token of a window: q (128), s (4), t (4).
 constexpr int64_t kLdsPerGroup = kGroup + 8;
 
-template <int LOG_CL, int RP, int MT, bool DOTS>
+// Groups quantised per 32-lane slot and pass in the fused variant.
+constexpr int kXRound = 8;
+
+template <int LOG_CL, int RP, int MT, bool DOTS, bool FUSED>
 __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
-    const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K, int64_t window) {
+    const float *__restrict__ x, const int8_t *__restrict__ q, const float *__restrict__ s,
+    const int32_t *__restrict__ t, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ ws, float *__restrict__ y, int32_t *__restrict__ d, int64_t M,
+    int64_t N, int64_t K, int64_t window) {
+    static_assert(!(FUSED && DOTS), "the fused variant writes y");
     using S = GemvShape<LOG_CL, RP>;
     constexpr int CL = S::CL, RL = S::RL, IB = S::IB;
     extern __shared__ uint4 smem[];
@@ -110,6 +119,32 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
     for (int r = 0; r < RP; ++r)
 #pragma unroll
         for (int m = 0; m < MT; ++m) facc[r][m] = 0.0f;
+
+    // Fused variant: the first pass of x loads goes out before the first code
+    // batch. Loads complete in issue order for the wait counter, so the block
+    // can then wait for x alone and quantise while the codes of its first
+    // batch are still in flight (later windows and passes are serial).
+    constexpr int kSlots = kGemvThreads / 32;
+    const int lane32 = threadIdx.x & 31, slot = threadIdx.x >> 5;
+    float4 xv[kXRound];
+    auto load_x = [&](int64_t kx, int base) {
+        const int wkx = (int)((K - kx < window) ? K - kx : window);
+        const int wgx = wkx / kGroup, ngx = MT * wgx;
+#pragma unroll
+        for (int i = 0; i < kXRound; ++i) {
+            int gi = base + slot + kSlots * i;
+            gi = gi < ngx ? gi : ngx - 1;
+            const int m = token_of<MT>(gi, wgx), gw = gi - m * wgx;
+            const int64_t mc = m < M ? m : M - 1;
+            xv[i] = *reinterpret_cast<const float4 *>(x + mc * K + kx + kGroup * gw + 4 * lane32);
+        }
+    };
+    if constexpr (FUSED) {
+        load_x(0, 0);
+        // keep the x loads ahead of the codes (no pass moves loads across)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     for (int64_t k0 = 0; k0 < K; k0 += window) {
         // window extent; all wave-uniform, kept in scalar registers
@@ -143,6 +178,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
             }
         };
         load_batch(bufa, wsa, 0);
+        if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
 
         // stage the window: q [token][plane][chunk], s [token][g],
         // t [token][g]; all loads of the staging are issued (clamped,
@@ -150,6 +186,40 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
         // trip with the first code batch
         float *s_l = reinterpret_cast<float *>(smem + 4 * MT * wchunks);
         int32_t *t_l = reinterpret_cast<int32_t *>(s_l + MT * wg);
+        if constexpr (FUSED) {
+            // quantise the window's MT x wg groups from x straight into the
+            // LDS layout: 32 lanes per group, kXRound groups per slot and pass,
+            // the same arithmetic as pq2_quantize_act (quantize_groups32)
+            uint32_t *qw = reinterpret_cast<uint32_t *>(smem);
+            const int ngr = MT * wg;
+            auto quantize_pass = [&](int base) {
+#pragma unroll
+                for (int i = 0; i < kXRound; ++i) {
+                    const int graw = base + slot + kSlots * i;
+                    const float4 xi[1] = {xv[i]};
+                    uint32_t word[1];
+                    float sc[1];
+                    int sm[1];
+                    quantize_groups32<1>(xi, lane32, word, sc, sm);   // all 32 lanes
+                    if (graw < ngr) {
+                        const int m = token_of<MT>(graw, wg), gw = graw - m * wg;
+                        const int p = lane32 & 3, j = lane32 >> 2;
+                        qw[((m * 4 + p) * wchunks + 2 * gw + (j >> 2)) * 4 + (j & 3)] = word[0];
+                        if (lane32 == 0) {
+                            s_l[m * wg + gw] = sc[0];
+                            t_l[m * wg + gw] = sm[0];
+                        }
+                    }
+                }
+            };
+            // pass 0 on the x loads issued ahead of the code batch (straight
+            // line, so the wait is for x alone); further passes load and wait
+            quantize_pass(0);
+            for (int base = kSlots * kXRound; base < ngr; base += kSlots * kXRound) {
+                load_x(k0, base);
+                quantize_pass(base);
+            }
+        } else
         {
             const int nq = wk / 16;                   // 16-byte q chunks per token
             uint4 qs[kQStagePer];
@@ -266,6 +336,14 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
                 if (it0 + 2 * IB >= iters) break;
             }
         }
+        if constexpr (FUSED) {
+            // the next window's first x pass (the last window reloads itself;
+            // unconditional, so the pending loads are the same on every path)
+            const int64_t last = ((K - 1) / window) * window;
+            load_x(k0 + window < K ? k0 + window : last, 0);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if (k0 + window < K) __syncthreads();    // window buffer is reused
     }
 
@@ -283,22 +361,25 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
 }
 
 template <int LOG_CL, int RP, int MT>
-hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
+hipError_t launch_cfg(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
                       const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     using S = GemvShape<LOG_CL, RP>;
     const int64_t blocks = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
-    const bool dots = out.d != nullptr;
     constexpr int64_t kWindow = kMaxStage / MT;       // a multiple of 64 * CL for every CL
     const int64_t window = K < kWindow ? K : kWindow;
     const size_t lds = (size_t)(MT * (window / kGroup) * kLdsPerGroup);
-    if (dots) {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), lds, stream, q, nullptr, t, codes, nullptr,
-                           nullptr, out.d, M, N, K, window);
+    if (x) {
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, true>), dim3((unsigned)blocks),
+                           dim3(kGemvThreads), lds, stream, x, nullptr, nullptr, nullptr, codes,
+                           out.ws, out.y, nullptr, M, N, K, window);
+    } else if (out.d) {
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true, false>), dim3((unsigned)blocks),
+                           dim3(kGemvThreads), lds, stream, nullptr, q, nullptr, t, codes,
+                           nullptr, nullptr, out.d, M, N, K, window);
     } else {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), lds, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, M, N, K, window);
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false>), dim3((unsigned)blocks),
+                           dim3(kGemvThreads), lds, stream, nullptr, q, out.s, t, codes, out.ws,
+                           out.y, nullptr, M, N, K, window);
     }
     return hipGetLastError();
 }
@@ -306,30 +387,43 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 // Two rows per lane when a row slot is wide (CL >= 32): each wave then still
 // covers four rows, and every q word read from LDS serves both rows.
 template <int LOG_CL>
-hipError_t launch_cl(const int8_t *q, const int32_t *t, const uint8_t *codes,
+hipError_t launch_cl(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
                      const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     constexpr int RP = (LOG_CL >= 5) ? 2 : 1;
-    if (M == 1) return launch_cfg<LOG_CL, RP, 1>(q, t, codes, out, M, N, K, stream);
-    if (M == 2) return launch_cfg<LOG_CL, RP, 2>(q, t, codes, out, M, N, K, stream);
-    return launch_cfg<LOG_CL, RP, 4>(q, t, codes, out, M, N, K, stream);
+    if (M == 1) return launch_cfg<LOG_CL, RP, 1>(x, q, t, codes, out, M, N, K, stream);
+    if (M == 2) return launch_cfg<LOG_CL, RP, 2>(x, q, t, codes, out, M, N, K, stream);
+    return launch_cfg<LOG_CL, RP, 4>(x, q, t, codes, out, M, N, K, stream);
+}
+
+// x != nullptr: the fused variant (quantises x itself); else q, t from
+// pq2_quantize_act.
+hipError_t launch_any(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
+                      const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    // chunk lanes per row: the largest power of two <= 64 dividing K/64
+    const int64_t chunks = K / 64;
+    int64_t cl = chunks & -chunks;
+    if (cl > 64) cl = 64;
+    switch (cl) {
+        case 2: return launch_cl<1>(x, q, t, codes, out, M, N, K, stream);
+        case 4: return launch_cl<2>(x, q, t, codes, out, M, N, K, stream);
+        case 8: return launch_cl<3>(x, q, t, codes, out, M, N, K, stream);
+        case 16: return launch_cl<4>(x, q, t, codes, out, M, N, K, stream);
+        case 32: return launch_cl<5>(x, q, t, codes, out, M, N, K, stream);
+        default: return launch_cl<6>(x, q, t, codes, out, M, N, K, stream);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_gemv(const int8_t *q, const int32_t *t, const uint8_t *codes,
                        const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    // chunk lanes per row: the largest power of two <= 64 dividing K/64
-    const int64_t chunks = K / 64;
-    int64_t cl = chunks & -chunks;
-    if (cl > 64) cl = 64;
-    switch (cl) {
-        case 2: return launch_cl<1>(q, t, codes, out, M, N, K, stream);
-        case 4: return launch_cl<2>(q, t, codes, out, M, N, K, stream);
-        case 8: return launch_cl<3>(q, t, codes, out, M, N, K, stream);
-        case 16: return launch_cl<4>(q, t, codes, out, M, N, K, stream);
-        case 32: return launch_cl<5>(q, t, codes, out, M, N, K, stream);
-        default: return launch_cl<6>(q, t, codes, out, M, N, K, stream);
-    }
+    return launch_any(nullptr, q, t, codes, out, M, N, K, stream);
+}
+
+hipError_t launch_gemv_fused(const float *x, const uint8_t *codes, const uint16_t *ws, float *y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    const GemmOut out{y, nullptr, nullptr, ws};
+    return launch_any(x, nullptr, nullptr, codes, out, M, N, K, stream);
 }
 
 }  // namespace pq2

@@ -57,7 +57,7 @@ const char *pq2_status_str(int status) {
         case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128, K <= 2^24";
         case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
         case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
-        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M";
+        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M, or M too large for pq2_linear";
         default: return "PQ2 unknown status";
     }
 }
@@ -83,6 +83,19 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uin
         return PQ2_ERR_ALIGN;
     const pq2::GemmOut out{y, nullptr, s, wscale};
     return run_path(auto_path(M, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+}
+
+pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
+                      int64_t M, int64_t N, int64_t K, void *hip_stream) {
+    static_assert(PQ2_LINEAR_MAX_M <= pq2::kGemvMaxM, "the fused GEMV covers pq2_linear");
+    if (!x || !codes || !wscale || !y) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, N, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(wscale, 2) || !aligned(y, 4))
+        return PQ2_ERR_ALIGN;
+    if (M > PQ2_LINEAR_MAX_M) return PQ2_ERR_ARG;
+    return from_hip(pq2::launch_gemv_fused(x, codes, wscale, y, M, N, K,
+                                           static_cast<hipStream_t>(hip_stream)));
 }
 
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,

@@ -51,6 +51,148 @@ __device__ __forceinline__ v4i planes_of(uint32_t w) {
     return p;
 }
 
+// Lane exchange patterns within aligned 32-lane segments, all symmetric (so a
+// max or sum over the segment is the same value on every lane): DPP quad
+// permutes (lane ^ 1, lane ^ 2), DPP row half-mirror (lane i <-> 7 - i in 8
+// lanes) and row mirror (i <-> 15 - i in 16 lanes) stay in the VALU; the
+// exchange across the two 16-lane rows is one ds_swizzle (lane ^ 16).
+__device__ __forceinline__ int dpp_xor2(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int dpp_half_mirror(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int dpp_mirror(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int swizzle_xor16(int v) {
+    return __builtin_amdgcn_ds_swizzle(v, 0x401F);   // and 0x1F, or 0, xor 0x10
+}
+// Value of lane i of this lane's quad.
+template <int I>
+__device__ __forceinline__ int dpp_quad_bcast(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, I * 0x55, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float seg32_max(float a) {
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(int, a))));
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_xor2(__builtin_bit_cast(int, a))));
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_half_mirror(__builtin_bit_cast(int, a))));
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_mirror(__builtin_bit_cast(int, a))));
+    a = fmaxf(a, __builtin_bit_cast(float, swizzle_xor16(__builtin_bit_cast(int, a))));
+    return a;
+}
+
+__device__ __forceinline__ int seg32_sum(int v) {
+    v += dpp_xor1(v);
+    v += dpp_xor2(v);
+    v += dpp_half_mirror(v);
+    v += dpp_mirror(v);
+    v += swizzle_xor16(v);
+    return v;
+}
+
+// Per-128-group int8 quantisation of activations in plane order, shared by
+// the quantise kernel and the fused GEMV so both give identical q, s, t.
+// 32 lanes hold one group (lane b: x[4b .. 4b+3]); amax and the sum of q are
+// reductions over the 32 lanes (exact in any order). s = amax / 127 is the
+// IEEE float32 quotient (the library is built with correctly rounded
+// division and float32 denormals) and q = clamp(rne(fl32(x / s)), -127, 127)
+// the IEEE result as well, through an exact shortcut:
+//   with rc = v_rcp_f32(s) (relative error <= 2^-23) and y = fl32(x * rc),
+//   |y - x/s| <= 127.5 * (2^-23 + 2^-24) < 2^-15.4 and |fl32(x/s) - x/s|
+//   <= 2^-18 (|x / s| <= 127.5), so y and fl32(x/s) are within 2^-15 of each
+//   other; when y is farther than 2^-13 from every half-integer both round
+//   to the same integer and neither is a tie. Otherwise (about 2e-4 of
+//   random inputs), and for scales below 2^-100 (whose reciprocal may
+//   overflow), the IEEE division decides. s == 0 gives q = 0.
+// A 4x4 byte transpose inside each quad (lanes 4j..4j+3: quad broadcasts and
+// byte permutes) leaves lane 4j+p holding the 32-bit plane word (p, j): the
+// group's bytes 32p + 4j .. 32p + 4j + 3.
+// NR groups per 32-lane slot are processed stage by stage, so their latency
+// chains (lane exchanges, divisions) overlap; the exact fallback is a single
+// wave-uniform branch, taken only when some lane needs it.
+template <int NR>
+__device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lane32,
+                                                  uint32_t (&word)[NR], float (&scale)[NR],
+                                                  int (&sum)[NR]) {
+    float a[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        a[r] = fmaxf(fmaxf(fabsf(v[r].x), fabsf(v[r].y)), fmaxf(fabsf(v[r].z), fabsf(v[r].w)));
+#define PQ2_SEG_MAX_STEP(EXCH)                                                            \
+    _Pragma("unroll") for (int r = 0; r < NR; ++r)                                      \
+        a[r] = fmaxf(a[r], __builtin_bit_cast(float, EXCH(__builtin_bit_cast(int, a[r]))));
+    PQ2_SEG_MAX_STEP(dpp_xor1)
+    PQ2_SEG_MAX_STEP(dpp_xor2)
+    PQ2_SEG_MAX_STEP(dpp_half_mirror)
+    PQ2_SEG_MAX_STEP(dpp_mirror)
+    PQ2_SEG_MAX_STEP(swizzle_xor16)
+#undef PQ2_SEG_MAX_STEP
+    float rc[NR];
+    bool slow = false;
+    float qf[NR][4];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        scale[r] = a[r] / 127.0f;                   // IEEE division
+        rc[r] = __builtin_amdgcn_rcpf(scale[r]);
+        const bool tiny = scale[r] < 0x1p-100f;     // includes s == 0
+        const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float y = xs[e] * rc[r];
+            const float ry = rintf(y);
+            const bool ok = !tiny && fabsf(fabsf(y - ry) - 0.5f) > 0x1p-13f;
+            slow |= !ok && scale[r] != 0.0f;
+            qf[r][e] = ry;
+        }
+    }
+    if (__any(slow)) {                              // rare: the IEEE division decides
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const bool tiny = scale[r] < 0x1p-100f;
+            const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float y = xs[e] * rc[r];
+                const bool ok = !tiny && fabsf(fabsf(y - rintf(y)) - 0.5f) > 0x1p-13f;
+                if (!ok && scale[r] != 0.0f) qf[r][e] = rintf(xs[e] / scale[r]);
+            }
+        }
+    }
+    int u[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        int q[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            q[e] = scale[r] == 0.0f ? 0 : (int)fminf(fmaxf(qf[r][e], -127.0f), 127.0f);
+        sum[r] = q[0] + q[1] + q[2] + q[3];
+        // byte p of u = q of column 4*lane32 + p, i.e. plane p, position lane32
+        u[r] = (int)((uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                     ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24));
+    }
+#define PQ2_SEG_SUM_STEP(EXCH) _Pragma("unroll") for (int r = 0; r < NR; ++r) sum[r] += EXCH(sum[r]);
+    PQ2_SEG_SUM_STEP(dpp_xor1)
+    PQ2_SEG_SUM_STEP(dpp_xor2)
+    PQ2_SEG_SUM_STEP(dpp_half_mirror)
+    PQ2_SEG_SUM_STEP(dpp_mirror)
+    PQ2_SEG_SUM_STEP(swizzle_xor16)
+#undef PQ2_SEG_SUM_STEP
+    // byte i of the word = byte p of quad lane i's u (v_perm: selector bytes
+    // 0-3 pick the second operand's bytes, 4-7 the first's, 0x0C gives zero)
+    const uint32_t p = (uint32_t)(lane32 & 3);
+    const uint32_t sel = p | ((4u + p) << 8) | 0x0C0C0000u;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const uint32_t o0 = (uint32_t)dpp_quad_bcast<0>(u[r]), o1 = (uint32_t)dpp_quad_bcast<1>(u[r]);
+        const uint32_t o2 = (uint32_t)dpp_quad_bcast<2>(u[r]), o3 = (uint32_t)dpp_quad_bcast<3>(u[r]);
+        const uint32_t t01 = __builtin_amdgcn_perm(o1, o0, sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(o3, o2, sel);
+        word[r] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    }
+}
+
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

@@ -25,6 +25,10 @@ constexpr int64_t kGemvMaxM = 4;
 hipError_t launch_gemv(const int8_t *q, const int32_t *t, const uint8_t *codes,
                        const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Quantise + GEMV in one launch (M <= kGemvMaxM): y from float32 x.
+hipError_t launch_gemv_fused(const float *x, const uint8_t *codes, const uint16_t *ws, float *y,
+                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // The small-batch kernel stages 3 * 16 * (G + 1) words of scales in LDS.
 constexpr int64_t kSmallMaxK = 32768;
 

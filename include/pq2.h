@@ -41,7 +41,8 @@
  *                PQ2_MAX_DIM, or K above PQ2_MAX_K (the kernels address a
  *                block's rows with 32-bit offsets);
  *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above;
- *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots);
+ *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), or M above
+ *                PQ2_LINEAR_MAX_M (pq2_linear);
  *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
  * Nothing is enqueued when a status other than PQ2_OK is returned, except for
  * PQ2_ERR_HIP. A fault during execution surfaces at the caller's next
@@ -111,6 +112,27 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
 pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
                     const uint8_t *codes, const uint16_t *wscale, float *y,
                     int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/*
+ * Quantise and multiply in one launch, for decode batches of 1 to 4 token
+ * rows (PQ2_LINEAR_MAX_M): y = the PQ2_0 product of x quantised exactly as
+ * pq2_quantize_act would (page "Making a ternary reasoning model fast in
+ * vLLM", section "Prompt processing: check configuration and launch costs",
+ * counts a separate quantiser launch per projection; this entry removes it).
+ * Every block of the v_dot4 GEMV quantises the activations it needs into
+ * LDS, with the same arithmetic as pq2_quantize_act, so y is bit-identical
+ * to pq2_quantize_act followed by pq2_gemm's GEMV path. q, s and t are not
+ * written anywhere. For callers that cannot hold q/s/t buffers: every block
+ * re-quantises the whole activation row, which on MI355X costs more than the
+ * separate quantiser launch it saves (pq2_quantize_act + pq2_gemm is the
+ * faster decode step).
+ *   x  float32 [M][K], 16-byte aligned; codes, wscale, y as for pq2_gemm.
+ * M above PQ2_LINEAR_MAX_M returns PQ2_ERR_ARG (use pq2_quantize_act and
+ * pq2_gemm with caller-owned q, s, t).
+ */
+#define PQ2_LINEAR_MAX_M 4
+pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
+                      int64_t M, int64_t N, int64_t K, void *hip_stream);
 
 /*
  * Test and diagnostic entry: runs the main loop of the selected kernel path

@@ -73,6 +73,17 @@ def test_gemm_validation():
     assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
 
 
+def test_linear_validation():
+    f = pq2.lib.pq2_linear
+    assert f(None, P, P, P, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, None, P, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, 0, 8, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, 8, 200, None) == ERR_SHAPE
+    assert f(P + 4, P, P, P, 1, 8, 128, None) == ERR_ALIGN     # x needs 16 B
+    assert f(P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN     # codes needs 16 B
+    assert f(P, P, P, P, 5, 8, 128, None) == ERR_ARG            # M above PQ2_LINEAR_MAX_M
+
+
 def test_group_dots_validation():
     f = pq2.lib.pq2_gemm_group_dots
     assert f(P, P, P, None, 1, 8, 128, 0, None) == ERR_NULL

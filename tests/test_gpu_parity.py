@@ -253,6 +253,43 @@ def test_smallest_problem(pq2):
     assert oracle.rel_err(y, yo, tabs) < TOL
 
 
+# ---------------------------------------------------------------- fused quantise + GEMV
+
+LINEAR_SHAPES = [(M, N, K) for M in (1, 2, 3, 4)
+                 for (N, K) in ((1, 128), (300, 640), (257, 6144), (65, 8320), (40, 17408))]
+
+
+@pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
+def test_linear_equals_quantize_then_gemm(pq2, M, N, K):
+    """pq2_linear quantises with the quantiser's own arithmetic, so y is bit-identical
+    to pq2_quantize_act + pq2_gemm on the GEMV path, and within tolerance of the oracle."""
+    print(f"linear M={M} N={N} K={K}", flush=True)
+    x = synth.activations(M, K, M * 31 + N, outlier_frac=0.01)
+    x[0, :128] = 0.0                                   # a zero group (s = 0)
+    w = synth.weights(N, K, synth.matrix_seed(M + N))
+    xd, cd, wd = dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    y1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_linear(xd, cd, wd, y1)
+    q, s, t = pq2.quantize_act(xd)
+    y2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(q, s, t, cd, wd, y2)
+    yh = host(y1)
+    if M <= 2:       # pq2_gemm takes the GEMV path: identical arithmetic
+        np.testing.assert_array_equal(yh, host(y2))
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(yh, yo, tabs) < TOL
+    # unit scales, through the float path of the same kernel: exact integers
+    ones_w = torch.full((N, K // G), 0x3C00, dtype=torch.int16, device="cuda")
+    xs = np.repeat(np.float32(127.0) * np.sign(x.reshape(M, -1, G)[:, :, :1]), G, -1)
+    xs = np.where(xs == 0, np.float32(127.0), xs).reshape(M, K)   # amax 127 -> s = 1
+    xs[:, 1::3] = np.float32(-3.0)
+    pq2.pq2_linear(dev(xs), cd, ones_w, y1)
+    qo, so, to = oracle.quantize(xs)
+    assert (so == 1.0).all()
+    D = oracle.group_dots(qo, w.codes)
+    np.testing.assert_array_equal(host(y1), D.sum(-1).astype(np.float32))
+
+
 # ---------------------------------------------------------------- full workload sizes
 
 FULL = [
@@ -266,6 +303,24 @@ FULL = [
     ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
     ("prefill_m4096_up", 4096, 17408, 5120, synth.PREFILL_CODES, 0.0),
 ]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (2, 17408, 5120), (4, 5120, 17408)])
+def test_linear_full_size_sampled(pq2, M, N, K):
+    """pq2_linear at the decode and small-batch sizes against sampled oracle outputs."""
+    print(f"linear full M={M} N={N} K={K}", flush=True)
+    x = synth.activations(M, K, 0, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(0))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_linear(dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16)), y)
+    yh = host(y)
+    qo, so, to = oracle.quantize(x)
+    rng = np.random.default_rng(2)
+    P = 384
+    mm = np.concatenate([rng.integers(0, M, P - 2), [0, M - 1]])
+    nn = np.concatenate([rng.integers(0, N, P - 2), [N - 1, 0]])
+    ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
+    assert oracle.rel_err(yh[mm, nn], ys, ts) < TOL
 
 
 @pytest.mark.parametrize("name,M,N,K,probs,outl", FULL, ids=[f[0] for f in FULL])

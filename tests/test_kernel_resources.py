@@ -10,9 +10,15 @@ import re
 import shutil
 import subprocess
 
+import importlib.util
+
 import pytest
 
-from gemm_pq2_w2a8_amd import build as hip_build
+# the build script, loaded by path (importing the package needs a built library)
+_spec = importlib.util.spec_from_file_location(
+    "pq2_hip_build", os.path.join(os.path.dirname(__file__), "..", "gemm_pq2_w2a8_amd", "build.py"))
+hip_build = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(hip_build)
 
 SOURCES = [s for s in hip_build.SOURCES if s.endswith(".hip")]
 
