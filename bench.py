@@ -170,10 +170,10 @@ def traffic_record(kernel_tag):
         return None
     import hashlib
     rec = json.load(open(path))
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if sha != rec.get("source_sha256"):
-        return None
+    root = os.path.dirname(os.path.abspath(__file__))
+    for src, sha in rec["source_sha256"].items():
+        if hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest() != sha:
+            return None        # the kernel changed since the counters were taken
     return rec.get("hbm_bytes_per_launch")
 
 
@@ -391,6 +391,9 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="one line per configuration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise kernel (y = 2x, float32) over MIB MiB, "
+                         "the calibration for HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -403,6 +406,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        reps = 10
+        for _ in range(reps):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe": {"kernel": "torch.mul(src, 2.0, out=dst)",
+                                         "read_bytes_per_launch": 4 * n,
+                                         "write_bytes_per_launch": 4 * n, "launches": reps}}))
+        return
+
     import gemm_pq2_w2a8_amd as pq2
 
     wls = workload_list()
