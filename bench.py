@@ -277,7 +277,8 @@ def report_gemm(args, wl, r, torch):
     sbytes = step_bytes(M, N, K)
     prefill = M > 16
     fused = r["fused"]
-    path = "gemv_dot4" if M <= 2 else ("small_mfma" if M <= 16 else "prefill_mfma")
+    gemv = M <= 2 or (M <= 4 and N * K > (1 << 25))     # pq2_gemm's choice
+    path = "gemv_dot4" if gemv else ("small_mfma" if M <= 16 else "prefill_mfma")
     if prefill:
         value = gemm_ops(M, N, K) / (r["ms_step"] * 1e-3) / 1e12
         unit = "TOP/s"

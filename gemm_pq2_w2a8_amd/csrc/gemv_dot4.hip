@@ -20,17 +20,22 @@
 //    splits into RL = 64/CL row slots of CL lanes; lane cs of a slot handles
 //    chunks cs, cs+CL, cs+2CL, ... of RP rows. CL = gcd(K/64, 64), so every
 //    lane is busy on every iteration and each load instruction covers RL
-//    contiguous runs of CL*16 bytes (coalesced HBM streaming).
-//  * K is processed in LDS windows of up to 32768/MT activations per token
-//    (one window for every K up to that). Per window the block stages the
-//    MT token rows of q into LDS chunk-major by plane ([token][plane][chunk]
-//    of 16 bytes, so the CL lanes of a slot read consecutive 16-byte words),
-//    with s and t.
+//    contiguous runs of CL*16 bytes (coalesced HBM streaming). A block (four
+//    waves) covers a row group of ROWS_PER_BLOCK rows.
+//  * The MT token rows of q are staged in LDS chunk-major by plane
+//    ([token][plane][chunk] of 16 bytes, so the CL lanes of a slot read
+//    consecutive 16-byte words), with s and t, in windows of up to
+//    kMaxStage / MT activations per token.
+//  * When one window covers K (every shape of the decode and small-batch
+//    workloads) the kernel is persistent: at most kPersistBlocks blocks each
+//    stage q once and then walk row groups blockIdx.x, + gridDim.x, ...; the
+//    staging is paid once per block instead of once per row group. Otherwise
+//    each block takes one row group and loops over the windows.
 //  * Memory-level parallelism: a lane issues the code loads (and the weight
 //    scale of each chunk's group) of IB chunk iterations x RP rows at once
-//    (one batch) and the next batch is in flight while the current one is
-//    computed. A window's first batch and all of its staging loads are
-//    issued before the first wait: one memory round trip before compute.
+//    (one batch); the next batch -- of the same row group or the next one --
+//    is in flight while the current one is computed. The first batch and all
+//    staging loads share one memory round trip.
 //  * Planes 0 and 2 are masked to bits 0..1 (plane 2 after one shift by 4);
 //    planes 1 and 3 are masked in place at bits 2..3, which is 4 * code, and
 //    go to a second accumulator divided by 4 (exactly) before the two are
@@ -39,13 +44,15 @@
 //  * The even lane of a chunk pair seeds its accumulators with -t[m][g]; the
 //    two half-group sums meet through a DPP lane swap, giving the exact group
 //    dot on both lanes. The even lane applies the float32 epilogue.
-//  * Rows are reduced over their CL lanes with a fixed butterfly at the end.
+//  * Rows are reduced over their CL lanes with a fixed butterfly when their
+//    row group is done.
 //  * Token rows past M (M = 3 runs as MT = 4) read token M-1 and are never
 //    stored.
 //  * The fused variant (pq2_linear) reads float32 x instead of q, s, t: each
 //    block quantises its window in LDS with the quantiser's own arithmetic
-//    (quantize_groups32) while its first batch of code loads is in flight,
-//    which saves the separate quantise launch of a decode step.
+//    (quantize_groups32). The first pass of x loads is issued before the
+//    first code batch (loads complete in issue order for the wait counter),
+//    so the block quantises while its codes are in flight.
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
@@ -65,8 +72,11 @@ __device__ __forceinline__ int token_of(int u, int n) {
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kLoadsPerBatch = 8;                 // uint4 code loads per lane per batch
-constexpr int64_t kMaxStage = 32768;              // activations staged per window (all tokens)
+constexpr int64_t kMaxStage = 40960;              // activations staged per window (all tokens)
 constexpr int kQStagePer = kMaxStage / 16 / kGemvThreads;   // q chunks per thread
+constexpr int kSTStagePer = (kMaxStage / 128 + kGemvThreads - 1) / kGemvThreads;  // s, t per thread
+constexpr int64_t kPersistBlocks = 512;           // two blocks per CU
+constexpr int kXRound = 8;                        // groups per 32-lane slot and pass (fused)
 
 template <int LOG_CL, int RP>
 struct GemvShape {
@@ -79,9 +89,6 @@ struct GemvShape {
 
 // LDS bytes per group and token of a window: q (128), s (4), t (4).
 constexpr int64_t kLdsPerGroup = kGroup + 8;
-
-// Groups quantised per 32-lane slot and pass in the fused variant.
-constexpr int kXRound = 8;
 
 template <int LOG_CL, int RP, int MT, bool DOTS, bool FUSED>
 __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
@@ -100,19 +107,9 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
     const int rs = lane >> LOG_CL;
     const int h = cs & 1;                         // half of the group this lane holds
     const int64_t G = K / kGroup;
-    const int64_t block_row0 = (int64_t)blockIdx.x * S::ROWS_PER_BLOCK;
-    const int local0 = wave * S::ROWS_PER_WAVE + rs;     // first local row of this lane
-    const int64_t row0 = block_row0 + local0;
-
-    const uint4 *rowp[RP];
-    const uint16_t *wsp[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-        const int64_t row = row0 + (int64_t)r * RL;
-        const int64_t rc = row < N ? row : N - 1;
-        rowp[r] = reinterpret_cast<const uint4 *>(codes + rc * (K / 4));
-        wsp[r] = ws + rc * G;
-    }
+    const int local0 = wave * S::ROWS_PER_WAVE + rs;     // first row of this lane in a row group
+    const int64_t n_rg = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
+    const bool single = K <= window;              // uniform: one LDS window covers K
 
     float facc[RP][MT];
 #pragma unroll
@@ -120,14 +117,34 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
 #pragma unroll
         for (int m = 0; m < MT; ++m) facc[r][m] = 0.0f;
 
-    // Fused variant: the first pass of x loads goes out before the first code
-    // batch. Loads complete in issue order for the wait counter, so the block
-    // can then wait for x alone and quantise while the codes of its first
-    // batch are still in flight (later windows and passes are serial).
+    // ---------------------------------------------------------------- loads
+    // (native vectors: copies of the HIP uint4 struct can leave arrays in scratch)
+    v4i bufa[IB][RP], bufb[IB][RP];
+    uint16_t wsa[IB][RP], wsb[IB][RP];
+    // code chunks of row group rg, window starting at k0, iterations it0..
+    // (never predicated: past the window the last chunk is re-read, unused)
+    auto load_batch = [&](v4i (&buf)[IB][RP], uint16_t (&wsv)[IB][RP], int64_t rg, int64_t k0,
+                          int iters, int it0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+            const int64_t row = rg * S::ROWS_PER_BLOCK + local0 + (int64_t)r * RL;
+            const int64_t rc = row < N ? row : N - 1;
+            const v4i *cp = reinterpret_cast<const v4i *>(codes + rc * (K / 4)) + k0 / 64 + cs;
+            const uint16_t *wp = ws + rc * G + k0 / kGroup;
+#pragma unroll
+            for (int b = 0; b < IB; ++b) {
+                const int it = min(it0 + b, iters - 1);
+                buf[b][r] = cp[CL * it];
+                if (!DOTS) wsv[b][r] = wp[(cs + CL * it) >> 1];
+            }
+        }
+    };
+
+    // x loads of the fused variant (first pass of window kx)
     constexpr int kSlots = kGemvThreads / 32;
     const int lane32 = threadIdx.x & 31, slot = threadIdx.x >> 5;
     float4 xv[kXRound];
-    auto load_x = [&](int64_t kx, int base) {
+    auto load_x = [&](int64_t kx, int base) __attribute__((always_inline)) {
         const int wkx = (int)((K - kx < window) ? K - kx : window);
         const int wgx = wkx / kGroup, ngx = MT * wgx;
 #pragma unroll
@@ -139,60 +156,21 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
             xv[i] = *reinterpret_cast<const float4 *>(x + mc * K + kx + kGroup * gw + 4 * lane32);
         }
     };
-    if constexpr (FUSED) {
-        load_x(0, 0);
-        // keep the x loads ahead of the codes (no pass moves loads across)
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    }
 
-    for (int64_t k0 = 0; k0 < K; k0 += window) {
-        // window extent; all wave-uniform, kept in scalar registers
-        const int wk = __builtin_amdgcn_readfirstlane((int)((K - k0 < window) ? K - k0 : window));
-        const int wg = wk / kGroup;                   // groups in window
+    // ---------------------------------------------------------------- staging
+    // window k0 of wk activations per token: q [token][plane][chunk],
+    // s [token][g], t [token][g]. Ends with a barrier.
+    auto stage = [&](int64_t k0, int wk) __attribute__((always_inline)) {
+        const int wg = wk / kGroup;
         const int wchunks = wk / 64;
-        const int iters = wchunks / CL;
-        const int64_t g0 = k0 / kGroup;
-        const uint4 *wrow[RP];                        // this lane's first chunk of the window
-        const uint16_t *wsrow[RP];                    // the rows' scales of the window
-#pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            wrow[r] = rowp[r] + k0 / 64 + cs;
-            wsrow[r] = wsp[r] + g0;
-        }
-
-        // Loads are never predicated (a chunk past the window re-reads the
-        // window's last chunk and is not used), so each batch is a fixed
-        // number of loads and the compiler's wait counts stay exact.
-        uint4 bufa[IB][RP], bufb[IB][RP];
-        uint16_t wsa[IB][RP], wsb[IB][RP];
-        auto load_batch = [&](uint4 (&buf)[IB][RP], uint16_t (&wsv)[IB][RP], int it0) {
-#pragma unroll
-            for (int b = 0; b < IB; ++b) {
-                const int it = min(it0 + b, iters - 1);
-#pragma unroll
-                for (int r = 0; r < RP; ++r) {
-                    buf[b][r] = wrow[r][CL * it];
-                    if (!DOTS) wsv[b][r] = wsrow[r][(cs + CL * it) >> 1];
-                }
-            }
-        };
-        load_batch(bufa, wsa, 0);
-        if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
-
-        // stage the window: q [token][plane][chunk], s [token][g],
-        // t [token][g]; all loads of the staging are issued (clamped,
-        // unpredicated) before any LDS store, so they share one memory round
-        // trip with the first code batch
         float *s_l = reinterpret_cast<float *>(smem + 4 * MT * wchunks);
         int32_t *t_l = reinterpret_cast<int32_t *>(s_l + MT * wg);
         if constexpr (FUSED) {
             // quantise the window's MT x wg groups from x straight into the
-            // LDS layout: 32 lanes per group, kXRound groups per slot and pass,
-            // the same arithmetic as pq2_quantize_act (quantize_groups32)
+            // LDS layout: 32 lanes per group, kXRound groups per slot and pass
             uint32_t *qw = reinterpret_cast<uint32_t *>(smem);
             const int ngr = MT * wg;
-            auto quantize_pass = [&](int base) {
+            auto quantize_pass = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
                 for (int i = 0; i < kXRound; ++i) {
                     const int graw = base + slot + kSlots * i;
@@ -212,34 +190,34 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
                     }
                 }
             };
-            // pass 0 on the x loads issued ahead of the code batch (straight
-            // line, so the wait is for x alone); further passes load and wait
+            // pass 0 on x loads issued ahead of the first code batch
             quantize_pass(0);
             for (int base = kSlots * kXRound; base < ngr; base += kSlots * kXRound) {
                 load_x(k0, base);
                 quantize_pass(base);
             }
-        } else
-        {
+        } else {
             const int nq = wk / 16;                   // 16-byte q chunks per token
-            uint4 qs[kQStagePer];
+            v4i qs[kQStagePer];
 #pragma unroll
             for (int i = 0; i < kQStagePer; ++i) {
                 int u = (int)threadIdx.x + i * kGemvThreads;
                 u = u < MT * nq ? u : MT * nq - 1;
                 const int m = token_of<MT>(u, nq), uu = u - m * nq;
                 const int64_t mc = m < M ? m : M - 1;
-                qs[i] = reinterpret_cast<const uint4 *>(q + mc * K + k0)[uu];
+                qs[i] = reinterpret_cast<const v4i *>(q + mc * K + k0)[uu];
             }
-            float sv = 0.0f;
-            int32_t tv = 0;
-            {
-                int e = (int)threadIdx.x;
+            float sv[kSTStagePer];
+            int32_t tv[kSTStagePer];
+#pragma unroll
+            for (int i = 0; i < kSTStagePer; ++i) {
+                int e = (int)threadIdx.x + i * kGemvThreads;
                 e = e < MT * wg ? e : MT * wg - 1;
                 const int m = token_of<MT>(e, wg), gi = e - m * wg;
                 const int64_t mc = m < M ? m : M - 1;
-                if (!DOTS) sv = s[mc * G + g0 + gi];
-                tv = t[mc * G + g0 + gi];
+                sv[i] = 0.0f;
+                if (!DOTS) sv[i] = s[mc * G + k0 / kGroup + gi];
+                tv[i] = t[mc * G + k0 / kGroup + gi];
             }
 #pragma unroll
             for (int i = 0; i < kQStagePer; ++i) {
@@ -247,115 +225,173 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
                 if (u < MT * nq) {
                     const int m = token_of<MT>(u, nq), uu = u - m * nq;
                     const int g = uu >> 3, p = (uu >> 1) & 3, hh = uu & 1;
-                    smem[(m * 4 + p) * wchunks + 2 * g + hh] = qs[i];
+                    reinterpret_cast<v4i *>(smem)[(m * 4 + p) * wchunks + 2 * g + hh] = qs[i];
                 }
             }
-            if ((int)threadIdx.x < MT * wg) {
-                if (!DOTS) s_l[threadIdx.x] = sv;
-                t_l[threadIdx.x] = tv;
+#pragma unroll
+            for (int i = 0; i < kSTStagePer; ++i) {
+                const int e = (int)threadIdx.x + i * kGemvThreads;
+                if (e < MT * wg) {
+                    if (!DOTS) s_l[e] = sv[i];
+                    t_l[e] = tv[i];
+                }
             }
         }
         __syncthreads();
+    };
 
-        auto compute_batch = [&](const uint4 (&buf)[IB][RP], const uint16_t (&wsv)[IB][RP],
-                                 int it0) {
+    // ---------------------------------------------------------------- compute
+    auto compute_batch = [&](const v4i (&buf)[IB][RP], const uint16_t (&wsv)[IB][RP],
+                             int64_t rg, int64_t k0, int wk, int it0) __attribute__((always_inline)) {
+        const int wg = wk / kGroup;
+        const int wchunks = wk / 64;
+        const int iters = wchunks / CL;
+        const float *s_l = reinterpret_cast<const float *>(smem + 4 * MT * wchunks);
+        const int32_t *t_l = reinterpret_cast<const int32_t *>(s_l + MT * wg);
+        const int64_t row0 = rg * S::ROWS_PER_BLOCK + local0;
 #pragma unroll
-            for (int b = 0; b < IB; ++b) {
-                if (it0 + b >= iters) break;
-                const int c = cs + CL * (it0 + b);    // chunk within window
-                const int g = c >> 1;                 // group within window
-                // the planes of every code word of the RP rows, shared by the tokens
-                uint32_t pa0[RP][4], pa1[RP][4], pa2[RP][4], pa3[RP][4];
+        for (int b = 0; b < IB; ++b) {
+            if (it0 + b >= iters) break;
+            const int c = cs + CL * (it0 + b);    // chunk within window
+            const int g = c >> 1;                 // group within window
+            // the planes of every code word of the RP rows, shared by the tokens
+            uint32_t pa0[RP][4], pa1[RP][4], pa2[RP][4], pa3[RP][4];
 #pragma unroll
-                for (int r = 0; r < RP; ++r) {
-                    const uint4 w = buf[b][r];
-                    const uint32_t wr[4] = {w.x, w.y, w.z, w.w};
+            for (int r = 0; r < RP; ++r) {
+                const v4i w = buf[b][r];
+                const uint32_t wr[4] = {(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const uint32_t wd = wr[jj];
-                        const uint32_t hi = wd >> 4;
-                        pa0[r][jj] = wd & kPlaneMask;
-                        pa1[r][jj] = wd & kPlaneMaskX4;
-                        pa2[r][jj] = hi & kPlaneMask;
-                        pa3[r][jj] = hi & kPlaneMaskX4;
-                    }
-                }
-                float cw[RP];
-                if (!DOTS) {
-#pragma unroll
-                    for (int r = 0; r < RP; ++r) cw[r] = half_bits_to_float(wsv[b][r]);
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    uint4 qv[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) qv[p] = smem[(m * 4 + p) * wchunks + c];
-                    const int tg = t_l[m * wg + g];
-                    float sg = 0.0f;
-                    if (!DOTS) sg = s_l[m * wg + g];
-                    const uint32_t p0[4] = {qv[0].x, qv[0].y, qv[0].z, qv[0].w};
-                    const uint32_t p1[4] = {qv[1].x, qv[1].y, qv[1].z, qv[1].w};
-                    const uint32_t p2[4] = {qv[2].x, qv[2].y, qv[2].z, qv[2].w};
-                    const uint32_t p3[4] = {qv[3].x, qv[3].y, qv[3].z, qv[3].w};
-#pragma unroll
-                    for (int r = 0; r < RP; ++r) {
-                        int da = h ? 0 : -tg;   // planes 0 and 2, and the -sum(q) offset
-                        int db = 0;             // planes 1 and 3, in place: 4 * (their dot)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            da = dot4(pa0[r][jj], p0[jj], da);
-                            db = dot4(pa1[r][jj], p1[jj], db);
-                            da = dot4(pa2[r][jj], p2[jj], da);
-                            db = dot4(pa3[r][jj], p3[jj], db);
-                        }
-                        const int half_dot = da + (db >> 2);            // db is a multiple of 4
-                        const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
-                        if (DOTS) {
-                            const int64_t row = row0 + (int64_t)r * RL;
-                            if (!h && m < M && row < N) d[(m * N + row) * G + g0 + g] = dot;
-                        } else {
-                            facc[r][m] = fmaf((float)dot, h ? 0.0f : sg * cw[r], facc[r][m]);
-                        }
-                    }
+                for (int jj = 0; jj < 4; ++jj) {
+                    const uint32_t wd = wr[jj];
+                    const uint32_t hi = wd >> 4;
+                    pa0[r][jj] = wd & kPlaneMask;
+                    pa1[r][jj] = wd & kPlaneMaskX4;
+                    pa2[r][jj] = hi & kPlaneMask;
+                    pa3[r][jj] = hi & kPlaneMaskX4;
                 }
             }
-        };
-
-        // ping-pong: the other buffer's loads are in flight during each
-        // compute. Prefetches are unconditional (clamped), so the wait counts
-        // inside the loop are static.
-        if (iters <= IB) {
-            compute_batch(bufa, wsa, 0);
-        } else {
-            for (int it0 = 0;; it0 += 2 * IB) {
-                load_batch(bufb, wsb, it0 + IB);
-                compute_batch(bufa, wsa, it0);
-                if (it0 + IB >= iters) break;
-                load_batch(bufa, wsa, it0 + 2 * IB);
-                compute_batch(bufb, wsb, it0 + IB);
-                if (it0 + 2 * IB >= iters) break;
-            }
-        }
-        if constexpr (FUSED) {
-            // the next window's first x pass (the last window reloads itself;
-            // unconditional, so the pending loads are the same on every path)
-            const int64_t last = ((K - 1) / window) * window;
-            load_x(k0 + window < K ? k0 + window : last, 0);
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (k0 + window < K) __syncthreads();    // window buffer is reused
-    }
-
-    if (!DOTS) {
+            float cw[RP];
+            if (!DOTS) {
 #pragma unroll
-        for (int r = 0; r < RP; ++r) {
-            const int64_t row = row0 + (int64_t)r * RL;
+                for (int r = 0; r < RP; ++r) cw[r] = half_bits_to_float(wsv[b][r]);
+            }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const float v = segment_sum<CL>(facc[r][m]);
-                if (cs == 0 && m < M && row < N) y[m * N + row] = v;
+                v4i qv[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    qv[p] = reinterpret_cast<const v4i *>(smem)[(m * 4 + p) * wchunks + c];
+                const int tg = t_l[m * wg + g];
+                float sg = 0.0f;
+                if (!DOTS) sg = s_l[m * wg + g];
+                uint32_t p0[4], p1[4], p2[4], p3[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    p0[jj] = (uint32_t)qv[0][jj];
+                    p1[jj] = (uint32_t)qv[1][jj];
+                    p2[jj] = (uint32_t)qv[2][jj];
+                    p3[jj] = (uint32_t)qv[3][jj];
+                }
+#pragma unroll
+                for (int r = 0; r < RP; ++r) {
+                    int da = h ? 0 : -tg;   // planes 0 and 2, and the -sum(q) offset
+                    int db = 0;             // planes 1 and 3, in place: 4 * (their dot)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        da = dot4(pa0[r][jj], p0[jj], da);
+                        db = dot4(pa1[r][jj], p1[jj], db);
+                        da = dot4(pa2[r][jj], p2[jj], da);
+                        db = dot4(pa3[r][jj], p3[jj], db);
+                    }
+                    const int half_dot = da + (db >> 2);            // db is a multiple of 4
+                    const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
+                    if (DOTS) {
+                        const int64_t row = row0 + (int64_t)r * RL;
+                        if (!h && m < M && row < N) d[(m * N + row) * G + k0 / kGroup + g] = dot;
+                    } else {
+                        facc[r][m] = fmaf((float)dot, h ? 0.0f : sg * cw[r], facc[r][m]);
+                    }
+                }
             }
+        }
+    };
+
+    // reduce the rows of row group rg over their CL lanes, store, reset
+    auto finish = [&](int64_t rg) __attribute__((always_inline)) {
+        if (!DOTS) {
+            const int64_t row0 = rg * S::ROWS_PER_BLOCK + local0;
+#pragma unroll
+            for (int r = 0; r < RP; ++r) {
+                const int64_t row = row0 + (int64_t)r * RL;
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float v = segment_sum<CL>(facc[r][m]);
+                    if (cs == 0 && m < M && row < N) y[m * N + row] = v;
+                    facc[r][m] = 0.0f;
+                }
+            }
+        }
+    };
+
+    // This block's batches in order: row groups rg_first, + gridDim.x, ...
+    // (rg_count of them), nb batches of IB iterations each.
+    auto run = [&](int64_t k0, int wk, int64_t rg_first, int64_t rg_count,
+                   bool last_window) __attribute__((always_inline)) {
+        const int iters = wk / 64 / CL;
+        const int nb = (iters + IB - 1) / IB;
+        const int J = (int)(rg_count * nb);
+        auto rg_of = [&](int j) __attribute__((always_inline)) { return rg_first + (int64_t)(j / nb) * gridDim.x; };
+        auto it_of = [&](int j) __attribute__((always_inline)) { return (j % nb) * IB; };
+        if (J == 1) {                  // one batch in all: nothing to prefetch
+            compute_batch(bufa, wsa, rg_first, k0, wk, 0);
+            if (last_window) finish(rg_first);
+            return;
+        }
+        // ping-pong: the other buffer's loads are in flight during each
+        // compute; prefetches are unconditional (clamped), so the wait counts
+        // inside the loop are static
+        for (int j = 0;; j += 2) {
+            const int j1 = j + 1 < J ? j + 1 : J - 1;
+            load_batch(bufb, wsb, rg_of(j1), k0, iters, it_of(j1));
+            compute_batch(bufa, wsa, rg_of(j), k0, wk, it_of(j));
+            if (last_window && j % nb == nb - 1) finish(rg_of(j));
+            if (j + 1 >= J) break;
+            const int j2 = j + 2 < J ? j + 2 : J - 1;
+            load_batch(bufa, wsa, rg_of(j2), k0, iters, it_of(j2));
+            compute_batch(bufb, wsb, rg_of(j + 1), k0, wk, it_of(j + 1));
+            if (last_window && (j + 1) % nb == nb - 1) finish(rg_of(j + 1));
+            if (j + 2 >= J) break;
+        }
+    };
+
+    const int64_t rg0 = blockIdx.x;
+    if (single) {
+        // persistent: stage once, then every row group of this block
+        const int wk = (int)K;
+        const int64_t count = (n_rg - rg0 + gridDim.x - 1) / gridDim.x;
+        if constexpr (FUSED) {
+            load_x(0, 0);
+            asm volatile("" ::: "memory");     // keep the x loads ahead of the codes
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        load_batch(bufa, wsa, rg0, 0, wk / 64 / CL, 0);
+        if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
+        stage(0, wk);
+        run(0, wk, rg0, count, true);
+    } else {
+        // one row group per block, windows in turn
+        for (int64_t k0 = 0; k0 < K; k0 += window) {
+            const int wk = __builtin_amdgcn_readfirstlane((int)((K - k0 < window) ? K - k0 : window));
+            if constexpr (FUSED) {
+                load_x(k0, 0);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            load_batch(bufa, wsa, rg0, k0, wk / 64 / CL, 0);
+            if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
+            stage(k0, wk);
+            run(k0, wk, rg0, 1, k0 + window >= K);
+            if (k0 + window < K) __syncthreads();    // window buffer is reused
         }
     }
 }
@@ -364,9 +400,14 @@ template <int LOG_CL, int RP, int MT>
 hipError_t launch_cfg(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
                       const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     using S = GemvShape<LOG_CL, RP>;
-    const int64_t blocks = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
-    constexpr int64_t kWindow = kMaxStage / MT;       // a multiple of 64 * CL for every CL
+    const int64_t n_rg = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
+    // window: the largest multiple of 64 * CL activations per token within
+    // kMaxStage / MT (iterations then divide every window)
+    constexpr int64_t kUnit = 64 * S::CL;
+    constexpr int64_t kWindow = (kMaxStage / MT) / kUnit * kUnit;
+    static_assert(kWindow >= kUnit, "window");
     const int64_t window = K < kWindow ? K : kWindow;
+    const int64_t blocks = K <= window ? (n_rg < kPersistBlocks ? n_rg : kPersistBlocks) : n_rg;
     const size_t lds = (size_t)(MT * (window / kGroup) * kLdsPerGroup);
     if (x) {
         hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, true>), dim3((unsigned)blocks),

@@ -34,12 +34,13 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
     }
 }
 
-#ifndef PQ2_GEMV_AUTO_M
-#define PQ2_GEMV_AUTO_M 2   // largest M that pq2_gemm sends to the dot4 GEMV
-#endif
-
-int auto_path(int64_t M, int64_t K) {
-    if (M <= PQ2_GEMV_AUTO_M) return PQ2_PATH_GEMV;
+// Kernel choice of pq2_gemm (from MI355X measurements on the decode and
+// small-batch shapes): the dot4 GEMV reads only the real token rows and wins
+// for M <= 2 everywhere, and for M = 3..4 on large matrices (N*K > 2^25); the
+// 16-token MFMA kernel wins for M = 3..4 on smaller ones and up to M = 16.
+int auto_path(int64_t M, int64_t N, int64_t K) {
+    if (M <= 2) return PQ2_PATH_GEMV;
+    if (M <= pq2::kGemvMaxM && N * K > (int64_t(1) << 25)) return PQ2_PATH_GEMV;
     if (M <= 16 && K <= pq2::kSmallMaxK) return PQ2_PATH_SMALL;
     return PQ2_PATH_PREFILL;
 }
@@ -82,7 +83,7 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uin
         !aligned(wscale, 2) || !aligned(y, 4))
         return PQ2_ERR_ALIGN;
     const pq2::GemmOut out{y, nullptr, s, wscale};
-    return run_path(auto_path(M, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+    return run_path(auto_path(M, N, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
@@ -106,7 +107,7 @@ pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t 
     if (st != PQ2_OK) return st;
     if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(t, 4) || !aligned(d, 4))
         return PQ2_ERR_ALIGN;
-    if (path == PQ2_PATH_AUTO) path = auto_path(M, K);
+    if (path == PQ2_PATH_AUTO) path = auto_path(M, N, K);
     if (path == PQ2_PATH_GEMV && M > pq2::kGemvMaxM) return PQ2_ERR_ARG;
     if (path == PQ2_PATH_SMALL && (M > 16 || K > pq2::kSmallMaxK)) return PQ2_ERR_ARG;
     if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PREFILL) return PQ2_ERR_ARG;

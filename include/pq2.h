@@ -100,10 +100,11 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
 
 /*
  * y = the PQ2_0 product defined above. The kernel depends on M:
- *   1 <= M <= 2   -> GEMV streaming code words into v_dot4 (2-bit planes
+ *   M <= 2, or M <= 4 with N*K > 2^25
+ *                 -> GEMV streaming code words into v_dot4 (2-bit planes
  *                    masked out of each 32-bit word, no decode step; each
  *                    word serves every token row);
- *   3 <= M <= 16  -> small-batch kernel on int8 MFMA, tokens padded to 16
+ *   other M <= 16 -> small-batch kernel on int8 MFMA, tokens padded to 16
  *                    (K <= 32768; larger K takes the tiled kernel);
  *   M >= 17       -> tiled int8 MFMA GEMM (prefill).
  * Group dots are exact int32; the float32 epilogue sums the G terms in an
