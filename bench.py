@@ -264,6 +264,7 @@ def run_gemm(args, wl, torch, pq2):
     # including the dispatch gap between launches)
     gemm_total, _, _ = timed(lambda i: gemm(qp, sp, tp, cps[i % R], wps[i % R], yp, M, N, K, stream))
     out = dict(ms_step=total_ms / args.steps, gemm_ms=gemm_total / args.steps, wall=wall,
+               path=pq2.PATH_NAMES[pq2.gemm_kernel_path(M, N, K)],
                M=M, N=N, K=K, host_enqueue_ms=enq_ms, gpu_ms=total_ms, fused=fused)
     out["kernel_ms"] = out["gemm_ms"]
     if fused:
@@ -277,8 +278,7 @@ def report_gemm(args, wl, r, torch):
     sbytes = step_bytes(M, N, K)
     prefill = M > 16
     fused = r["fused"]
-    gemv = M <= 2 or (M <= 4 and N * K > (1 << 25))     # pq2_gemm's choice
-    path = "gemv_dot4" if gemv else ("small_mfma" if M <= 16 else "prefill_mfma")
+    path = r["path"]
     if prefill:
         value = gemm_ops(M, N, K) / (r["ms_step"] * 1e-3) / 1e12
         unit = "TOP/s"

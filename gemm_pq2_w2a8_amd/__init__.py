@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpq2.so")
 
 GROUP = 128
-PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_PREFILL = 0, 1, 2, 3
+PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_PREFILL, PATH_PANEL = 0, 1, 2, 3, 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python gemm_pq2_w2a8_amd/build.py`")
@@ -37,6 +37,10 @@ lib.pq2_quantize_act.restype = ctypes.c_int
 lib.pq2_quantize_act.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
 lib.pq2_gemm.restype = ctypes.c_int
 lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.pq2_gemm_kernel_path.restype = ctypes.c_int
+lib.pq2_gemm_kernel_path.argtypes = [_I64, _I64, _I64]
+lib.pq2_gemm_path.restype = ctypes.c_int
+lib.pq2_gemm_path.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
 lib.pq2_gemm_group_dots.restype = ctypes.c_int
 lib.pq2_gemm_group_dots.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
 lib.pq2_linear.restype = ctypes.c_int
@@ -46,7 +50,15 @@ LINEAR_MAX_M = 4    # PQ2_LINEAR_MAX_M
 
 # Every extern "C" symbol declared in include/pq2.h.
 ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_gemm",
-               "pq2_linear", "pq2_gemm_group_dots")
+               "pq2_gemm_kernel_path", "pq2_gemm_path", "pq2_linear", "pq2_gemm_group_dots")
+
+PATH_NAMES = {PATH_GEMV: "gemv_dot4", PATH_SMALL: "small_mfma", PATH_PREFILL: "prefill_mfma",
+              PATH_PANEL: "small_panel"}
+
+
+def gemm_kernel_path(M: int, N: int, K: int) -> int:
+    """PATH_* that pq2_gemm takes for this shape on the current device (-1: bad shape)."""
+    return int(lib.pq2_gemm_kernel_path(M, N, K))
 
 
 class PQ2Error(RuntimeError):
@@ -120,6 +132,25 @@ def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Ten
     _need(y, "y", torch.float32, (M, N))
     _check(lib.pq2_gemm(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
                         wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
+
+
+def pq2_gemm_path(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
+                  wscale: torch.Tensor, y: torch.Tensor, path: int, stream=None) -> None:
+    """pq2_gemm through the selected kernel path (PATH_*)."""
+    M, K = _mk(q)
+    N = int(codes.shape[0])
+    G = K // GROUP
+    _need(q, "q", torch.int8, (M, K))
+    _need(s, "s", torch.float32, (M, G))
+    _need(t, "t", torch.int32, (M, G))
+    _need(codes, "codes", torch.uint8, (N, K // 4))
+    if wscale.dtype == torch.float16:
+        wscale = wscale.view(torch.int16)
+    _need(wscale, "wscale", torch.int16, (N, G))
+    _need(y, "y", torch.float32, (M, N))
+    _check(lib.pq2_gemm_path(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
+                             wscale.data_ptr(), y.data_ptr(), M, N, K, int(path),
+                             _stream(q, stream)))
 
 
 def pq2_linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor, y: torch.Tensor,

@@ -18,7 +18,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpq2.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["pq2_abi.cpp", "quantize.hip", "gemv_dot4.hip", "small_mfma.hip", "prefill_mfma.hip"]
+SOURCES = ["pq2_abi.cpp", "quantize.hip", "gemv_dot4.hip", "small_mfma.hip", "small_panel.hip",
+           "prefill_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

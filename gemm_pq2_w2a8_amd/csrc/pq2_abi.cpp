@@ -29,6 +29,8 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
             return from_hip(pq2::launch_small(q, t, codes, out, M, N, K, stream));
         case PQ2_PATH_PREFILL:
             return from_hip(pq2::launch_prefill(q, t, codes, out, M, N, K, stream));
+        case PQ2_PATH_PANEL:
+            return from_hip(pq2::launch_small_panel(q, t, codes, out, M, N, K, stream));
         default:
             return PQ2_ERR_ARG;
     }
@@ -36,13 +38,31 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
 
 // Kernel choice of pq2_gemm (from MI355X measurements on the decode and
 // small-batch shapes): the dot4 GEMV reads only the real token rows and wins
-// for M <= 2 everywhere, and for M = 3..4 on large matrices (N*K > 2^25); the
-// 16-token MFMA kernel wins for M = 3..4 on smaller ones and up to M = 16.
+// for M <= 2 everywhere. For 3 <= M <= 16 the persistent panel kernel wins
+// on large matrices (N*K > 2^25) and, from M = 8, on every size it can hold
+// (K from 2048 to 8192); otherwise the dot4 GEMV for M = 3..4 on large
+// matrices with K too large for the panel, else the 16-token MFMA kernel.
+#ifndef PQ2_AUTO_OVERRIDE
+#define PQ2_AUTO_OVERRIDE
+#endif
 int auto_path(int64_t M, int64_t N, int64_t K) {
+    PQ2_AUTO_OVERRIDE
     if (M <= 2) return PQ2_PATH_GEMV;
-    if (M <= pq2::kGemvMaxM && N * K > (int64_t(1) << 25)) return PQ2_PATH_GEMV;
+    const bool large = N * K > (int64_t(1) << 25);
+    if (M <= 16 && (large || M >= 8) && pq2::small_panel_fits(M, K)) return PQ2_PATH_PANEL;
+    if (M <= pq2::kGemvMaxM && large) return PQ2_PATH_GEMV;
     if (M <= 16 && K <= pq2::kSmallMaxK) return PQ2_PATH_SMALL;
     return PQ2_PATH_PREFILL;
+}
+
+// Resolves PQ2_PATH_AUTO and rejects a path that cannot run this shape.
+pq2_status resolve_path(int &path, int64_t M, int64_t N, int64_t K) {
+    if (path == PQ2_PATH_AUTO) path = auto_path(M, N, K);
+    if (path == PQ2_PATH_GEMV && M > pq2::kGemvMaxM) return PQ2_ERR_ARG;
+    if (path == PQ2_PATH_SMALL && (M > 16 || K > pq2::kSmallMaxK)) return PQ2_ERR_ARG;
+    if (path == PQ2_PATH_PANEL && !pq2::small_panel_fits(M, K)) return PQ2_ERR_ARG;
+    if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PANEL) return PQ2_ERR_ARG;
+    return PQ2_OK;
 }
 
 }  // namespace
@@ -86,6 +106,26 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uin
     return run_path(auto_path(M, N, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
 }
 
+int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K) {
+    if (check_mnk(M, N, K) != PQ2_OK) return -1;
+    return auto_path(M, N, K);
+}
+
+pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
+                         const uint16_t *wscale, float *y, int64_t M, int64_t N, int64_t K,
+                         int path, void *hip_stream) {
+    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, N, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
+        !aligned(wscale, 2) || !aligned(y, 4))
+        return PQ2_ERR_ALIGN;
+    st = resolve_path(path, M, N, K);
+    if (st != PQ2_OK) return st;
+    const pq2::GemmOut out{y, nullptr, s, wscale};
+    return run_path(path, q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+}
+
 pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
                       int64_t M, int64_t N, int64_t K, void *hip_stream) {
     static_assert(PQ2_LINEAR_MAX_M <= pq2::kGemvMaxM, "the fused GEMV covers pq2_linear");
@@ -107,10 +147,8 @@ pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t 
     if (st != PQ2_OK) return st;
     if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(t, 4) || !aligned(d, 4))
         return PQ2_ERR_ALIGN;
-    if (path == PQ2_PATH_AUTO) path = auto_path(M, N, K);
-    if (path == PQ2_PATH_GEMV && M > pq2::kGemvMaxM) return PQ2_ERR_ARG;
-    if (path == PQ2_PATH_SMALL && (M > 16 || K > pq2::kSmallMaxK)) return PQ2_ERR_ARG;
-    if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PREFILL) return PQ2_ERR_ARG;
+    st = resolve_path(path, M, N, K);
+    if (st != PQ2_OK) return st;
     const pq2::GemmOut out{nullptr, d, nullptr, nullptr};
     return run_path(path, q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
 }

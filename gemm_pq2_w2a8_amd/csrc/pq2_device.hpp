@@ -193,6 +193,15 @@ __device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lan
     }
 }
 
+// Buffer resource over [base, base + bytes) (bytes clamped to 32 bits; every
+// offset used is in range by construction, the hardware range check is a
+// second guard: loads beyond the range return zero). Word 3 selects 32-bit
+// raw data, as for all gfx9 buffers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes >= 0xffffffffLL ? (int)0xffffffffu : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
 __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

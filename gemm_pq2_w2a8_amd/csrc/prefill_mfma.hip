@@ -89,14 +89,6 @@ struct PfCfg {
     };
 };
 
-// Buffer resource over [base, base + bytes) (bytes clamped to 32 bits; every
-// offset used is in range by construction, the hardware range check is a
-// second guard). Word 3 selects 32-bit raw data, as for all gfx9 buffers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const int n = bytes >= 0xffffffffLL ? (int)0xffffffffu : (int)bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
-
 // 16-byte staging chunks: global -> registers (buffer loads: fixed per-lane
 // offset plus a uniform group offset), registers -> LDS. Native vector
 // types: copies of the HIP uint4 struct become memcpys that can leave the

@@ -76,7 +76,9 @@ enum {
     PQ2_PATH_AUTO = 0,      /* same choice as pq2_gemm */
     PQ2_PATH_GEMV = 1,      /* M <= 4 only: the v_dot4 GEMV */
     PQ2_PATH_SMALL = 2,     /* M <= 16, K <= 32768: the small-batch MFMA kernel */
-    PQ2_PATH_PREFILL = 3    /* any M: the tiled MFMA GEMM */
+    PQ2_PATH_PREFILL = 3,   /* any M: the tiled MFMA GEMM */
+    PQ2_PATH_PANEL = 4      /* M <= 16, 2048 <= K <= 8192: the persistent
+                               small-batch MFMA kernel (activation panel in LDS) */
 };
 
 /* Returns PQ2_ABI_VERSION of the loaded library. */
@@ -100,13 +102,16 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
 
 /*
  * y = the PQ2_0 product defined above. The kernel depends on M:
- *   M <= 2, or M <= 4 with N*K > 2^25
- *                 -> GEMV streaming code words into v_dot4 (2-bit planes
+ *   M <= 2        -> GEMV streaming code words into v_dot4 (2-bit planes
  *                    masked out of each 32-bit word, no decode step; each
  *                    word serves every token row);
- *   other M <= 16 -> small-batch kernel on int8 MFMA, tokens padded to 16
- *                    (K <= 32768; larger K takes the tiled kernel);
- *   M >= 17       -> tiled int8 MFMA GEMM (prefill).
+ *   3 <= M <= 16  -> persistent small-batch kernel on int8 MFMA with the
+ *                    activation panel in LDS (PQ2_PATH_PANEL) when N*K > 2^25
+ *                    or M >= 8 and the panel fits (2048 <= K <= 8192);
+ *                    else the GEMV for M <= 4 with N*K > 2^25; else the
+ *                    16-token MFMA kernel (K <= 32768);
+ *   otherwise     -> tiled int8 MFMA GEMM (prefill).
+ * pq2_gemm_kernel_path reports the choice.
  * Group dots are exact int32; the float32 epilogue sums the G terms in an
  * order that differs from a sequential sum only by float32 rounding.
  */
@@ -136,11 +141,31 @@ pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wsca
                       int64_t M, int64_t N, int64_t K, void *hip_stream);
 
 /*
+ * The PQ2_PATH_* kernel path pq2_gemm takes for this shape on the current
+ * device, or -1 when pq2_gemm would reject the shape (PQ2_ERR_SHAPE). Pure
+ * host query; enqueues nothing.
+ */
+int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Test and tuning entry: pq2_gemm through the selected kernel path instead of
+ * pq2_gemm's own choice. Arguments, layouts and results as for pq2_gemm; path
+ * is one of PQ2_PATH_* with the limits listed for pq2_gemm_group_dots
+ * (PQ2_ERR_ARG otherwise).
+ */
+pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t,
+                         const uint8_t *codes, const uint16_t *wscale, float *y,
+                         int64_t M, int64_t N, int64_t K, int path, void *hip_stream);
+
+/*
  * Test and diagnostic entry: runs the main loop of the selected kernel path
  * but stores the exact per-group dots instead of the float epilogue:
  *   d int32 [M][N][G],  d[m][n][g] = D[m][n][g] as defined above.
- * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M <= 4 and
- * PQ2_PATH_SMALL requires M <= 16 and K <= 32768 (else PQ2_ERR_ARG).
+ * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M <= 4,
+ * PQ2_PATH_SMALL requires M <= 16 and K <= 32768, PQ2_PATH_PANEL requires
+ * M <= 16 and 2048 <= K <= 8192 and a device whose LDS per block holds the
+ * activation panel and its tables (MI355X: M * (K + 16) + 320 * K / 128
+ * + 16512 bytes <= 160 KiB) (else PQ2_ERR_ARG).
  */
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t,
                                const uint8_t *codes, int32_t *d,

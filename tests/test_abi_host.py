@@ -91,10 +91,36 @@ def test_group_dots_validation():
     assert f(P, P, P, P, 5, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG   # GEMV: M <= 4
     assert f(P, P, P, P, 17, 8, 128, pq2.PATH_SMALL, None) == ERR_ARG
     assert f(P, P, P, P, 16, 8, 32768 + 128, pq2.PATH_SMALL, None) == ERR_ARG
+    assert f(P, P, P, P, 8, 8, 1920, pq2.PATH_PANEL, None) == ERR_ARG
     assert f(P, P, P, P, 1, 8, 128, 7, None) == ERR_ARG
     assert f(P, P, P, P, 1, 8, 128, -1, None) == ERR_ARG
     assert f(P, P, P + 8, P, 1, 8, 128, 0, None) == ERR_ALIGN   # codes needs 16 B
     assert f(P + 8, P, P, P, 1, 8, 128, 0, None) == ERR_ALIGN   # q needs 16 B
+
+
+def test_gemm_path_validation():
+    f = pq2.lib.pq2_gemm_path
+    assert f(None, P, P, P, P, P, 1, 8, 128, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 8, 200, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, 1, None) == ERR_ALIGN
+    assert f(P, P, P, P, P, P, 5, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG
+    assert f(P, P, P, P, P, P, 17, 8, 1024, pq2.PATH_SMALL, None) == ERR_ARG
+    assert f(P, P, P, P, P, P, 17, 8, 1024, pq2.PATH_PANEL, None) == ERR_ARG   # M <= 16
+    assert f(P, P, P, P, P, P, 8, 8, 1920, pq2.PATH_PANEL, None) == ERR_ARG    # K >= 2048
+    assert f(P, P, P, P, P, P, 8, 8, 8320, pq2.PATH_PANEL, None) == ERR_ARG    # K <= 8192
+    assert f(P, P, P, P, P, P, 1, 8, 128, 5, None) == ERR_ARG
+
+
+def test_kernel_path_query():
+    f = pq2.lib.pq2_gemm_kernel_path
+    assert f(1, 8, 100) == -1 and f(0, 8, 128) == -1
+    assert f(1, 5120, 6144) == pq2.PATH_GEMV
+    assert f(2, 17408, 5120) == pq2.PATH_GEMV
+    assert f(17, 8, 128) == pq2.PATH_PREFILL
+    assert f(16, 8, 32768 + 128) == pq2.PATH_PREFILL
+    # without a GPU the panel kernel never fits: the 16-token kernel is chosen
+    assert f(8, 5120, 17408) == pq2.PATH_SMALL
 
 
 def test_python_binding_rejects_cpu_tensors():

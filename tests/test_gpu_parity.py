@@ -148,6 +148,23 @@ def test_group_dots_small(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
+PANEL_SHAPES = [(1, 40, 2048), (2, 7, 2048), (3, 300, 2176), (5, 4100, 2304), (8, 4130, 5120),
+                (16, 8200, 2048), (8, 520, 8192), (11, 5000, 3200), (16, 4097, 6144)]
+
+
+@pytest.mark.parametrize("M,N,K", PANEL_SHAPES)
+def test_group_dots_panel(pq2, M, N, K):
+    """The persistent small-batch kernel: odd G (a half-empty last group pair),
+    ragged K slices (pairs not a multiple of the wave count), several tiles per
+    block with a ragged last tile, N below one tile."""
+    print(f"dots panel M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 1000 + N + K + 2)
+    qn, t = rand_q(M, K, rng)
+    codes = synth.draw_codes(N, K, rng, synth.PREFILL_CODES)
+    np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, pq2.PATH_PANEL),
+                                  oracle.group_dots(qn, codes))
+
+
 PREFILL_SHAPES = [(1, 1, 128), (17, 129, 384), (130, 300, 1024), (257, 129, 640), (128, 128, 128)]
 
 
@@ -161,21 +178,21 @@ def test_group_dots_prefill(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
-@pytest.mark.parametrize("path,M", [(1, 1), (1, 4), (2, 5), (3, 20)])
+@pytest.mark.parametrize("path,M", [(1, 1), (1, 4), (2, 5), (3, 20), (4, 7)])
 def test_code3_is_plus_two(pq2, path, M):
     """Code 3 is not a PQ2_0 code; both sides decode it as +2."""
     rng = np.random.default_rng(path)
-    N, K = 40, 256
+    N, K = 40, 2048 if path == 4 else 256     # the panel kernel needs K >= 2048
     qn, t = rand_q(M, K, rng)
     c = rng.integers(0, 4, size=(N, K)).astype(np.uint8)
     codes = synth.pack_codes(c)
     np.testing.assert_array_equal(gpu_dots(pq2, qn, t, codes, path), oracle.group_dots(qn, codes))
 
 
-@pytest.mark.parametrize("path,M", [(1, 1), (1, 3), (2, 16), (3, 130)])
+@pytest.mark.parametrize("path,M", [(1, 1), (1, 3), (2, 16), (3, 130), (4, 16)])
 def test_extreme_dots(pq2, path, M):
     """q = +-127 everywhere with codes 2 or 0: |D| = 16256, the int32 extreme of a group."""
-    N, K = 20, 384
+    N, K = 20, 2048 if path == 4 else 384
     qn = np.full((M, K), 127, np.int8)
     qn[::2] = -127
     t = qn.reshape(M, -1, G).astype(np.int32).sum(-1).astype(np.int32)
@@ -202,6 +219,29 @@ def test_gemm_y_within_tolerance(pq2, M, N, K):
     y = host(pq2.linear(dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))))
     yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
     assert oracle.rel_err(y, yo, tabs) < TOL
+
+
+PATH_Y = [(1, 3, 300, 1024), (2, 5, 130, 1024), (4, 5, 4100, 2176), (4, 16, 8200, 2048),
+          (4, 8, 300, 8192), (4, 16, 5000, 7168), (4, 1, 33, 2048), (3, 16, 130, 640)]
+
+
+@pytest.mark.parametrize("path,M,N,K", PATH_Y)
+def test_gemm_path_y(pq2, path, M, N, K):
+    """y through each kernel path (pq2_gemm_path) against the oracle; with unit scales
+    every partial sum is an integer below 2^24, so y is then exact."""
+    print(f"gemm path={path} M={M} N={N} K={K}", flush=True)
+    x = synth.activations(M, K, M + N + path, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(N + K + path))
+    qo, so, to = oracle.quantize(x)
+    qd, td, cd = dev(oracle.plane_order(qo)), dev(to), dev(w.codes)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm_path(qd, dev(so), td, cd, dev(w.wscale_bits.view(np.int16)), y, path)
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(host(y), yo, tabs) < TOL
+    ones_w = torch.full((N, K // G), 0x3C00, dtype=torch.int16, device="cuda")
+    pq2.pq2_gemm_path(qd, torch.ones((M, K // G), device="cuda"), td, cd, ones_w, y, path)
+    D = oracle.group_dots(qo, w.codes)
+    np.testing.assert_array_equal(host(y), D.sum(-1).astype(np.float32))
 
 
 def test_tiny_workload(pq2):
@@ -299,6 +339,7 @@ FULL = [
     ("small_m4_up", 4, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("small_m3_down", 3, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("small_m16_up", 16, 17408, 5120, synth.UNIFORM_CODES, 0.01),
+    ("small_m8_up", 8, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("small_m8_down", 8, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
     ("prefill_m4096_up", 4096, 17408, 5120, synth.PREFILL_CODES, 0.0),
@@ -352,7 +393,8 @@ def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
 
 @pytest.mark.parametrize("M,N,K,path", [(1, 5120, 6144, 1), (4, 5120, 6144, 1),
                                         (2, 2048, 17408, 1), (16, 5120, 6144, 2),
-                                        (16, 2048, 17408, 2), (256, 1024, 5120, 3)])
+                                        (16, 2048, 17408, 2), (256, 1024, 5120, 3),
+                                        (16, 4100, 5120, 4), (9, 17408, 8192, 4)])
 def test_full_row_dots(pq2, M, N, K, path):
     """Exact per-group dots over whole decode-size weight matrices."""
     print(f"full dots M={M} N={N} K={K} path={path}", flush=True)
