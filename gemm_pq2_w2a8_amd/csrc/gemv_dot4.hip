@@ -34,8 +34,12 @@
 //  * Memory-level parallelism: a lane issues the code loads (and the weight
 //    scale of each chunk's group) of IB chunk iterations x RP rows at once
 //    (one batch); the next batch -- of the same row group or the next one --
-//    is in flight while the current one is computed. The first batch and all
-//    staging loads share one memory round trip.
+//    is in flight while the current one is computed. The staging loads go
+//    out first and the first batch right behind them, in one memory round
+//    trip; the block computes on each code word as it arrives. Six loads
+//    per batch: the decode shapes' rows then split into whole batches
+//    (K = 6144: 3 iterations x 2 rows), so no lane re-reads a chunk whose
+//    line is still in flight.
 //  * Planes 0 and 2 are masked to bits 0..1 (plane 2 after one shift by 4);
 //    planes 1 and 3 are masked in place at bits 2..3, which is 4 * code, and
 //    go to a second accumulator divided by 4 (exactly) before the two are
@@ -71,7 +75,7 @@ __device__ __forceinline__ int token_of(int u, int n) {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
-constexpr int kLoadsPerBatch = 8;                 // uint4 code loads per lane per batch
+constexpr int kLoadsPerBatch = 6;                 // uint4 code loads per lane per batch
 constexpr int64_t kMaxStage = 40960;              // activations staged per window (all tokens)
 constexpr int kQStagePer = kMaxStage / 16 / kGemvThreads;   // q chunks per thread
 constexpr int kSTStagePer = (kMaxStage / 128 + kGemvThreads - 1) / kGemvThreads;  // s, t per thread
@@ -147,18 +151,64 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
     auto load_x = [&](int64_t kx, int base) __attribute__((always_inline)) {
         const int wkx = (int)((K - kx < window) ? K - kx : window);
         const int wgx = wkx / kGroup, ngx = MT * wgx;
+        // rounds i with a group for some slot (a uniform bound); the rest
+        // quantise zeros that are never stored
+        const int rounds = (ngx - base + kSlots - 1) / kSlots;
 #pragma unroll
         for (int i = 0; i < kXRound; ++i) {
-            int gi = base + slot + kSlots * i;
-            gi = gi < ngx ? gi : ngx - 1;
-            const int m = token_of<MT>(gi, wgx), gw = gi - m * wgx;
-            const int64_t mc = m < M ? m : M - 1;
-            xv[i] = *reinterpret_cast<const float4 *>(x + mc * K + kx + kGroup * gw + 4 * lane32);
+            xv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (i < rounds) {
+                int gi = base + slot + kSlots * i;
+                gi = gi < ngx ? gi : ngx - 1;
+                const int m = token_of<MT>(gi, wgx), gw = gi - m * wgx;
+                const int64_t mc = m < M ? m : M - 1;
+                xv[i] = *reinterpret_cast<const float4 *>(x + mc * K + kx + kGroup * gw + 4 * lane32);
+            }
         }
     };
 
     // ---------------------------------------------------------------- staging
-    // window k0 of wk activations per token: q [token][plane][chunk],
+    // q, s, t of window k0 into registers (the non-fused variant), issued
+    // ahead of the first code batch: loads complete in issue order for the
+    // wait counter, so the LDS stores below then wait only for these loads
+    // and the block starts computing while its codes are still arriving.
+    v4i qs[kQStagePer];
+    float sv[kSTStagePer];
+    int32_t tv[kSTStagePer];
+    auto stage_load = [&](int64_t k0, int wk) __attribute__((always_inline)) {
+        const int wg = wk / kGroup;
+        const int nq = wk / 16;                   // 16-byte q chunks per token
+        // only the passes the window needs (a uniform bound): a clamped load
+        // past the end re-reads the last chunk, so every extra pass would
+        // queue behind a line already in flight
+        const int passes = (MT * nq + kGemvThreads - 1) / kGemvThreads;
+#pragma unroll
+        for (int i = 0; i < kQStagePer; ++i) {
+            if (i < passes) {
+                int u = (int)threadIdx.x + i * kGemvThreads;
+                u = u < MT * nq ? u : MT * nq - 1;
+                const int m = token_of<MT>(u, nq), uu = u - m * nq;
+                const int64_t mc = m < M ? m : M - 1;
+                qs[i] = reinterpret_cast<const v4i *>(q + mc * K + k0)[uu];
+            }
+        }
+        const int st_passes = (MT * wg + kGemvThreads - 1) / kGemvThreads;
+#pragma unroll
+        for (int i = 0; i < kSTStagePer; ++i) {
+            sv[i] = 0.0f;
+            tv[i] = 0;
+            if (i < st_passes) {
+                int e = (int)threadIdx.x + i * kGemvThreads;
+                e = e < MT * wg ? e : MT * wg - 1;
+                const int m = token_of<MT>(e, wg), gi = e - m * wg;
+                const int64_t mc = m < M ? m : M - 1;
+                if (!DOTS) sv[i] = s[mc * G + k0 / kGroup + gi];
+                tv[i] = t[mc * G + k0 / kGroup + gi];
+            }
+        }
+    };
+
+    // window k0 of wk activations per token into LDS: q [token][plane][chunk],
     // s [token][g], t [token][g]. Ends with a barrier.
     auto stage = [&](int64_t k0, int wk) __attribute__((always_inline)) {
         const int wg = wk / kGroup;
@@ -198,27 +248,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
             }
         } else {
             const int nq = wk / 16;                   // 16-byte q chunks per token
-            v4i qs[kQStagePer];
-#pragma unroll
-            for (int i = 0; i < kQStagePer; ++i) {
-                int u = (int)threadIdx.x + i * kGemvThreads;
-                u = u < MT * nq ? u : MT * nq - 1;
-                const int m = token_of<MT>(u, nq), uu = u - m * nq;
-                const int64_t mc = m < M ? m : M - 1;
-                qs[i] = reinterpret_cast<const v4i *>(q + mc * K + k0)[uu];
-            }
-            float sv[kSTStagePer];
-            int32_t tv[kSTStagePer];
-#pragma unroll
-            for (int i = 0; i < kSTStagePer; ++i) {
-                int e = (int)threadIdx.x + i * kGemvThreads;
-                e = e < MT * wg ? e : MT * wg - 1;
-                const int m = token_of<MT>(e, wg), gi = e - m * wg;
-                const int64_t mc = m < M ? m : M - 1;
-                sv[i] = 0.0f;
-                if (!DOTS) sv[i] = s[mc * G + k0 / kGroup + gi];
-                tv[i] = t[mc * G + k0 / kGroup + gi];
-            }
 #pragma unroll
             for (int i = 0; i < kQStagePer; ++i) {
                 const int u = threadIdx.x + i * kGemvThreads;
@@ -369,26 +398,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
         // persistent: stage once, then every row group of this block
         const int wk = (int)K;
         const int64_t count = (n_rg - rg0 + gridDim.x - 1) / gridDim.x;
-        if constexpr (FUSED) {
-            load_x(0, 0);
-            asm volatile("" ::: "memory");     // keep the x loads ahead of the codes
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        if constexpr (FUSED) load_x(0, 0);
+        else stage_load(0, wk);
+        asm volatile("" ::: "memory");         // keep the staging loads ahead of the codes
+        __builtin_amdgcn_sched_barrier(0);
         load_batch(bufa, wsa, rg0, 0, wk / 64 / CL, 0);
-        if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
         stage(0, wk);
         run(0, wk, rg0, count, true);
     } else {
         // one row group per block, windows in turn
         for (int64_t k0 = 0; k0 < K; k0 += window) {
             const int wk = __builtin_amdgcn_readfirstlane((int)((K - k0 < window) ? K - k0 : window));
-            if constexpr (FUSED) {
-                load_x(k0, 0);
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            if constexpr (FUSED) load_x(k0, 0);
+            else stage_load(k0, wk);
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
             load_batch(bufa, wsa, rg0, k0, wk / 64 / CL, 0);
-            if constexpr (FUSED) __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
             stage(k0, wk);
             run(k0, wk, rg0, 1, k0 + window >= K);
             if (k0 + window < K) __syncthreads();    // window buffer is reused
