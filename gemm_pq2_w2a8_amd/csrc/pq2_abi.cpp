@@ -40,7 +40,7 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
 // small-batch shapes): the dot4 GEMV reads only the real token rows and wins
 // for M <= 2 everywhere. For 3 <= M <= 16 the persistent panel kernel wins
 // on large matrices (N*K > 2^25) and, from M = 8, on every size it can hold
-// (K from 2048 to 8192); otherwise the dot4 GEMV for M = 3..4 on large
+// (K from 2048 to 18432, within LDS); otherwise the dot4 GEMV for M = 3..4 on large
 // matrices with K too large for the panel, else the 16-token MFMA kernel.
 #ifndef PQ2_AUTO_OVERRIDE
 #define PQ2_AUTO_OVERRIDE

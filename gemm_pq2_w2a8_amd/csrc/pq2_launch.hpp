@@ -39,7 +39,7 @@ hipError_t launch_small(const int8_t *q, const int32_t *t, const uint8_t *codes,
 // The persistent small-batch kernel keeps the M x K activation panel in LDS:
 // K <= kPanelMaxK, K >= 16 * 128, M <= 16, and the panel plus tables must fit
 // the device's LDS per block (small_panel_fits checks all of it).
-constexpr int64_t kPanelMaxK = 8192;
+constexpr int64_t kPanelMaxK = 18432;
 
 bool small_panel_fits(int64_t M, int64_t K);
 

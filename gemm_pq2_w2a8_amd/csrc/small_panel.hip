@@ -44,6 +44,10 @@
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace pq2 {
 
 namespace {
@@ -54,18 +58,25 @@ namespace {
 
 constexpr int kPanelPad = 16;       // LDS row stride of the panel: K + 16 bytes
 
-// LDS bytes: panel [Mr][K + 16]; s and -t tables [G][16]; weight scales of two
-// tiles [2][16][G + 1] floats; partials [2][NW][64][4] floats.
-__host__ __device__ constexpr int64_t panel_lds_bytes(int64_t Mr, int64_t K, int nw) {
-    return Mr * (K + kPanelPad) + 2 * 16 * (K / kGroup) * 4 + 2 * 16 * (K / kGroup + 1) * 4 +
+// LDS bytes for K chunks of up to gc groups: panel [Mr][128 gc + 16]; s and -t
+// tables [gc][16]; weight scales of two tiles [2][16][gc + 1] floats;
+// partials [2][NW][64][4] floats.
+__host__ __device__ constexpr int64_t panel_lds_bytes(int64_t Mr, int64_t gc, int nw) {
+    return Mr * (kGroup * gc + kPanelPad) + 2 * 16 * gc * 4 + 2 * 16 * (gc + 1) * 4 +
            2 * (int64_t)nw * kWave * 16;
 }
 
+// Split-K: the G groups are cut into chunks of gsplit groups (the last one
+// shorter); blocks [s * bps, (s + 1) * bps) take chunk s for every tile
+// (tiles bl, bl + bps, ... for block bl of the chunk) and write their sums to
+// part[s][M][N] instead of y. One chunk (gsplit = G, bps = gridDim.x) is the
+// plain case.
 template <int NW, int GS, int R, bool DOTS>
 __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
+    int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M, int64_t N, int64_t K,
+    int gsplit, int bps) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int T = NW * kWave;
     const int tid = threadIdx.x;
@@ -75,51 +86,67 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     const int lg = lane >> 4;
     const int sh0 = 2 * (lg >> 1);
     const int G = (int)(K / kGroup);
-    const int GP = G + 1;
     const int KB = (int)(K / 4);                 // code bytes per weight row
-    const int RS = (int)K + kPanelPad;
     const int Mr = M < 16 ? (int)M : 16;
     const int64_t NT = (N + 15) / 16;
-    const int B = gridDim.x;
     const int bid = blockIdx.x;
-    const int cnt = (int)((NT - bid + B - 1) / B);    // tiles of this block (>= 1)
+    const int sidx = bid / bps;                  // K chunk of this block
+    const int bl = bid - sidx * bps;             // block within the chunk
+    const int g0 = sidx * gsplit;                // first group of the chunk
+    const int Gc = G - g0 < gsplit ? G - g0 : gsplit;
+    const int GP = Gc + 1;
+    const int RS = kGroup * gsplit + kPanelPad;  // panel row stride
+    const int cnt = (int)((NT - bl + bps - 1) / bps);    // tiles of this block (>= 1)
 
-    int8_t *panel = reinterpret_cast<int8_t *>(smem);                        // [Mr][RS]
-    float *s_l = reinterpret_cast<float *>(smem + (int64_t)Mr * RS);         // [G][16]
-    int32_t *tn_l = reinterpret_cast<int32_t *>(s_l + 16 * G);               // [G][16], -t
-    float *wsl = reinterpret_cast<float *>(tn_l + 16 * G);                   // [2][16][GP]
-    float *part = wsl + 2 * 16 * GP;                                         // [2][NW][64][4]
+    int8_t *panel = reinterpret_cast<int8_t *>(smem);                          // [Mr][RS]
+    float *s_l = reinterpret_cast<float *>(smem + (int64_t)Mr * RS);           // [Gc][16]
+    int32_t *tn_l = reinterpret_cast<int32_t *>(s_l + 16 * gsplit);            // [Gc][16], -t
+    float *wsl = reinterpret_cast<float *>(tn_l + 16 * gsplit);                // [2][16][GP]
+    float *part = wsl + 2 * 16 * (gsplit + 1);                                 // [2][NW][64][4]
 
-    // This wave's group pairs of every tile: [p_lo, p_lo + np), 1 <= np <= GS
-    // (the last pair has one group when G is odd).
-    const int NP = (G + 1) / 2;
+    // This wave's group pairs of the chunk: [p_lo, p_lo + np), 1 <= np <= GS
+    // (the last pair has one group when Gc is odd).
+    const int NP = (Gc + 1) / 2;
     const int p_lo = (NP * wave) / NW;
     const int np = (NP * (wave + 1)) / NW - p_lo;
-    const int voff_c = c * KB + 16 * lg;
+    const int voff_c = c * KB + 32 * g0 + 16 * lg;
 
-    // Weight scales of a tile: 16 * G halves, contiguous, as 2G 16-byte
-    // chunks; thread tid < 2G loads chunk tid, elements 8 * tid .. + 7, whose
-    // (row, column) in the [16][G] block starts at divmod(8 * tid, G).
-    const int nwc = 2 * G;
-    int w_row0 = 0, w_col0 = 0;
+    // Weight scales of a tile's chunk, [16][Gc] halves, as 16-byte chunks of
+    // eight groups. With G % 8 == 0 (every split shape) each row's part is
+    // whole chunks: thread tid < 2 Gc takes row tid / (Gc/8), chunk tid %
+    // (Gc/8). Otherwise (one chunk only) the tile's 16 G halves are
+    // contiguous and thread tid < 2G takes elements 8 tid .. 8 tid + 7, at
+    // (row, column) = divmod(8 tid, G). Only the waves that hold a chunk load.
+    const bool rowwise = G % 8 == 0;
+    const int nwc = 2 * Gc;
+    const bool ws_wave = !DOTS && wave * kWave < nwc;
+    int w_row0 = 0, w_col0 = 0, w_off = 0;
     if (!DOTS) {
-        w_row0 = (8 * tid) / G;
-        w_col0 = 8 * tid - w_row0 * G;
+        if (rowwise) {
+            const int cpr8 = Gc / 8;
+            w_row0 = tid / cpr8;
+            w_col0 = 8 * (tid - w_row0 * cpr8);
+            w_off = 2 * (w_row0 * G + g0 + w_col0);
+        } else {
+            w_row0 = (8 * tid) / G;
+            w_col0 = 8 * tid - w_row0 * G;
+            w_off = 16 * tid;
+        }
     }
 
     v4i cb[R][GS];
     v4i wv[R];
-    // Past the block's last tile the loads still issue (so the wait counts
-    // stay exact) but every lane reads the first bytes of the last tile:
-    // one cache line per instruction instead of a tile slice.
+    // Past the block's last tile the code loads still issue (so the wait
+    // counts stay exact) but every lane reads the first bytes of the last
+    // tile: one cache line per instruction instead of a tile slice.
     auto load_tile = [&](v4i (&cbs)[GS], v4i &wvs, int j) __attribute__((always_inline)) {
         const bool live = j < cnt;
         const int jj = live ? j : cnt - 1;
-        const int64_t n0 = (int64_t)(bid + (int64_t)jj * B) * 16;
+        const int64_t n0 = (int64_t)(bl + (int64_t)jj * bps) * 16;
         const int64_t rows = N - n0 < 16 ? N - n0 : 16;
-        if (!DOTS) {
+        if (ws_wave) {
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + n0 * G, rows * G * 2);
-            wvs = __builtin_amdgcn_raw_buffer_load_b128(rw, live && tid < nwc ? 16 * tid : 0, 0, 0);
+            wvs = __builtin_amdgcn_raw_buffer_load_b128(rw, tid < nwc ? w_off : 0, 0, 0);
         }
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + n0 * KB, rows * KB);
         const int oc = live ? voff_c : 0;
@@ -131,14 +158,14 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     };
     // Eight halves of a weight-scale chunk -> floats in wsl[buf][row][col].
     auto store_ws = [&](const v4i &wvs, int buf) __attribute__((always_inline)) {
-        if (!DOTS && tid < nwc) {
+        if (ws_wave && tid < nwc) {
             float *dst = wsl + buf * 16 * GP;
             int row = w_row0, col = w_col0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const uint32_t word = (uint32_t)wvs[k >> 1];
                 dst[row * GP + col] = half_bits_to_float((uint16_t)((k & 1) ? word >> 16 : word));
-                if (++col == G) {
+                if (++col == Gc) {
                     col = 0;
                     ++row;
                 }
@@ -146,13 +173,13 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
         }
     };
 
-    // Prefetch the first R - 1 tiles, then stage the panel, the token tables
-    // and the first tile's weight scales.
+    // Prefetch the first R - 1 tiles, then stage the panel chunk, the token
+    // tables and the first tile's weight scales.
 #pragma unroll
     for (int u = 0; u < R - 1; ++u) load_tile(cb[u], wv[u], u);
 
     {
-        const int cpr = (int)(K / 16);           // 16-byte chunks per token row
+        const int cpr = 8 * Gc;                  // 16-byte chunks per token row of the chunk
         const int total = Mr * cpr;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)Mr * K);
         // chunk e = tid + i*T sits at (row, col) = divmod(e, cpr), advanced by
@@ -160,20 +187,15 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
         const int dr = T / cpr, dc = T - dr * cpr;
         int row = tid / cpr, col = tid - row * cpr;
         for (int e0 = 0; e0 < total; e0 += 8 * T) {
-            v4i v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = e0 + tid + i * T;
-                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * (e < total ? e : total - 1), 0, 0);
-            }
-            // unconditional stores (a conditional one lets the compiler sink its
-            // load next to it): a chunk past the end was loaded as the last
-            // chunk and is stored there again, the same bytes
+            // a chunk past the end is the last chunk again, loaded and stored
+            // unconditionally (a conditional store lets the compiler sink the
+            // load next to it), the same bytes twice
+            int rr[8], cc[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const bool in = e0 + tid + i * T < total;
-                *reinterpret_cast<v4i *>(panel + (in ? row : Mr - 1) * RS +
-                                         16 * (in ? col : cpr - 1)) = v[i];
+                rr[i] = in ? row : Mr - 1;
+                cc[i] = in ? col : cpr - 1;
                 row += dr;
                 col += dc;
                 if (col >= cpr) {
@@ -181,13 +203,20 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
                     ++row;
                 }
             }
+            v4i v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, rr[i] * (int)K + kGroup * g0 + 16 * cc[i], 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<v4i *>(panel + rr[i] * RS + 16 * cc[i]) = v[i];
         }
         // tables [g][m]: tokens m >= M hold 0 (their outputs are never stored)
-        for (int e = tid; e < 16 * G; e += T) {
+        for (int e = tid; e < 16 * Gc; e += T) {
             const int g = e >> 4, m = e & 15;
             const bool ok = m < Mr;
-            if (!DOTS) s_l[e] = ok ? s[m * G + g] : 0.0f;
-            tn_l[e] = ok ? -t[m * G + g] : 0;
+            if (!DOTS) s_l[e] = ok ? s[m * G + g0 + g] : 0.0f;
+            tn_l[e] = ok ? -t[m * G + g0 + g] : 0;
         }
         store_ws(wv[0], 0);
     }
@@ -196,7 +225,8 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     const int arow = c < Mr ? c : Mr - 1;   // padded tokens read the last real row
     const int8_t *abase = panel + arow * RS + 16 * lg;
 
-    // One group: planes of this lane's four code words (w), two MFMAs, epilogue.
+    // One group (g within the chunk): planes of this lane's four code words
+    // (w), two MFMAs, epilogue.
     auto group = [&](const v4i &w, int g, int64_t n0, const float *wrow, float (&acc)[4])
         __attribute__((always_inline)) {
         const v4i a0 = *reinterpret_cast<const v4i *>(abase + kGroup * g);
@@ -216,7 +246,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * lg + i;
-                if (m < M && n < N) d[((int64_t)m * N + n) * G + g] = dd[i];
+                if (m < M && n < N) d[((int64_t)m * N + n) * G + g0 + g] = dd[i];
             }
         } else {
             const float4 sv = *reinterpret_cast<const float4 *>(s_l + 16 * g + 4 * lg);
@@ -229,7 +259,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     };
 
     auto compute_tile = [&](const v4i (&cbs)[GS], int j) __attribute__((always_inline)) {
-        const int64_t n0 = (int64_t)(bid + (int64_t)j * B) * 16;
+        const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
         const float *wrow = wsl + (j & 1) * 16 * GP + c * GP;
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -245,7 +275,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
                     hi[k] = (int)sw[1];
                 }
                 group(lo, g, n0, wrow, acc);
-                if (g + 1 < G) group(hi, g + 1, n0, wrow, acc);
+                if (g + 1 < Gc) group(hi, g + 1, n0, wrow, acc);
             }
         }
         if (!DOTS) {
@@ -255,9 +285,10 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
         }
     };
 
+    float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
     auto reduce_tile = [&](int j) __attribute__((always_inline)) {
         if (!DOTS && tid < 256) {
-            const int64_t n0 = (int64_t)(bid + (int64_t)j * B) * 16;
+            const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
             const float *pb = part + (j & 1) * (NW * kWave * 4);
             // output (token m, row cc) sits in lane cc + 16 * (m / 4), slot m % 4
             const int m = tid >> 4, cc = tid & 15;
@@ -266,7 +297,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
 #pragma unroll
             for (int w = 1; w < NW; ++w) v += pb[w * kWave * 4 + at];
             const int64_t n = n0 + cc;
-            if (m < M && n < N) y[(int64_t)m * N + n] = v;
+            if (m < M && n < N) out[(int64_t)m * N + n] = v;
         }
     };
 
@@ -282,6 +313,17 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
             }
         }
     }
+}
+
+// y = sum over the S chunks of part[s] (fixed order s = 0, 1, ...).
+__global__ __launch_bounds__(256) void panel_split_sum_kernel(const float *__restrict__ part,
+                                                              float *__restrict__ y, int64_t MN,
+                                                              int S) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= MN) return;
+    float v = part[i];
+    for (int k = 1; k < S; ++k) v += part[(int64_t)k * MN + i];
+    y[i] = v;
 }
 
 struct DevLimits {
@@ -314,62 +356,164 @@ const DevLimits &dev_limits() {
 
 template <int NW, int GS, int R>
 hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                      const GemmOut &out, int64_t M, int64_t N, int64_t K, int64_t blocks,
-                      size_t lds, hipStream_t stream) {
+                      const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
+                      int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
     if (out.d) {
         hipLaunchKernelGGL((small_panel_kernel<NW, GS, R, true>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, nullptr, t, codes, nullptr, nullptr,
-                           out.d, M, N, K);
+                           out.d, nullptr, M, N, K, gsplit, bps);
     } else {
         hipLaunchKernelGGL((small_panel_kernel<NW, GS, R, false>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, M, N, K);
+                           nullptr, part, M, N, K, gsplit, bps);
     }
     return hipGetLastError();
 }
 
-// GS = ceil(pairs / NW) exactly: a wave's short slice costs at most one repeated load.
+// GS = ceil(pairs per chunk / NW) exactly: a wave's short slice costs at most
+// one repeated load.
 template <int NW, int R>
 hipError_t launch_gs(int64_t gs, const int8_t *q, const int32_t *t, const uint8_t *codes,
-                     const GemmOut &out, int64_t M, int64_t N, int64_t K, int64_t blocks,
-                     size_t lds, hipStream_t stream) {
+                     const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
+                     int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
+#define PQ2_PANEL_GS(V)                                                                        \
+    case V:                                                                                    \
+        return launch_cfg<NW, V, R>(q, t, codes, out, part, M, N, K, gsplit, bps, blocks, lds, \
+                                    stream);
     switch (gs) {
-        case 1: return launch_cfg<NW, 1, R>(q, t, codes, out, M, N, K, blocks, lds, stream);
-        case 2: return launch_cfg<NW, 2, R>(q, t, codes, out, M, N, K, blocks, lds, stream);
-        case 3: return launch_cfg<NW, 3, R>(q, t, codes, out, M, N, K, blocks, lds, stream);
-        case 4: return launch_cfg<NW, 4, R>(q, t, codes, out, M, N, K, blocks, lds, stream);
+        PQ2_PANEL_GS(1)
+        PQ2_PANEL_GS(2)
+        PQ2_PANEL_GS(3)
+        PQ2_PANEL_GS(4)
+        PQ2_PANEL_GS(5)
+        PQ2_PANEL_GS(6)
+        PQ2_PANEL_GS(7)
+        PQ2_PANEL_GS(8)
+        PQ2_PANEL_GS(9)
         default: return hipErrorInvalidValue;
     }
+#undef PQ2_PANEL_GS
+}
+
+constexpr int kPanelWaves = 8;
+constexpr int kPanelMaxSplits = 8;
+constexpr int kPanelMaxGs = 9;
+
+struct PanelPlan {
+    int S = 0;            // K chunks (0: no plan fits)
+    int gsplit = 0;       // groups per chunk (the last one may be shorter)
+    int bps = 0;          // blocks per chunk
+    int64_t lds = 0;
+    int64_t gs = 0;       // group pairs per wave and tile
+};
+
+// Whether K can be cut into S chunks here: chunks of a multiple of 8 groups
+// (whole 16-byte scale chunks per row), at least 16 groups each (every wave
+// gets a pair), at most 9 pairs per wave, LDS within the block limit.
+PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l) {
+    PanelPlan p;
+    const int64_t G = K / kGroup, NT = (N + 15) / 16, Mr = M < 16 ? M : 16;
+    if (S > 1 && G % 8 != 0) return p;
+    const int64_t gsplit = S == 1 ? G : ((G + S - 1) / S + 7) / 8 * 8;
+    if ((G + gsplit - 1) / gsplit != S) return p;
+    const int64_t last = G - (S - 1) * gsplit;
+    if ((gsplit < last ? gsplit : last) < 16) return p;
+    const int64_t gs = ((gsplit + 1) / 2 + kPanelWaves - 1) / kPanelWaves;
+    if (gs > kPanelMaxGs) return p;
+    const int64_t lds = panel_lds_bytes(Mr, gsplit, kPanelWaves);
+    if (lds > l.lds_block) return p;
+    const int64_t per_cu = (S == 1 && l.lds_cu / lds >= 2) ? 2 : 1;
+    int64_t bps = l.cus * per_cu / S;
+    if (bps > NT) bps = NT;
+    if (bps < 1) return p;
+    p.S = S;
+    p.gsplit = (int)gsplit;
+    p.bps = (int)bps;
+    p.lds = lds;
+    p.gs = gs;
+    return p;
+}
+
+// The split count (MI355X sweeps over the 5120 / 6144 / 17408 shapes at M = 4,
+// 8, 16): chunks of about 48 groups win -- K = 5120 and 6144 unsplit (a
+// split's partial sums and extra summing launch cost more than the uneven
+// tile count saves), K = 17408 in three chunks (14.3-15.8 us against 15.6-17.4
+// for two or four, 17.0 unsplit where it fits). The count nearest to G / 48
+// that fits, preferring more chunks.
+PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s) {
+    PanelPlan none;
+    if (l.cus <= 0 || M < 1 || M > 16) return none;
+    if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_for(force_s, M, N, K, l) : none;
+    const int64_t G = K / kGroup;
+    int target = (int)((G + 24) / 48);
+    target = target < 1 ? 1 : target > kPanelMaxSplits ? kPanelMaxSplits : target;
+    for (int S = target; S <= kPanelMaxSplits; ++S) {
+        const PanelPlan p = plan_for(S, M, N, K, l);
+        if (p.S) return p;
+    }
+    for (int S = target - 1; S >= 1; --S) {
+        const PanelPlan p = plan_for(S, M, N, K, l);
+        if (p.S) return p;
+    }
+    return none;
+}
+
+// Device workspace for split partials, one per (device, stream): work on one
+// stream is ordered, so calls on different streams never share a buffer.
+// Grown on demand (hipFree of the old buffer waits for the device), kept
+// until the process ends.
+float *split_workspace(size_t bytes, hipStream_t stream) {
+    struct Buf {
+        void *ptr = nullptr;
+        size_t size = 0;
+    };
+    static std::mutex mu;
+    static std::map<std::pair<int, hipStream_t>, Buf> bufs;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    Buf &b = bufs[{dev, stream}];
+    if (b.size < bytes) {
+        if (b.ptr && hipFree(b.ptr) != hipSuccess) return nullptr;
+        b.ptr = nullptr;
+        b.size = 0;
+        if (hipMalloc(&b.ptr, bytes) != hipSuccess) return nullptr;
+        b.size = bytes;
+    }
+    return static_cast<float *>(b.ptr);
 }
 
 }  // namespace
 
 bool small_panel_fits(int64_t M, int64_t K) {
     if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
-    const DevLimits &l = dev_limits();
-    return l.cus > 0 && panel_lds_bytes(M, K, 8) <= l.lds_block;
+    return plan_panel(M, 16, K, dev_limits(), 0).S > 0;
 }
 
-// One block of 8 waves per CU (two when two panels fit in a CU's LDS), at
-// most one block per 16-row tile; each wave gets (G / 2) / 8 group pairs per
-// tile (G >= 16 is required; K <= 8192 keeps that at most 4). Two tiles in
-// flight per wave (R = 2): sweeps on MI355X found deeper rings, 16-wave
-// blocks and two blocks per CU all slower on the 5120 / 6144 / 17408 shapes.
+// One block of 8 waves per CU (two when two panels fit in a CU's LDS and K
+// is not split). Two tiles in flight per wave (R = 2): sweeps on MI355X found
+// deeper rings, 16-wave blocks and two blocks per CU all slower on the
+// 5120 / 6144 / 17408 shapes.
 hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *codes,
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream) {
-    constexpr int kNW = 8;
-    const DevLimits &l = dev_limits();
-    const int64_t Mr = M < 16 ? M : 16;
-    const int64_t G = K / kGroup;
-    const int64_t lds = panel_lds_bytes(Mr, K, kNW);
-    if (l.cus <= 0 || lds > l.lds_block || (G + 1) / 2 < kNW) return hipErrorInvalidValue;
-    int64_t blocks = l.cus * (l.lds_cu / lds >= 2 ? 2 : 1);
+    int force_s = 0;
     PANEL_TUNE_OVERRIDE
-    const int64_t NT = (N + 15) / 16;
-    if (blocks > NT) blocks = NT;
-    const int64_t gs = ((G + 1) / 2 + kNW - 1) / kNW;
-    return launch_gs<kNW, 2>(gs, q, t, codes, out, M, N, K, blocks, lds, stream);
+    const PanelPlan plan = plan_panel(M, N, K, dev_limits(), force_s);
+    if (plan.S == 0) return hipErrorInvalidValue;
+    float *part = nullptr;
+    if (plan.S > 1 && !out.d) {
+        part = split_workspace((size_t)plan.S * M * N * sizeof(float), stream);
+        if (!part) return hipErrorOutOfMemory;
+    }
+    const int64_t blocks = (int64_t)plan.bps * plan.S;
+    hipError_t e = launch_gs<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K,
+                                             plan.gsplit, plan.bps, blocks, plan.lds, stream);
+    if (e != hipSuccess || !part) return e;
+    const int64_t MN = M * N;
+    hipLaunchKernelGGL(panel_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
+                       stream, part, out.y, MN, plan.S);
+    return hipGetLastError();
 }
 
 }  // namespace pq2

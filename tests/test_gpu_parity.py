@@ -149,14 +149,17 @@ def test_group_dots_small(pq2, M, N, K):
 
 
 PANEL_SHAPES = [(1, 40, 2048), (2, 7, 2048), (3, 300, 2176), (5, 4100, 2304), (8, 4130, 5120),
-                (16, 8200, 2048), (8, 520, 8192), (11, 5000, 3200), (16, 4097, 6144)]
+                (16, 8200, 2048), (8, 520, 8192), (11, 5000, 3200), (16, 4097, 6144),
+                (4, 1030, 17408), (5, 300, 18432), (3, 200, 17536), (16, 700, 17408),
+                (9, 5000, 16384), (16, 33, 18432)]
 
 
 @pytest.mark.parametrize("M,N,K", PANEL_SHAPES)
 def test_group_dots_panel(pq2, M, N, K):
     """The persistent small-batch kernel: odd G (a half-empty last group pair),
     ragged K slices (pairs not a multiple of the wave count), several tiles per
-    block with a ragged last tile, N below one tile."""
+    block with a ragged last tile, N below one tile, and K split into chunks
+    (the panel of 16 x 17408 bytes does not fit one block's LDS)."""
     print(f"dots panel M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M * 1000 + N + K + 2)
     qn, t = rand_q(M, K, rng)
@@ -222,7 +225,8 @@ def test_gemm_y_within_tolerance(pq2, M, N, K):
 
 
 PATH_Y = [(1, 3, 300, 1024), (2, 5, 130, 1024), (4, 5, 4100, 2176), (4, 16, 8200, 2048),
-          (4, 8, 300, 8192), (4, 16, 5000, 7168), (4, 1, 33, 2048), (3, 16, 130, 640)]
+          (4, 8, 300, 8192), (4, 16, 5000, 7168), (4, 5, 700, 17408), (4, 16, 1000, 17408),
+          (4, 12, 5120, 18432), (4, 1, 33, 2048), (3, 16, 130, 640)]
 
 
 @pytest.mark.parametrize("path,M,N,K", PATH_Y)
@@ -341,6 +345,7 @@ FULL = [
     ("small_m16_up", 16, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("small_m8_up", 8, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("small_m8_down", 8, 5120, 17408, synth.UNIFORM_CODES, 0.01),
+    ("small_m16_down", 16, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
     ("prefill_m4096_up", 4096, 17408, 5120, synth.PREFILL_CODES, 0.0),
 ]
@@ -422,3 +427,42 @@ def test_small_multi_tile_blocks(pq2, M, N, K):
     nn = np.concatenate([rng.integers(0, N, 38), [0, N - 1]] * M)
     ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
     assert oracle.rel_err(y[mm, nn], ys, ts) < TOL
+
+
+def test_split_k_streams_and_workspace_growth(pq2):
+    """Split-K y (K = 17408 at M = 16: three chunks through the library's
+    workspace) is identical on repeated calls, on two streams running
+    concurrently with different inputs (one workspace per stream), and after
+    the workspace grows for a larger N."""
+    M, K = 16, 17408
+    outs = []
+    for N in (300, 700, 300):     # grows, then a smaller call reuses the buffer
+        assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PANEL
+        x = synth.activations(M, K, N, outlier_frac=0.01)
+        w = synth.weights(N, K, synth.matrix_seed(N))
+        q, s, t = pq2.quantize_act(dev(x))
+        cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        pq2.pq2_gemm(q, s, t, cd, wd, y)
+        y0 = host(y)
+        pq2.pq2_gemm(q, s, t, cd, wd, y)
+        np.testing.assert_array_equal(host(y), y0)
+        qo, so, to = oracle.quantize(x)
+        mm = np.repeat(np.arange(M), 24)
+        nn = np.random.default_rng(N).integers(0, N, M * 24)
+        ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
+        assert oracle.rel_err(y0[mm, nn], ys, ts) < TOL
+        outs.append((q, s, t, cd, wd, y0))
+    # the two 700- and 300-row problems at once on two streams
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    ya = torch.empty((M, 700), dtype=torch.float32, device="cuda")
+    yb = torch.empty((M, 300), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            pq2.pq2_gemm(*outs[1][:5], ya, stream=sa)
+        with torch.cuda.stream(sb):
+            pq2.pq2_gemm(*outs[0][:5], yb, stream=sb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ya), outs[1][5])
+    np.testing.assert_array_equal(host(yb), outs[0][5])
