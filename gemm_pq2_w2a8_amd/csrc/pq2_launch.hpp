@@ -47,6 +47,14 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream);
 
+// Split-K support shared by the panel and prefill kernels: a device buffer
+// of at least `bytes`, one per (device, stream), allocated on first need and
+// kept (nullptr if allocation fails); and y = sum over the chunks of
+// part[c][M*N], added in chunk order.
+float *split_workspace(size_t bytes, hipStream_t stream);
+hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
+                            hipStream_t stream);
+
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream);

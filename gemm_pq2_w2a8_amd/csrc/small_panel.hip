@@ -458,6 +458,8 @@ PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int fo
     return none;
 }
 
+}  // namespace
+
 // Device workspace for split partials, one per (device, stream): work on one
 // stream is ordered, so calls on different streams never share a buffer.
 // Grown on demand (hipFree of the old buffer waits for the device), kept
@@ -483,7 +485,12 @@ float *split_workspace(size_t bytes, hipStream_t stream) {
     return static_cast<float *>(b.ptr);
 }
 
-}  // namespace
+hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(panel_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
+                       stream, part, y, MN, splits);
+    return hipGetLastError();
+}
 
 bool small_panel_fits(int64_t M, int64_t K) {
     if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
@@ -510,10 +517,7 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
     hipError_t e = launch_gs<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K,
                                              plan.gsplit, plan.bps, blocks, plan.lds, stream);
     if (e != hipSuccess || !part) return e;
-    const int64_t MN = M * N;
-    hipLaunchKernelGGL(panel_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
-                       stream, part, out.y, MN, plan.S);
-    return hipGetLastError();
+    return launch_split_sum(part, out.y, M * N, plan.S, stream);
 }
 
 }  // namespace pq2

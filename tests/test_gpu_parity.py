@@ -168,7 +168,8 @@ def test_group_dots_panel(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
-PREFILL_SHAPES = [(1, 1, 128), (17, 129, 384), (130, 300, 1024), (257, 129, 640), (128, 128, 128)]
+PREFILL_SHAPES = [(1, 1, 128), (17, 129, 384), (130, 300, 1024), (257, 129, 640), (128, 128, 128),
+                  (20, 300, 4096), (130, 1000, 3200)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL_SHAPES)
@@ -226,7 +227,8 @@ def test_gemm_y_within_tolerance(pq2, M, N, K):
 
 PATH_Y = [(1, 3, 300, 1024), (2, 5, 130, 1024), (4, 5, 4100, 2176), (4, 16, 8200, 2048),
           (4, 8, 300, 8192), (4, 16, 5000, 7168), (4, 5, 700, 17408), (4, 16, 1000, 17408),
-          (4, 12, 5120, 18432), (4, 1, 33, 2048), (3, 16, 130, 640)]
+          (4, 12, 5120, 18432), (4, 1, 33, 2048), (3, 16, 130, 640), (3, 40, 700, 5120),
+          (3, 200, 520, 2048)]
 
 
 @pytest.mark.parametrize("path,M,N,K", PATH_Y)
