@@ -315,6 +315,258 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     }
 }
 
+// LDS bytes of the staged-codes variant: the panel-kernel tables plus one
+// [16][32 gc + 16] code tile.
+__host__ __device__ constexpr int64_t panel_lds_bytes_sc(int64_t Mr, int64_t gc, int nw) {
+    return panel_lds_bytes(Mr, gc, nw) + 16 * (32 * gc + kPanelPad);
+}
+
+// Staged-codes variant: same arithmetic and split-K scheme, but each 16-row
+// code tile (its chunk of K) is read with fully coalesced 16-byte loads --
+// every cache line is requested by exactly one instruction -- into LDS, and
+// each wave reads its MFMA B operands from there (row c, bytes 32 g + 16 (lg
+// & 1) of group g). A load that covers part of a line which another load has
+// in flight stalls the L1 until the line arrives; the register layout of the
+// operands cannot be loaded in whole lines. Waves split the chunk's groups
+// (not pairs); code tiles are prefetched RQ tiles ahead in registers, and a
+// tile takes two barriers (partials and code buffer, then the next tile's
+// codes in LDS).
+template <int NW, int GSG, int CPT, int RQ, bool DOTS>
+__global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
+    int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M, int64_t N, int64_t K,
+    int gsplit, int bps) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int T = NW * kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int c = lane & 15;
+    const int lg = lane >> 4;
+    const int sh0 = 2 * (lg >> 1);
+    const int G = (int)(K / kGroup);
+    const int KB = (int)(K / 4);
+    const int Mr = M < 16 ? (int)M : 16;
+    const int64_t NT = (N + 15) / 16;
+    const int bid = blockIdx.x;
+    const int sidx = bid / bps;
+    const int bl = bid - sidx * bps;
+    const int g0 = sidx * gsplit;
+    const int Gc = G - g0 < gsplit ? G - g0 : gsplit;
+    const int GP = Gc + 1;
+    const int RS = kGroup * gsplit + kPanelPad;
+    const int RSC = 32 * gsplit + kPanelPad;     // code tile row stride in LDS
+    const int cnt = (int)((NT - bl + bps - 1) / bps);
+
+    int8_t *panel = reinterpret_cast<int8_t *>(smem);                          // [Mr][RS]
+    float *s_l = reinterpret_cast<float *>(smem + (int64_t)Mr * RS);           // [Gc][16]
+    int32_t *tn_l = reinterpret_cast<int32_t *>(s_l + 16 * gsplit);            // [Gc][16], -t
+    float *wsl = reinterpret_cast<float *>(tn_l + 16 * gsplit);                // [2][16][GP]
+    float *part = wsl + 2 * 16 * (gsplit + 1);                                 // [2][NW][64][4]
+    uint8_t *codes_l = reinterpret_cast<uint8_t *>(part + 2 * NW * kWave * 4); // [16][RSC]
+
+    // this wave's groups of the chunk: [g_lo, g_lo + ng), 1 <= ng <= GSG
+    const int g_lo = (Gc * wave) / NW;
+    const int ng = (Gc * (wave + 1)) / NW - g_lo;
+
+    // code tile chunks: e = tid + i*T < 32 Gc is (row e / (2 Gc), 16-byte
+    // column e % (2 Gc)); past the end a lane re-reads the last chunk in the
+    // same instruction
+    const int nch = 32 * Gc;
+    int goff[CPT], loff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        int e = tid + i * T;
+        e = e < nch ? e : nch - 1;
+        const int row = e / (2 * Gc), col = e - row * 2 * Gc;
+        goff[i] = row * KB + 32 * g0 + 16 * col;
+        loff[i] = row * RSC + 16 * col;
+    }
+
+    // weight scales as in the register-operand kernel
+    const bool rowwise = G % 8 == 0;
+    const int nwc = 2 * Gc;
+    const bool ws_wave = !DOTS && wave * kWave < nwc;
+    int w_row0 = 0, w_col0 = 0, w_off = 0;
+    if (!DOTS) {
+        if (rowwise) {
+            const int cpr8 = Gc / 8;
+            w_row0 = tid / cpr8;
+            w_col0 = 8 * (tid - w_row0 * cpr8);
+            w_off = 2 * (w_row0 * G + g0 + w_col0);
+        } else {
+            w_row0 = (8 * tid) / G;
+            w_col0 = 8 * tid - w_row0 * G;
+            w_off = 16 * tid;
+        }
+    }
+
+    v4i cr[RQ][CPT];
+    v4i wv[RQ];
+    // tile j's codes (and scales) into register set cs; past the block's last
+    // tile every lane reads the first 16 bytes of the last tile (one line)
+    auto load_tile = [&](v4i (&crs)[CPT], v4i &wvs, int j) __attribute__((always_inline)) {
+        const bool live = j < cnt;
+        const int jj = live ? j : cnt - 1;
+        const int64_t n0 = (int64_t)(bl + (int64_t)jj * bps) * 16;
+        const int64_t rows = N - n0 < 16 ? N - n0 : 16;
+        if (ws_wave) {
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + n0 * G, rows * G * 2);
+            wvs = __builtin_amdgcn_raw_buffer_load_b128(rw, tid < nwc ? w_off : 0, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + n0 * KB, rows * KB);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            crs[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, live ? goff[i] : 0, 0, 0);
+    };
+    auto store_codes = [&](const v4i (&crs)[CPT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) *reinterpret_cast<v4i *>(codes_l + loff[i]) = crs[i];
+    };
+    auto store_ws = [&](const v4i &wvs, int buf) __attribute__((always_inline)) {
+        if (ws_wave && tid < nwc) {
+            float *dst = wsl + buf * 16 * GP;
+            int row = w_row0, col = w_col0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t word = (uint32_t)wvs[k >> 1];
+                dst[row * GP + col] = half_bits_to_float((uint16_t)((k & 1) ? word >> 16 : word));
+                if (++col == Gc) {
+                    col = 0;
+                    ++row;
+                }
+            }
+        }
+    };
+
+    // prologue: RQ tiles in flight, the panel chunk and tables, tile 0 into
+    // LDS, its register set refilled with tile RQ
+#pragma unroll
+    for (int u = 0; u < RQ; ++u) load_tile(cr[u], wv[u], u);
+    {
+        const int cpr = 8 * Gc;
+        const int total = Mr * cpr;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)Mr * K);
+        const int dr = T / cpr, dc = T - dr * cpr;
+        int row = tid / cpr, col = tid - row * cpr;
+        for (int e0 = 0; e0 < total; e0 += 8 * T) {
+            int rr[8], cc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool in = e0 + tid + i * T < total;
+                rr[i] = in ? row : Mr - 1;
+                cc[i] = in ? col : cpr - 1;
+                row += dr;
+                col += dc;
+                if (col >= cpr) {
+                    col -= cpr;
+                    ++row;
+                }
+            }
+            v4i v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, rr[i] * (int)K + kGroup * g0 + 16 * cc[i], 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<v4i *>(panel + rr[i] * RS + 16 * cc[i]) = v[i];
+        }
+        for (int e = tid; e < 16 * Gc; e += T) {
+            const int g = e >> 4, m = e & 15;
+            const bool ok = m < Mr;
+            if (!DOTS) s_l[e] = ok ? s[m * G + g0 + g] : 0.0f;
+            tn_l[e] = ok ? -t[m * G + g0 + g] : 0;
+        }
+        store_codes(cr[0]);
+        store_ws(wv[0], 0);
+        load_tile(cr[0], wv[0], RQ);
+    }
+    __syncthreads();
+
+    const int arow = c < Mr ? c : Mr - 1;
+    const int8_t *abase = panel + arow * RS + 16 * lg;
+    const uint8_t *bbase = codes_l + c * RSC + 16 * (lg & 1);
+
+    auto compute_tile = [&](int j) __attribute__((always_inline)) {
+        const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
+        const float *wrow = wsl + (j & 1) * 16 * GP + c * GP;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int b = 0; b < GSG; ++b) {
+            if (b < ng) {
+                const int g = g_lo + b;
+                const v4i w = *reinterpret_cast<const v4i *>(bbase + 32 * g);
+                const v4i a0 = *reinterpret_cast<const v4i *>(abase + kGroup * g);
+                const v4i a1 = *reinterpret_cast<const v4i *>(abase + kGroup * g + 64);
+                const v4i seed = *reinterpret_cast<const v4i *>(tn_l + 16 * g + 4 * lg);
+                v4i b0, b1;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t sh = (uint32_t)w[k] >> sh0;
+                    b0[k] = (int)(sh & kPlaneMask);
+                    b1[k] = (int)((sh >> 4) & kPlaneMask);
+                }
+                v4i dd = mfma16x16x64(a0, b0, seed);
+                dd = mfma16x16x64(a1, b1, dd);
+                if (DOTS) {
+                    const int64_t n = n0 + c;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * lg + i;
+                        if (m < M && n < N) d[((int64_t)m * N + n) * G + g0 + g] = dd[i];
+                    }
+                } else {
+                    const float4 sv = *reinterpret_cast<const float4 *>(s_l + 16 * g + 4 * lg);
+                    const float wsf = wrow[g];
+                    acc[0] = fmaf((float)dd[0], sv.x * wsf, acc[0]);
+                    acc[1] = fmaf((float)dd[1], sv.y * wsf, acc[1]);
+                    acc[2] = fmaf((float)dd[2], sv.z * wsf, acc[2]);
+                    acc[3] = fmaf((float)dd[3], sv.w * wsf, acc[3]);
+                }
+            }
+        }
+        if (!DOTS) {
+            float *pb = part + (j & 1) * (NW * kWave * 4);
+            *reinterpret_cast<float4 *>(pb + (wave * kWave + lane) * 4) =
+                make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    };
+
+    float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
+    auto reduce_tile = [&](int j) __attribute__((always_inline)) {
+        if (!DOTS && tid < 256) {
+            const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
+            const float *pb = part + (j & 1) * (NW * kWave * 4);
+            const int m = tid >> 4, cc = tid & 15;
+            const int at = (cc + 16 * (m >> 2)) * 4 + (m & 3);
+            float v = pb[at];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += pb[w * kWave * 4 + at];
+            const int64_t n = n0 + cc;
+            if (m < M && n < N) out[(int64_t)m * N + n] = v;
+        }
+    };
+
+    // tile j's codes are in LDS; tile j + 1's in register set (j + 1) % RQ
+    for (int j0 = 0; j0 < cnt; j0 += RQ) {
+#pragma unroll
+        for (int u = 0; u < RQ; ++u) {
+            const int j = j0 + u;
+            if (j < cnt) {
+                compute_tile(j);
+                __syncthreads();            // code buffer free, partials visible
+                reduce_tile(j);
+                const int v = (u + 1) % RQ;
+                store_codes(cr[v]);
+                store_ws(wv[v], (j + 1) & 1);
+                load_tile(cr[v], wv[v], j + 1 + RQ);
+                __syncthreads();            // tile j + 1 in LDS
+            }
+        }
+    }
+}
+
 // y = sum over the S chunks of part[s] (fixed order s = 0, 1, ...).
 __global__ __launch_bounds__(256) void panel_split_sum_kernel(const float *__restrict__ part,
                                                               float *__restrict__ y, int64_t MN,
@@ -395,6 +647,45 @@ hipError_t launch_gs(int64_t gs, const int8_t *q, const int32_t *t, const uint8_
 #undef PQ2_PANEL_GS
 }
 
+template <int NW, int GSG, int RQ>
+hipError_t launch_sc_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                         const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
+                         int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
+    constexpr int CPT = (GSG + 1) / 2;     // ceil(32 gsplit / (64 NW)) for NW = 8
+    if (out.d) {
+        hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, RQ, true>), dim3((unsigned)blocks),
+                           dim3(NW * kWave), lds, stream, q, nullptr, t, codes, nullptr, nullptr,
+                           out.d, nullptr, M, N, K, gsplit, bps);
+    } else {
+        hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, RQ, false>), dim3((unsigned)blocks),
+                           dim3(NW * kWave), lds, stream, q, out.s, t, codes, out.ws, out.y,
+                           nullptr, part, M, N, K, gsplit, bps);
+    }
+    return hipGetLastError();
+}
+
+template <int NW, int RQ>
+hipError_t launch_sc(int64_t gs, const int8_t *q, const int32_t *t, const uint8_t *codes,
+                     const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
+                     int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
+#define PQ2_PANEL_SC(V)                                                                          \
+    case V:                                                                                      \
+        return launch_sc_cfg<NW, V, RQ>(q, t, codes, out, part, M, N, K, gsplit, bps, blocks, lds, \
+                                        stream);
+    switch (gs) {
+        PQ2_PANEL_SC(2)
+        PQ2_PANEL_SC(3)
+        PQ2_PANEL_SC(4)
+        PQ2_PANEL_SC(5)
+        PQ2_PANEL_SC(6)
+        PQ2_PANEL_SC(7)
+        PQ2_PANEL_SC(8)
+        PQ2_PANEL_SC(9)
+        default: return hipErrorInvalidValue;
+    }
+#undef PQ2_PANEL_SC
+}
+
 constexpr int kPanelWaves = 8;
 constexpr int kPanelMaxSplits = 8;
 constexpr int kPanelMaxGs = 9;
@@ -410,7 +701,7 @@ struct PanelPlan {
 // Whether K can be cut into S chunks here: chunks of a multiple of 8 groups
 // (whole 16-byte scale chunks per row), at least 16 groups each (every wave
 // gets a pair), at most 9 pairs per wave, LDS within the block limit.
-PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l) {
+PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l, bool sc) {
     PanelPlan p;
     const int64_t G = K / kGroup, NT = (N + 15) / 16, Mr = M < 16 ? M : 16;
     if (S > 1 && G % 8 != 0) return p;
@@ -418,9 +709,12 @@ PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l) {
     if ((G + gsplit - 1) / gsplit != S) return p;
     const int64_t last = G - (S - 1) * gsplit;
     if ((gsplit < last ? gsplit : last) < 16) return p;
-    const int64_t gs = ((gsplit + 1) / 2 + kPanelWaves - 1) / kPanelWaves;
+    // register-operand kernel: group pairs per wave; staged codes: groups
+    const int64_t gs = sc ? (gsplit + kPanelWaves - 1) / kPanelWaves
+                          : ((gsplit + 1) / 2 + kPanelWaves - 1) / kPanelWaves;
     if (gs > kPanelMaxGs) return p;
-    const int64_t lds = panel_lds_bytes(Mr, gsplit, kPanelWaves);
+    const int64_t lds = sc ? panel_lds_bytes_sc(Mr, gsplit, kPanelWaves)
+                           : panel_lds_bytes(Mr, gsplit, kPanelWaves);
     if (lds > l.lds_block) return p;
     const int64_t per_cu = (S == 1 && l.lds_cu / lds >= 2) ? 2 : 1;
     int64_t bps = l.cus * per_cu / S;
@@ -440,19 +734,20 @@ PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l) {
 // tile count saves), K = 17408 in three chunks (14.3-15.8 us against 15.6-17.4
 // for two or four, 17.0 unsplit where it fits). The count nearest to G / 48
 // that fits, preferring more chunks.
-PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s) {
+PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s,
+                     bool sc) {
     PanelPlan none;
     if (l.cus <= 0 || M < 1 || M > 16) return none;
-    if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_for(force_s, M, N, K, l) : none;
+    if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_for(force_s, M, N, K, l, sc) : none;
     const int64_t G = K / kGroup;
     int target = (int)((G + 24) / 48);
     target = target < 1 ? 1 : target > kPanelMaxSplits ? kPanelMaxSplits : target;
     for (int S = target; S <= kPanelMaxSplits; ++S) {
-        const PanelPlan p = plan_for(S, M, N, K, l);
+        const PanelPlan p = plan_for(S, M, N, K, l, sc);
         if (p.S) return p;
     }
     for (int S = target - 1; S >= 1; --S) {
-        const PanelPlan p = plan_for(S, M, N, K, l);
+        const PanelPlan p = plan_for(S, M, N, K, l, sc);
         if (p.S) return p;
     }
     return none;
@@ -494,7 +789,7 @@ hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
 
 bool small_panel_fits(int64_t M, int64_t K) {
     if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
-    return plan_panel(M, 16, K, dev_limits(), 0).S > 0;
+    return plan_panel(M, 16, K, dev_limits(), 0, false).S > 0;
 }
 
 // One block of 8 waves per CU (two when two panels fit in a CU's LDS and K
@@ -505,8 +800,15 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream) {
     int force_s = 0;
+    // the staged-codes kernel when it has a plan (MI355X sweeps: 2-14 %
+    // faster than the register-operand kernel on five of the nine 5120 /
+    // 6144 / 17408 shapes at M = 4, 8, 16, slower on one; one tile of
+    // register prefetch beat two on all nine)
+    int staged = 1;
     PANEL_TUNE_OVERRIDE
-    const PanelPlan plan = plan_panel(M, N, K, dev_limits(), force_s);
+    PanelPlan plan = plan_panel(M, N, K, dev_limits(), force_s, staged != 0);
+    const bool sc = staged != 0 && plan.S != 0;
+    if (!sc) plan = plan_panel(M, N, K, dev_limits(), force_s, false);
     if (plan.S == 0) return hipErrorInvalidValue;
     float *part = nullptr;
     if (plan.S > 1 && !out.d) {
@@ -514,8 +816,13 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
         if (!part) return hipErrorOutOfMemory;
     }
     const int64_t blocks = (int64_t)plan.bps * plan.S;
-    hipError_t e = launch_gs<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K,
-                                             plan.gsplit, plan.bps, blocks, plan.lds, stream);
+    hipError_t e;
+    if (sc)
+        e = launch_sc<kPanelWaves, 1>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
+                                      plan.bps, blocks, plan.lds, stream);
+    else
+        e = launch_gs<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
+                                      plan.bps, blocks, plan.lds, stream);
     if (e != hipSuccess || !part) return e;
     return launch_split_sum(part, out.y, M * N, plan.S, stream);
 }

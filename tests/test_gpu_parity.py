@@ -151,7 +151,8 @@ def test_group_dots_small(pq2, M, N, K):
 PANEL_SHAPES = [(1, 40, 2048), (2, 7, 2048), (3, 300, 2176), (5, 4100, 2304), (8, 4130, 5120),
                 (16, 8200, 2048), (8, 520, 8192), (11, 5000, 3200), (16, 4097, 6144),
                 (4, 1030, 17408), (5, 300, 18432), (3, 200, 17536), (16, 700, 17408),
-                (9, 5000, 16384), (16, 33, 18432)]
+                (9, 5000, 16384), (16, 33, 18432),
+                (2, 300, 9344), (3, 100, 9344)]   # G = 73: the register-operand variant
 
 
 @pytest.mark.parametrize("M,N,K", PANEL_SHAPES)
