@@ -36,10 +36,12 @@ hipError_t launch_small(const int8_t *q, const int32_t *t, const uint8_t *codes,
                         const GemmOut &out, int64_t M, int64_t N, int64_t K,
                         hipStream_t stream);
 
-// The persistent small-batch kernel keeps the M x K activation panel in LDS:
-// K <= kPanelMaxK, K >= 16 * 128, M <= 16, and the panel plus tables must fit
-// the device's LDS per block (small_panel_fits checks all of it).
+// The persistent small-batch kernel keeps the M x K activation panel (or a
+// K chunk of it) in LDS: K <= kPanelMaxK, K >= 16 * 128, M <= kPanelMaxM,
+// and a split of K into at most 16 chunks whose panel plus tables fit the
+// device's LDS per block (small_panel_fits checks all of it).
 constexpr int64_t kPanelMaxK = 18432;
+constexpr int64_t kPanelMaxM = 64;
 
 bool small_panel_fits(int64_t M, int64_t K);
 

@@ -315,10 +315,13 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     }
 }
 
-// LDS bytes of the staged-codes variant: the panel-kernel tables plus one
-// [16][32 gc + 16] code tile.
-__host__ __device__ constexpr int64_t panel_lds_bytes_sc(int64_t Mr, int64_t gc, int nw) {
-    return panel_lds_bytes(Mr, gc, nw) + 16 * (32 * gc + kPanelPad);
+// LDS bytes of the staged-codes variant for TT token tiles: panel
+// [Mr][128 gc + 16]; s and -t tables [gc][16 TT]; weight scales of two tiles
+// [2][16][gc + 1]; partials [NW][64][4] floats; one [16][32 gc + 16] code
+// tile.
+__host__ __device__ constexpr int64_t panel_lds_bytes_sc(int64_t Mr, int64_t gc, int nw, int tt) {
+    return Mr * (kGroup * gc + kPanelPad) + 2 * 16 * tt * gc * 4 + 2 * 16 * (gc + 1) * 4 +
+           (int64_t)nw * kWave * 16 + 16 * (32 * gc + kPanelPad);
 }
 
 // Staged-codes variant: same arithmetic and split-K scheme, but each 16-row
@@ -328,10 +331,13 @@ __host__ __device__ constexpr int64_t panel_lds_bytes_sc(int64_t Mr, int64_t gc,
 // & 1) of group g). A load that covers part of a line which another load has
 // in flight stalls the L1 until the line arrives; the register layout of the
 // operands cannot be loaded in whole lines. Waves split the chunk's groups
-// (not pairs); code tiles are prefetched RQ tiles ahead in registers, and a
-// tile takes two barriers (partials and code buffer, then the next tile's
-// codes in LDS).
-template <int NW, int GSG, int CPT, int RQ, bool DOTS>
+// (not pairs); the next code tile is prefetched in registers, and a tile
+// takes two barriers (partials and code buffer, then the next tile's codes
+// in LDS).
+// TT token tiles (M <= 16 TT): wave w computes token tile w % TT over its
+// share of the chunk's groups (the NW / TT waves of a token tile split the
+// groups), so each wave keeps one float partial per lane whatever TT is.
+template <int NW, int GSG, int CPT, int TT, bool DOTS>
 __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
@@ -339,15 +345,20 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
     int gsplit, int bps) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int T = NW * kWave;
+    constexpr int TM = 16 * TT;                  // tokens held
+    constexpr int KW = NW / TT;                  // waves per token tile
+    static_assert(KW * TT == NW, "token tiles must divide the waves");
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int tt = wave % TT;
+    const int kw = wave / TT;
     const int c = lane & 15;
     const int lg = lane >> 4;
     const int sh0 = 2 * (lg >> 1);
     const int G = (int)(K / kGroup);
     const int KB = (int)(K / 4);
-    const int Mr = M < 16 ? (int)M : 16;
+    const int Mr = M < TM ? (int)M : TM;
     const int64_t NT = (N + 15) / 16;
     const int bid = blockIdx.x;
     const int sidx = bid / bps;
@@ -360,15 +371,15 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
     const int cnt = (int)((NT - bl + bps - 1) / bps);
 
     int8_t *panel = reinterpret_cast<int8_t *>(smem);                          // [Mr][RS]
-    float *s_l = reinterpret_cast<float *>(smem + (int64_t)Mr * RS);           // [Gc][16]
-    int32_t *tn_l = reinterpret_cast<int32_t *>(s_l + 16 * gsplit);            // [Gc][16], -t
-    float *wsl = reinterpret_cast<float *>(tn_l + 16 * gsplit);                // [2][16][GP]
-    float *part = wsl + 2 * 16 * (gsplit + 1);                                 // [2][NW][64][4]
-    uint8_t *codes_l = reinterpret_cast<uint8_t *>(part + 2 * NW * kWave * 4); // [16][RSC]
+    float *s_l = reinterpret_cast<float *>(smem + (int64_t)Mr * RS);           // [Gc][TM]
+    int32_t *tn_l = reinterpret_cast<int32_t *>(s_l + TM * gsplit);            // [Gc][TM], -t
+    float *wsl = reinterpret_cast<float *>(tn_l + TM * gsplit);                // [2][16][GP]
+    float *part = wsl + 2 * 16 * (gsplit + 1);                                 // [NW][64][4]
+    uint8_t *codes_l = reinterpret_cast<uint8_t *>(part + NW * kWave * 4);     // [16][RSC]
 
     // this wave's groups of the chunk: [g_lo, g_lo + ng), 1 <= ng <= GSG
-    const int g_lo = (Gc * wave) / NW;
-    const int ng = (Gc * (wave + 1)) / NW - g_lo;
+    const int g_lo = (Gc * kw) / KW;
+    const int ng = (Gc * (kw + 1)) / KW - g_lo;
 
     // code tile chunks: e = tid + i*T < 32 Gc is (row e / (2 Gc), 16-byte
     // column e % (2 Gc)); past the end a lane re-reads the last chunk in the
@@ -402,35 +413,35 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
         }
     }
 
-    v4i cr[RQ][CPT];
-    v4i wv[RQ];
-    // tile j's codes (and scales) into register set cs; past the block's last
-    // tile every lane reads the first 16 bytes of the last tile (one line)
-    auto load_tile = [&](v4i (&crs)[CPT], v4i &wvs, int j) __attribute__((always_inline)) {
+    v4i cr[CPT];
+    v4i wv;
+    // tile j's codes (and scales) into registers; past the block's last tile
+    // every lane reads the first 16 bytes of the last tile (one line)
+    auto load_tile = [&](int j) __attribute__((always_inline)) {
         const bool live = j < cnt;
         const int jj = live ? j : cnt - 1;
         const int64_t n0 = (int64_t)(bl + (int64_t)jj * bps) * 16;
         const int64_t rows = N - n0 < 16 ? N - n0 : 16;
         if (ws_wave) {
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + n0 * G, rows * G * 2);
-            wvs = __builtin_amdgcn_raw_buffer_load_b128(rw, tid < nwc ? w_off : 0, 0, 0);
+            wv = __builtin_amdgcn_raw_buffer_load_b128(rw, tid < nwc ? w_off : 0, 0, 0);
         }
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + n0 * KB, rows * KB);
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
-            crs[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, live ? goff[i] : 0, 0, 0);
+            cr[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, live ? goff[i] : 0, 0, 0);
     };
-    auto store_codes = [&](const v4i (&crs)[CPT]) __attribute__((always_inline)) {
+    auto store_codes = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) *reinterpret_cast<v4i *>(codes_l + loff[i]) = crs[i];
+        for (int i = 0; i < CPT; ++i) *reinterpret_cast<v4i *>(codes_l + loff[i]) = cr[i];
     };
-    auto store_ws = [&](const v4i &wvs, int buf) __attribute__((always_inline)) {
+    auto store_ws = [&](int buf) __attribute__((always_inline)) {
         if (ws_wave && tid < nwc) {
             float *dst = wsl + buf * 16 * GP;
             int row = w_row0, col = w_col0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t word = (uint32_t)wvs[k >> 1];
+                const uint32_t word = (uint32_t)wv[k >> 1];
                 dst[row * GP + col] = half_bits_to_float((uint16_t)((k & 1) ? word >> 16 : word));
                 if (++col == Gc) {
                     col = 0;
@@ -440,10 +451,9 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
         }
     };
 
-    // prologue: RQ tiles in flight, the panel chunk and tables, tile 0 into
-    // LDS, its register set refilled with tile RQ
-#pragma unroll
-    for (int u = 0; u < RQ; ++u) load_tile(cr[u], wv[u], u);
+    // prologue: tile 0 in flight, the panel chunk and tables, tile 0 into
+    // LDS, its registers refilled with tile 1
+    load_tile(0);
     {
         const int cpr = 8 * Gc;
         const int total = Mr * cpr;
@@ -472,26 +482,29 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
             for (int i = 0; i < 8; ++i)
                 *reinterpret_cast<v4i *>(panel + rr[i] * RS + 16 * cc[i]) = v[i];
         }
-        for (int e = tid; e < 16 * Gc; e += T) {
-            const int g = e >> 4, m = e & 15;
+        // tables [g][m]: tokens m >= M hold 0 (their outputs are never stored)
+        for (int e = tid; e < TM * Gc; e += T) {
+            const int g = e / TM, m = e - g * TM;
             const bool ok = m < Mr;
             if (!DOTS) s_l[e] = ok ? s[m * G + g0 + g] : 0.0f;
             tn_l[e] = ok ? -t[m * G + g0 + g] : 0;
         }
-        store_codes(cr[0]);
-        store_ws(wv[0], 0);
-        load_tile(cr[0], wv[0], RQ);
+        store_codes();
+        store_ws(0);
+        load_tile(1);
     }
     __syncthreads();
 
-    const int arow = c < Mr ? c : Mr - 1;
+    const int arow = 16 * tt + c < Mr ? 16 * tt + c : Mr - 1;   // padded tokens: last real row
     const int8_t *abase = panel + arow * RS + 16 * lg;
     const uint8_t *bbase = codes_l + c * RSC + 16 * (lg & 1);
+    const int32_t *tnbase = tn_l + 16 * tt + 4 * lg;
+    const float *sbase = s_l + 16 * tt + 4 * lg;
 
     auto compute_tile = [&](int j) __attribute__((always_inline)) {
         const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
         const float *wrow = wsl + (j & 1) * 16 * GP + c * GP;
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
 #pragma unroll
         for (int b = 0; b < GSG; ++b) {
             if (b < ng) {
@@ -499,7 +512,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
                 const v4i w = *reinterpret_cast<const v4i *>(bbase + 32 * g);
                 const v4i a0 = *reinterpret_cast<const v4i *>(abase + kGroup * g);
                 const v4i a1 = *reinterpret_cast<const v4i *>(abase + kGroup * g + 64);
-                const v4i seed = *reinterpret_cast<const v4i *>(tn_l + 16 * g + 4 * lg);
+                const v4i seed = *reinterpret_cast<const v4i *>(tnbase + TM * g);
                 v4i b0, b1;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
@@ -513,57 +526,51 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
                     const int64_t n = n0 + c;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int m = 4 * lg + i;
+                        const int m = 16 * tt + 4 * lg + i;
                         if (m < M && n < N) d[((int64_t)m * N + n) * G + g0 + g] = dd[i];
                     }
                 } else {
-                    const float4 sv = *reinterpret_cast<const float4 *>(s_l + 16 * g + 4 * lg);
                     const float wsf = wrow[g];
-                    acc[0] = fmaf((float)dd[0], sv.x * wsf, acc[0]);
-                    acc[1] = fmaf((float)dd[1], sv.y * wsf, acc[1]);
-                    acc[2] = fmaf((float)dd[2], sv.z * wsf, acc[2]);
-                    acc[3] = fmaf((float)dd[3], sv.w * wsf, acc[3]);
+                    const float4 sv = *reinterpret_cast<const float4 *>(sbase + TM * g);
+                    acc0 = fmaf((float)dd[0], sv.x * wsf, acc0);
+                    acc1 = fmaf((float)dd[1], sv.y * wsf, acc1);
+                    acc2 = fmaf((float)dd[2], sv.z * wsf, acc2);
+                    acc3 = fmaf((float)dd[3], sv.w * wsf, acc3);
                 }
             }
         }
-        if (!DOTS) {
-            float *pb = part + (j & 1) * (NW * kWave * 4);
-            *reinterpret_cast<float4 *>(pb + (wave * kWave + lane) * 4) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
-        }
+        if (!DOTS)
+            *reinterpret_cast<float4 *>(part + (wave * kWave + lane) * 4) =
+                make_float4(acc0, acc1, acc2, acc3);
     };
 
     float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
     auto reduce_tile = [&](int j) __attribute__((always_inline)) {
-        if (!DOTS && tid < 256) {
+        if (!DOTS) {
             const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
-            const float *pb = part + (j & 1) * (NW * kWave * 4);
-            const int m = tid >> 4, cc = tid & 15;
-            const int at = (cc + 16 * (m >> 2)) * 4 + (m & 3);
-            float v = pb[at];
+            // output (token 16 u + ml, row cc) sits in lane cc + 16 (ml / 4),
+            // slot ml % 4 of waves u, u + TT, ..., summed in wave order
+            for (int e = tid; e < TT * 256; e += T) {
+                const int u = e >> 8, ml = (e >> 4) & 15, cc = e & 15;
+                const int at = (u * kWave + cc + 16 * (ml >> 2)) * 4 + (ml & 3);
+                float v = part[at];
 #pragma unroll
-            for (int w = 1; w < NW; ++w) v += pb[w * kWave * 4 + at];
-            const int64_t n = n0 + cc;
-            if (m < M && n < N) out[(int64_t)m * N + n] = v;
+                for (int w = 1; w < KW; ++w) v += part[w * TT * kWave * 4 + at];
+                const int64_t m = 16 * u + ml, n = n0 + cc;
+                if (m < M && n < N) out[m * N + n] = v;
+            }
         }
     };
 
-    // tile j's codes are in LDS; tile j + 1's in register set (j + 1) % RQ
-    for (int j0 = 0; j0 < cnt; j0 += RQ) {
-#pragma unroll
-        for (int u = 0; u < RQ; ++u) {
-            const int j = j0 + u;
-            if (j < cnt) {
-                compute_tile(j);
-                __syncthreads();            // code buffer free, partials visible
-                reduce_tile(j);
-                const int v = (u + 1) % RQ;
-                store_codes(cr[v]);
-                store_ws(wv[v], (j + 1) & 1);
-                load_tile(cr[v], wv[v], j + 1 + RQ);
-                __syncthreads();            // tile j + 1 in LDS
-            }
-        }
+    // tile j's codes are in LDS, tile j + 1's in registers
+    for (int j = 0; j < cnt; ++j) {
+        compute_tile(j);
+        __syncthreads();            // code buffer free, partials visible
+        reduce_tile(j);
+        store_codes();
+        store_ws((j + 1) & 1);
+        load_tile(j + 2);
+        __syncthreads();            // tile j + 1 in LDS; partials free again
     }
 }
 
@@ -647,32 +654,34 @@ hipError_t launch_gs(int64_t gs, const int8_t *q, const int32_t *t, const uint8_
 #undef PQ2_PANEL_GS
 }
 
-template <int NW, int GSG, int RQ>
+template <int NW, int GSG, int TT>
 hipError_t launch_sc_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
                          const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
                          int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
-    constexpr int CPT = (GSG + 1) / 2;     // ceil(32 gsplit / (64 NW)) for NW = 8
+    // 16-byte code chunks per thread: 32 gsplit <= 32 GSG NW / TT chunks
+    constexpr int CPT = (32 * GSG * (NW / TT) + NW * kWave - 1) / (NW * kWave);
     if (out.d) {
-        hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, RQ, true>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, TT, true>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, nullptr, t, codes, nullptr, nullptr,
                            out.d, nullptr, M, N, K, gsplit, bps);
     } else {
-        hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, RQ, false>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, TT, false>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, out.s, t, codes, out.ws, out.y,
                            nullptr, part, M, N, K, gsplit, bps);
     }
     return hipGetLastError();
 }
 
-template <int NW, int RQ>
+template <int NW, int TT>
 hipError_t launch_sc(int64_t gs, const int8_t *q, const int32_t *t, const uint8_t *codes,
                      const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
                      int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
 #define PQ2_PANEL_SC(V)                                                                          \
     case V:                                                                                      \
-        return launch_sc_cfg<NW, V, RQ>(q, t, codes, out, part, M, N, K, gsplit, bps, blocks, lds, \
+        return launch_sc_cfg<NW, V, TT>(q, t, codes, out, part, M, N, K, gsplit, bps, blocks, lds, \
                                         stream);
     switch (gs) {
+        PQ2_PANEL_SC(1)
         PQ2_PANEL_SC(2)
         PQ2_PANEL_SC(3)
         PQ2_PANEL_SC(4)
@@ -687,11 +696,16 @@ hipError_t launch_sc(int64_t gs, const int8_t *q, const int32_t *t, const uint8_
 }
 
 constexpr int kPanelWaves = 8;
-constexpr int kPanelMaxSplits = 8;
+constexpr int kPanelMaxSplits = 16;
 constexpr int kPanelMaxGs = 9;
+
+// 16-token tiles of the staged-codes kernel: 1, 2 or 4 (M <= 16, 32, 64;
+// the tiles must divide the 8 waves)
+int panel_token_tiles(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : 4; }
 
 struct PanelPlan {
     int S = 0;            // K chunks (0: no plan fits)
+    int tt = 1;           // 16-token tiles (staged-codes kernel)
     int gsplit = 0;       // groups per chunk (the last one may be shorter)
     int bps = 0;          // blocks per chunk
     int64_t lds = 0;
@@ -699,21 +713,27 @@ struct PanelPlan {
 };
 
 // Whether K can be cut into S chunks here: chunks of a multiple of 8 groups
-// (whole 16-byte scale chunks per row), at least 16 groups each (every wave
-// gets a pair), at most 9 pairs per wave, LDS within the block limit.
+// (whole 16-byte scale chunks per row) and at least 16 groups each (every
+// wave gets a pair; the staged-codes kernel needs one group per wave of a
+// token tile, 8 suffice), at most 9 pairs or groups per wave, LDS within the
+// block limit. Only the staged-codes kernel takes M > 16.
 PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l, bool sc) {
     PanelPlan p;
-    const int64_t G = K / kGroup, NT = (N + 15) / 16, Mr = M < 16 ? M : 16;
+    const int tt = sc ? panel_token_tiles(M) : 1;
+    const int64_t G = K / kGroup, NT = (N + 15) / 16, Mr = M < 16 * tt ? M : 16 * tt;
+    if (M > 16 * tt) return p;
     if (S > 1 && G % 8 != 0) return p;
     const int64_t gsplit = S == 1 ? G : ((G + S - 1) / S + 7) / 8 * 8;
     if ((G + gsplit - 1) / gsplit != S) return p;
     const int64_t last = G - (S - 1) * gsplit;
-    if ((gsplit < last ? gsplit : last) < 16) return p;
-    // register-operand kernel: group pairs per wave; staged codes: groups
-    const int64_t gs = sc ? (gsplit + kPanelWaves - 1) / kPanelWaves
+    if ((gsplit < last ? gsplit : last) < (sc && S > 1 ? 8 : 16)) return p;
+    // register-operand kernel: group pairs per wave; staged codes: groups per
+    // wave of a token tile
+    const int64_t kw = kPanelWaves / tt;
+    const int64_t gs = sc ? (gsplit + kw - 1) / kw
                           : ((gsplit + 1) / 2 + kPanelWaves - 1) / kPanelWaves;
     if (gs > kPanelMaxGs) return p;
-    const int64_t lds = sc ? panel_lds_bytes_sc(Mr, gsplit, kPanelWaves)
+    const int64_t lds = sc ? panel_lds_bytes_sc(Mr, gsplit, kPanelWaves, tt)
                            : panel_lds_bytes(Mr, gsplit, kPanelWaves);
     if (lds > l.lds_block) return p;
     const int64_t per_cu = (S == 1 && l.lds_cu / lds >= 2) ? 2 : 1;
@@ -721,6 +741,7 @@ PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l, b
     if (bps > NT) bps = NT;
     if (bps < 1) return p;
     p.S = S;
+    p.tt = tt;
     p.gsplit = (int)gsplit;
     p.bps = (int)bps;
     p.lds = lds;
@@ -737,7 +758,7 @@ PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l, b
 PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s,
                      bool sc) {
     PanelPlan none;
-    if (l.cus <= 0 || M < 1 || M > 16) return none;
+    if (l.cus <= 0 || M < 1 || M > (sc ? kPanelMaxM : 16)) return none;
     if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_for(force_s, M, N, K, l, sc) : none;
     const int64_t G = K / kGroup;
     int target = (int)((G + 24) / 48);
@@ -788,8 +809,9 @@ hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
 }
 
 bool small_panel_fits(int64_t M, int64_t K) {
-    if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
-    return plan_panel(M, 16, K, dev_limits(), 0, false).S > 0;
+    if (M < 1 || M > kPanelMaxM || K > kPanelMaxK || K / kGroup < 16) return false;
+    // M <= 16: the register-operand kernel's plan (the fallback) must exist
+    return plan_panel(M, 16, K, dev_limits(), 0, M > 16).S > 0;
 }
 
 // One block of 8 waves per CU (two when two panels fit in a CU's LDS and K
@@ -817,8 +839,14 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
     }
     const int64_t blocks = (int64_t)plan.bps * plan.S;
     hipError_t e;
-    if (sc)
+    if (sc && plan.tt == 1)
         e = launch_sc<kPanelWaves, 1>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
+                                      plan.bps, blocks, plan.lds, stream);
+    else if (sc && plan.tt == 2)
+        e = launch_sc<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
+                                      plan.bps, blocks, plan.lds, stream);
+    else if (sc)
+        e = launch_sc<kPanelWaves, 4>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
                                       plan.bps, blocks, plan.lds, stream);
     else
         e = launch_gs<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,

@@ -77,7 +77,7 @@ enum {
     PQ2_PATH_GEMV = 1,      /* M <= 4 only: the v_dot4 GEMV */
     PQ2_PATH_SMALL = 2,     /* M <= 16, K <= 32768: the small-batch MFMA kernel */
     PQ2_PATH_PREFILL = 3,   /* any M: the tiled MFMA GEMM */
-    PQ2_PATH_PANEL = 4      /* M <= 16, 2048 <= K <= 18432: the persistent
+    PQ2_PATH_PANEL = 4      /* M <= 64, 2048 <= K <= 18432: the persistent
                                small-batch MFMA kernel (activation panel in LDS) */
 };
 
@@ -111,16 +111,19 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
  *                    the LDS bound below);
  *                    else the GEMV for M <= 4 with N*K > 2^25; else the
  *                    16-token MFMA kernel (K <= 32768);
+ *   17 <= M <= 64 -> the same persistent kernel in 2 or 4 token tiles where
+ *                    the panel fits;
  *   otherwise     -> tiled int8 MFMA GEMM (prefill).
  * pq2_gemm_kernel_path reports the choice.
  * Group dots are exact int32; the float32 epilogue sums the G terms in an
  * order that differs from a sequential sum only by float32 rounding (a fixed
  * order: repeated calls give identical y).
  * Workspace: when the panel kernel splits K into chunks (K = 17408 and other
- * K above ~8000) the chunks' partial sums go to a device buffer of
- * chunks * M * N floats that the library allocates on first need, one per
- * device and stream, grows when a larger one is needed (hipFree of the old
- * one waits for the device) and keeps until the process ends. hipMalloc
+ * K above ~8000; at M > 16 most K) the chunks' partial sums go to a device
+ * buffer of chunks * M * N floats (at most 16 chunks) that the library
+ * allocates on first need, one per device and stream, grows when a larger
+ * one is needed (hipFree of the old one waits for the device) and keeps
+ * until the process ends. hipMalloc
  * makes such a first call unsafe under graph capture. A second small launch
  * sums the chunks in a fixed order. PQ2_ERR_HIP if it cannot allocate.
  */
@@ -172,9 +175,11 @@ pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t,
  *   d int32 [M][N][G],  d[m][n][g] = D[m][n][g] as defined above.
  * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M <= 4,
  * PQ2_PATH_SMALL requires M <= 16 and K <= 32768, PQ2_PATH_PANEL requires
- * M <= 16 and 2048 <= K <= 18432 and a device whose LDS per block holds the
- * activation panel and its tables (MI355X: M * (K + 16) + 320 * K / 128
- * + 16512 bytes <= 160 KiB) (else PQ2_ERR_ARG).
+ * M <= 64, 2048 <= K <= 18432 and a device whose LDS per block holds the
+ * activation panel of one K chunk and its tables. Chunks are whole multiples
+ * of 8 groups, at most 16 of them; an unsplit K (any G >= 16) needs, on
+ * MI355X (160 KiB), M * (K + 16) + 320 * K / 128 + 16512 bytes for M <= 16.
+ * Else PQ2_ERR_ARG.
  */
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t,
                                const uint8_t *codes, int32_t *d,

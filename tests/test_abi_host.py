@@ -106,7 +106,7 @@ def test_gemm_path_validation():
     assert f(P, P, P, P + 8, P, P, 1, 8, 128, 1, None) == ERR_ALIGN
     assert f(P, P, P, P, P, P, 5, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG
     assert f(P, P, P, P, P, P, 17, 8, 1024, pq2.PATH_SMALL, None) == ERR_ARG
-    assert f(P, P, P, P, P, P, 17, 8, 1024, pq2.PATH_PANEL, None) == ERR_ARG   # M <= 16
+    assert f(P, P, P, P, P, P, 65, 8, 2048, pq2.PATH_PANEL, None) == ERR_ARG   # M <= 64
     assert f(P, P, P, P, P, P, 8, 8, 1920, pq2.PATH_PANEL, None) == ERR_ARG    # K >= 2048
     assert f(P, P, P, P, P, P, 8, 8, 18560, pq2.PATH_PANEL, None) == ERR_ARG   # K <= 18432
     assert f(P, P, P, P, P, P, 1, 8, 128, 5, None) == ERR_ARG

@@ -152,15 +152,20 @@ PANEL_SHAPES = [(1, 40, 2048), (2, 7, 2048), (3, 300, 2176), (5, 4100, 2304), (8
                 (16, 8200, 2048), (8, 520, 8192), (11, 5000, 3200), (16, 4097, 6144),
                 (4, 1030, 17408), (5, 300, 18432), (3, 200, 17536), (16, 700, 17408),
                 (9, 5000, 16384), (16, 33, 18432),
-                (2, 300, 9344), (3, 100, 9344)]   # G = 73: the register-operand variant
+                (2, 300, 9344), (3, 100, 9344),   # G = 73: the register-operand variant
+                # 2 and 4 token tiles; K split so that the M-row panel fits LDS
+                (17, 300, 2048), (20, 1000, 5120), (24, 4100, 3200), (32, 700, 17408),
+                (33, 500, 2176), (40, 300, 6144), (48, 1030, 16384), (64, 4097, 5120),
+                (64, 129, 18432), (57, 33, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", PANEL_SHAPES)
 def test_group_dots_panel(pq2, M, N, K):
     """The persistent small-batch kernel: odd G (a half-empty last group pair),
     ragged K slices (pairs not a multiple of the wave count), several tiles per
-    block with a ragged last tile, N below one tile, and K split into chunks
-    (the panel of 16 x 17408 bytes does not fit one block's LDS)."""
+    block with a ragged last tile, N below one tile, K split into chunks (the
+    panel of 16 x 17408 bytes does not fit one block's LDS), and 17..64 tokens
+    in 2 or 4 token tiles with a partly padded last tile and chunks of 8 groups."""
     print(f"dots panel M={M} N={N} K={K}", flush=True)
     rng = np.random.default_rng(M * 1000 + N + K + 2)
     qn, t = rand_q(M, K, rng)
@@ -229,7 +234,8 @@ def test_gemm_y_within_tolerance(pq2, M, N, K):
 PATH_Y = [(1, 3, 300, 1024), (2, 5, 130, 1024), (4, 5, 4100, 2176), (4, 16, 8200, 2048),
           (4, 8, 300, 8192), (4, 16, 5000, 7168), (4, 5, 700, 17408), (4, 16, 1000, 17408),
           (4, 12, 5120, 18432), (4, 1, 33, 2048), (3, 16, 130, 640), (3, 40, 700, 5120),
-          (3, 200, 520, 2048)]
+          (3, 200, 520, 2048), (4, 17, 300, 2048), (4, 32, 1000, 5120), (4, 48, 700, 17408),
+          (4, 64, 4100, 6144)]
 
 
 @pytest.mark.parametrize("path,M,N,K", PATH_Y)
@@ -349,6 +355,8 @@ FULL = [
     ("small_m8_up", 8, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("small_m8_down", 8, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("small_m16_down", 16, 5120, 17408, synth.UNIFORM_CODES, 0.01),
+    ("tokens_m32_up", 32, 17408, 5120, synth.UNIFORM_CODES, 0.01),
+    ("tokens_m64_down", 64, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
     ("prefill_m4096_up", 4096, 17408, 5120, synth.PREFILL_CODES, 0.0),
 ]
@@ -375,6 +383,8 @@ def test_linear_full_size_sampled(pq2, M, N, K):
 @pytest.mark.parametrize("name,M,N,K,probs,outl", FULL, ids=[f[0] for f in FULL])
 def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
     print(f"full {name} M={M} N={N} K={K}", flush=True)
+    if name.startswith("tokens"):
+        assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PANEL   # 2 or 4 token tiles
     x = synth.activations(M, K, 0, outlier_frac=outl)
     w = synth.weights(N, K, synth.matrix_seed(0), probs)
     xd, cd, wd = dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))
@@ -402,7 +412,8 @@ def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
 @pytest.mark.parametrize("M,N,K,path", [(1, 5120, 6144, 1), (4, 5120, 6144, 1),
                                         (2, 2048, 17408, 1), (16, 5120, 6144, 2),
                                         (16, 2048, 17408, 2), (256, 1024, 5120, 3),
-                                        (16, 4100, 5120, 4), (9, 17408, 8192, 4)])
+                                        (16, 4100, 5120, 4), (9, 17408, 8192, 4),
+                                        (24, 5120, 5120, 4), (64, 4100, 5120, 4)])
 def test_full_row_dots(pq2, M, N, K, path):
     """Exact per-group dots over whole decode-size weight matrices."""
     print(f"full dots M={M} N={N} K={K} path={path}", flush=True)
