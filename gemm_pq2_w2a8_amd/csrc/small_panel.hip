@@ -45,6 +45,7 @@
 #include "pq2_launch.hpp"
 
 #include <map>
+#include <type_traits>
 #include <mutex>
 #include <utility>
 
@@ -574,6 +575,294 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
     }
 }
 
+// ---------------------------------------------------------------- ring variant
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Code tiles in LDS: one being computed, one in flight. MI355X sweeps over
+// the 5120 / 6144 / 17408 shapes: 2 slots beat 3, 4 and 5 by 5-15 % (more
+// copies in flight per CU made every tile land later), also when only tile 0
+// is issued ahead of the first compute and with non-temporal copies.
+constexpr int kRingSlots = 2;
+constexpr int kRingMaxGs = 6;                // groups per wave: A, seeds, scales and NG MFMA
+                                             // chains in at most 256 VGPRs
+constexpr int kRingOob = 0x7ffffff0;         // buffer offset past every range: no memory access
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// One 16-byte buffer -> LDS copy per lane: lane i writes bytes
+// [16 i, 16 i + 16) after lds (wave-uniform); offsets past the range write
+// zeros and read no memory. Counted by vmcnt like a load.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, 0, 0, 0);
+}
+
+// f(std::integral_constant<int, n>) for the run-time n in [1, NG].
+template <int NG, typename F>
+__device__ __forceinline__ void with_count(int n, F &&f) {
+    if constexpr (NG >= 1) {
+        if (n == NG) {
+            f(std::integral_constant<int, NG>{});
+            return;
+        }
+        with_count<NG - 1>(n, f);
+    }
+}
+
+// Block barrier after this wave's LDS accesses have completed. Without the
+// release fence of __syncthreads, which would also wait for every buffer ->
+// LDS copy in flight; the copies a tile needs are waited for explicitly.
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0); vmcnt and expcnt at their maxima
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// LDS bytes of the ring variant: R code slots of CPT * NW / 2 KB and R
+// weight-scale slots of 2 KB, a 1 KB sink for copies of idle waves, partials
+// [2][NW][4][64] floats.
+__host__ __device__ constexpr int64_t ring_lds_bytes(int cpt, int nw) {
+    return (int64_t)kRingSlots * (cpt * nw / 2 * 1024 + 2048) + 1024 + 2 * nw * 1024;
+}
+
+// Ring variant (M <= 16, chunks of a multiple of 8 groups): same arithmetic,
+// but the A side never moves again once loaded. Wave w owns groups
+// [g_lo, g_lo + ng) of the chunk for every tile, so its A fragments, -t seeds
+// and token scales for those groups live in VGPRs from the prologue on. Code
+// tiles stream through a ring of LDS slots by buffer -> LDS copies (16 bytes
+// per lane, no VGPRs held), kRingSlots - 1 tiles ahead of the one being
+// computed; each copy thread issues the same number of copies per tile (lanes
+// past the tile read past the buffer range, which moves no memory), so one
+// vmcnt wait per tile covers exactly the copies of that tile. Unit u (16 bytes) of a slot holds
+// row r = u / (2 Gc), column (u % (2 Gc)) ^ (r % 16) of the tile's chunk: every
+// 128-byte line is still fetched by one instruction, and the 16 rows of one
+// B read land in different LDS banks. The tile's [16][Gc] weight scales ride
+// in the same round, one copy per wave (waves past the block's 2 Gc scale units
+// copy into a sink). One barrier per tile: before it, each wave waits for its
+// own copies of the tile; after it, tile j - 1's slot is free for tile
+// j + kRingSlots - 1, and tile j - 1's partials (double-buffered) are summed
+// and stored.
+template <int NW, int GSG, int CPT, bool DOTS>
+__global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
+    int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M, int64_t N, int64_t K,
+    int gsplit, int bps) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr int T = NW * kWave;
+    constexpr int R = kRingSlots;
+    constexpr int TC = T / 2;                    // copy threads: waves NW/2 .. NW-1
+    constexpr int LPT = CPT + (DOTS ? 0 : 1);     // copies per copy thread and tile
+    constexpr int SLOT = CPT * TC * 16;          // code slot bytes
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int c = lane & 15;
+    const int lg = lane >> 4;
+    const int sh0 = 2 * (lg >> 1);
+    const int G = (int)(K / kGroup);
+    const int KB = (int)(K / 4);
+    const int Mr = M < 16 ? (int)M : 16;
+    const int64_t NT = (N + 15) / 16;
+    const int bid = blockIdx.x;
+    const int sidx = bid / bps;
+    const int bl = bid - sidx * bps;
+    const int g0 = sidx * gsplit;
+    const int Gc = G - g0 < gsplit ? G - g0 : gsplit;
+    const int cnt = (int)((NT - bl + bps - 1) / bps);
+
+    uint8_t *ring = smem;                                               // [R][SLOT]
+    uint8_t *wsr = smem + R * SLOT;                                     // [R][2048]
+    uint8_t *sink = wsr + R * 2048;                                     // 1 KB
+    float *part = reinterpret_cast<float *>(sink + 1024);               // [2][NW][4][64]
+
+    // this wave's groups of the chunk: [g_lo, g_lo + ng), 1 <= ng <= GSG
+    const int g_lo = (Gc * wave) / NW;
+    const int ng = (Gc * (wave + 1)) / NW - g_lo;
+
+    // Roles: the upper half of the waves issues every copy, the lower half
+    // sums and stores the outputs, so a copy wave's vmcnt counts copies only
+    // (no store between them) and its waits are exact; the summing waves
+    // never wait on the copies, the barrier orders them.
+    const bool copier = wave >= NW / 2;
+    const int tc = tid - TC;                     // copy thread index
+    const int cw = wave - NW / 2;                // copy wave index
+    // copy sources: code unit u = i TC + tc of a slot, weight-scale unit tc
+    const int ncu = 32 * Gc;
+    const int rc2 = 2 * Gc;
+    int coff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int u = i * TC + tc;
+        const int r = u / rc2;
+        const int col = (u - r * rc2) ^ (r & 15);
+        coff[i] = copier && u < ncu ? r * KB + 32 * g0 + 16 * col : kRingOob;
+    }
+    int woff = kRingOob;
+    if (!DOTS && copier && tc < 2 * Gc) {
+        const int cpr8 = Gc / 8;
+        const int r = tc / cpr8;
+        woff = 2 * (r * G + g0 + 8 * (tc - r * cpr8));
+    }
+    const bool ws_wave = kWave * cw < 2 * Gc;
+
+    // tile j's copies into slot j % R; past the block's last tile every copy
+    // reads past the range (zeros into the slot, no memory traffic)
+    auto issue = [&](int j) __attribute__((always_inline)) {
+        const bool live = j < cnt;
+        const int64_t n0 = (int64_t)(bl + (int64_t)(live ? j : 0) * bps) * 16;
+        const int64_t rows = N - n0 < 16 ? N - n0 : 16;
+        const int slot = j % R;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + n0 * KB, rows * KB);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i)
+            copy16_to_lds(rc, ring + slot * SLOT + (i * TC + kWave * cw) * 16,
+                          live ? coff[i] : kRingOob);
+        if (!DOTS) {
+            const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + n0 * G, rows * G * 2);
+            uint8_t *dst = ws_wave ? wsr + slot * 2048 + 1024 * cw : sink;
+            copy16_to_lds(rw, dst, live ? woff : kRingOob);
+        }
+    };
+
+    // prologue: the A fragments, -t seeds and token scales of this wave's
+    // groups straight into VGPRs (tokens past M read past the buffer ranges:
+    // zero seeds and scales, A repeats the last row; their outputs are never
+    // stored), then the first R - 1 tiles' copies behind them.
+    const int arow = c < Mr ? c : Mr - 1;
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4i a0[GSG], a1[GSG], seed[GSG];
+    v4f sv[GSG];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)Mr * K);
+        const __amdgpu_buffer_rsrc_t rt = make_rsrc(t, (int64_t)Mr * G * 4);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, DOTS ? 0 : (int64_t)Mr * G * 4);
+#pragma unroll
+        for (int b = 0; b < GSG; ++b) {
+            const int g = g0 + g_lo + (b < ng ? b : ng - 1);
+            const int off = arow * (int)K + kGroup * g + 16 * lg;
+            a0[b] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+            a1[b] = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * lg + i;
+                const int toff = m < Mr ? 4 * (m * G + g) : kRingOob;
+                seed[b][i] = -__builtin_amdgcn_raw_buffer_load_b32(rt, toff, 0, 0);
+                if (!DOTS)
+                    sv[b][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, toff, 0, 0));
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the copies behind these loads
+    if (copier) {
+#pragma unroll
+        for (int p = 0; p < R - 1; ++p) issue(p);
+    }
+    // Hand the fragments to the loop as plain register values: the compiler
+    // waits for their loads here (only the copies behind them may stay in
+    // flight) instead of draining every copy before the loop.
+#pragma unroll
+    for (int b = 0; b < GSG; ++b) {
+        asm volatile("" : "+v"(a0[b]), "+v"(a1[b]), "+v"(seed[b]));
+        if (!DOTS) asm volatile("" : "+v"(sv[b]));
+    }
+
+    // the tile's groups in straight-line code for the wave's exact count NG:
+    // every B read and weight scale first, then NG independent MFMA chains,
+    // then the epilogues (no per-group branch or LDS round trip in between)
+    auto compute_tile = [&](int j, auto ngc) __attribute__((always_inline)) {
+        constexpr int NG = decltype(ngc)::value;
+        const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
+        const uint8_t *cs = ring + (j % R) * SLOT + c * rc2 * 16;
+        const uint16_t *wrow = reinterpret_cast<const uint16_t *>(wsr + (j % R) * 2048) + c * Gc;
+        v4i w[NG];
+#pragma unroll
+        for (int b = 0; b < NG; ++b)
+            w[b] = *reinterpret_cast<const v4i *>(cs + 16 * ((2 * (g_lo + b) + (lg & 1)) ^ c));
+        float wsf[NG];
+        if (!DOTS) {
+#pragma unroll
+            for (int b = 0; b < NG; ++b) wsf[b] = half_bits_to_float(wrow[g_lo + b]);
+        }
+        v4i dd[NG];
+#pragma unroll
+        for (int b = 0; b < NG; ++b) {
+            v4i b0, b1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t sh = (uint32_t)w[b][k] >> sh0;
+                b0[k] = (int)(sh & kPlaneMask);
+                b1[k] = (int)((sh >> 4) & kPlaneMask);
+            }
+            dd[b] = mfma16x16x64(a0[b], b0, seed[b]);
+            dd[b] = mfma16x16x64(a1[b], b1, dd[b]);
+        }
+        if (DOTS) {
+            const int64_t n = n0 + c;
+#pragma unroll
+            for (int b = 0; b < NG; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = 4 * lg + i;
+                    if (m < M && n < N) d[((int64_t)m * N + n) * G + g0 + g_lo + b] = dd[b][i];
+                }
+        } else {
+            float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+#pragma unroll
+            for (int b = 0; b < NG; ++b) {
+                acc0 = fmaf((float)dd[b][0], sv[b][0] * wsf[b], acc0);
+                acc1 = fmaf((float)dd[b][1], sv[b][1] * wsf[b], acc1);
+                acc2 = fmaf((float)dd[b][2], sv[b][2] * wsf[b], acc2);
+                acc3 = fmaf((float)dd[b][3], sv[b][3] * wsf[b], acc3);
+            }
+            float *pw = part + ((j & 1) * NW + wave) * 4 * kWave + lane;
+            pw[0] = acc0;
+            pw[kWave] = acc1;
+            pw[2 * kWave] = acc2;
+            pw[3 * kWave] = acc3;
+        }
+    };
+
+    float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
+    // summing wave i (< 4) adds slot i of every lane's partials (token
+    // 4 (lane / 16) + i, row lane % 16) in wave order
+    auto reduce_tile = [&](int j) __attribute__((always_inline)) {
+        if (!DOTS) {
+            const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
+            const float *pr = part + (j & 1) * NW * 4 * kWave + wave * kWave + lane;
+            float v = pr[0];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += pr[w * 4 * kWave];
+            const int64_t m = 4 * lg + wave, n = n0 + c;
+            if (m < M && n < N) out[m * N + n] = v;
+        }
+    };
+
+    static_assert(NW == 8, "four summing waves, one per partial slot");
+    if (copier) {
+        for (int j = 0; j < cnt; ++j) {
+            wait_vmem<(R - 2) * LPT>();  // this thread's copies of tile j have landed
+            ring_barrier();              // ... and every copier's; tile j - 1 is done
+            issue(j + R - 1);            // into tile j - 1's slot
+            with_count<GSG>(ng, [&](auto ngc) { compute_tile(j, ngc); });
+        }
+        wait_vmem<0>();                  // no copy may land after the block ends
+        ring_barrier();
+    } else {
+        for (int j = 0; j < cnt; ++j) {
+            ring_barrier();
+            if (j > 0) reduce_tile(j - 1);
+            with_count<GSG>(ng, [&](auto ngc) { compute_tile(j, ngc); });
+        }
+        ring_barrier();
+        reduce_tile(cnt - 1);
+    }
+}
+
 // y = sum over the S chunks of part[s] (fixed order s = 0, 1, ...).
 __global__ __launch_bounds__(256) void panel_split_sum_kernel(const float *__restrict__ part,
                                                               float *__restrict__ y, int64_t MN,
@@ -695,6 +984,40 @@ hipError_t launch_sc(int64_t gs, const int8_t *q, const int32_t *t, const uint8_
 #undef PQ2_PANEL_SC
 }
 
+template <int NW, int GSG, bool DOTS>
+hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                           const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
+                           int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
+    constexpr int CPT = GSG;     // 32 * 8 GSG code units over the 256 copy threads, NW = 8
+    hipLaunchKernelGGL((small_panel_ring_kernel<NW, GSG, CPT, DOTS>), dim3((unsigned)blocks),
+                       dim3(NW * kWave), lds, stream, q, DOTS ? nullptr : out.s, t, codes,
+                       DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y, out.d, part, M, N, K,
+                       gsplit, bps);
+    return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_ring(int64_t gs, const int8_t *q, const int32_t *t, const uint8_t *codes,
+                       const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
+                       int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
+#define PQ2_PANEL_RING(V)                                                                    \
+    case V:                                                                                  \
+        return out.d ? launch_ring_cfg<NW, V, true>(q, t, codes, out, part, M, N, K, gsplit, \
+                                                     bps, blocks, lds, stream)               \
+                     : launch_ring_cfg<NW, V, false>(q, t, codes, out, part, M, N, K,        \
+                                                      gsplit, bps, blocks, lds, stream);
+    switch (gs) {
+        PQ2_PANEL_RING(1)
+        PQ2_PANEL_RING(2)
+        PQ2_PANEL_RING(3)
+        PQ2_PANEL_RING(4)
+        PQ2_PANEL_RING(5)
+        PQ2_PANEL_RING(6)
+        default: return hipErrorInvalidValue;
+    }
+#undef PQ2_PANEL_RING
+}
+
 constexpr int kPanelWaves = 8;
 constexpr int kPanelMaxSplits = 16;
 constexpr int kPanelMaxGs = 9;
@@ -774,6 +1097,44 @@ PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int fo
     return none;
 }
 
+// Ring variant: M <= 16, chunks of a multiple of 8 groups (the column swizzle
+// permutes within 16-unit blocks of a row), at most 8 groups per wave, LDS
+// within the block limit; same split rule as the other variants.
+PanelPlan plan_ring_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l) {
+    PanelPlan p;
+    const int64_t G = K / kGroup, NT = (N + 15) / 16;
+    if (M > 16 || G % 8 != 0) return p;
+    const int64_t gsplit = ((G + S - 1) / S + 7) / 8 * 8;
+    if ((G + gsplit - 1) / gsplit != S) return p;
+    const int64_t gs = gsplit / kPanelWaves;
+    if (gs < 1 || gs > kRingMaxGs) return p;
+    const int64_t lds = ring_lds_bytes((int)gs, kPanelWaves);
+    if (lds > l.lds_block) return p;
+    int64_t bps = l.cus / S;
+    if (bps > NT) bps = NT;
+    if (bps < 1) return p;
+    p.S = S;
+    p.gsplit = (int)gsplit;
+    p.bps = (int)bps;
+    p.lds = lds;
+    p.gs = gs;
+    return p;
+}
+
+PanelPlan plan_ring(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s) {
+    PanelPlan none;
+    if (l.cus <= 0 || M < 1 || M > 16) return none;
+    if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_ring_for(force_s, M, N, K, l) : none;
+    const int64_t G = K / kGroup;
+    int target = (int)((G + 24) / 48);
+    target = target < 1 ? 1 : target > kPanelMaxSplits ? kPanelMaxSplits : target;
+    for (int S = target; S <= kPanelMaxSplits; ++S) {
+        const PanelPlan p = plan_ring_for(S, M, N, K, l);
+        if (p.S) return p;
+    }
+    return none;
+}
+
 }  // namespace
 
 // Device workspace for split partials, one per (device, stream): work on one
@@ -827,10 +1188,13 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
     // 6144 / 17408 shapes at M = 4, 8, 16, slower on one; one tile of
     // register prefetch beat two on all nine)
     int staged = 1;
+    int ring = 1;
     PANEL_TUNE_OVERRIDE
-    PanelPlan plan = plan_panel(M, N, K, dev_limits(), force_s, staged != 0);
-    const bool sc = staged != 0 && plan.S != 0;
-    if (!sc) plan = plan_panel(M, N, K, dev_limits(), force_s, false);
+    PanelPlan plan = ring ? plan_ring(M, N, K, dev_limits(), force_s) : PanelPlan();
+    const bool rg = plan.S != 0;
+    if (!rg) plan = plan_panel(M, N, K, dev_limits(), force_s, staged != 0);
+    const bool sc = !rg && staged != 0 && plan.S != 0;
+    if (!rg && !sc) plan = plan_panel(M, N, K, dev_limits(), force_s, false);
     if (plan.S == 0) return hipErrorInvalidValue;
     float *part = nullptr;
     if (plan.S > 1 && !out.d) {
@@ -839,7 +1203,10 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
     }
     const int64_t blocks = (int64_t)plan.bps * plan.S;
     hipError_t e;
-    if (sc && plan.tt == 1)
+    if (rg)
+        e = launch_ring<kPanelWaves>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
+                                     plan.bps, blocks, plan.lds, stream);
+    else if (sc && plan.tt == 1)
         e = launch_sc<kPanelWaves, 1>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
                                       plan.bps, blocks, plan.lds, stream);
     else if (sc && plan.tt == 2)
