@@ -38,10 +38,13 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
 
 // Kernel choice of pq2_gemm (from MI355X measurements on the decode and
 // small-batch shapes): the dot4 GEMV reads only the real token rows and wins
-// for M <= 2 everywhere. For 3 <= M <= 16 the persistent panel kernel wins
-// on large matrices (N*K > 2^25) and, from M = 8, on every size it can hold
-// (K from 2048 to 18432, within LDS); otherwise the dot4 GEMV for M = 3..4 on large
-// matrices with K too large for the panel, else the 16-token MFMA kernel. For
+// for M <= 2 everywhere. For 3 <= M <= 16 the panel kernel's ring variant
+// (K chunks of whole multiples of 8 groups) beats the GEMV and the 16-token
+// kernel on every shape measured (5120 x 6144 at M = 3: 7.0 us against 8.4);
+// where only its other variants run it wins on large matrices (N*K > 2^25)
+// and, from M = 8, on every size it can hold (K from 2048 to 18432, within
+// LDS); otherwise the dot4 GEMV for M = 3..4 on large matrices with K too
+// large for the panel, else the 16-token MFMA kernel. For
 // 17 <= M <= 64 the panel kernel in 2 or 4 token tiles takes 0.3-0.77 of the
 // tiled GEMM's time on the 5120 / 6144 / 17408 shapes, wherever it has a plan.
 #ifndef PQ2_AUTO_OVERRIDE
@@ -50,6 +53,7 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
 int auto_path(int64_t M, int64_t N, int64_t K) {
     PQ2_AUTO_OVERRIDE
     if (M <= 2) return PQ2_PATH_GEMV;
+    if (M <= 16 && pq2::small_panel_ring_fits(M, K)) return PQ2_PATH_PANEL;
     const bool large = N * K > (int64_t(1) << 25);
     if (M <= 16 && (large || M >= 8) && pq2::small_panel_fits(M, K)) return PQ2_PATH_PANEL;
     if (M <= pq2::kGemvMaxM && large) return PQ2_PATH_GEMV;

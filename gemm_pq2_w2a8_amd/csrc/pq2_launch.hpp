@@ -44,6 +44,10 @@ constexpr int64_t kPanelMaxK = 18432;
 constexpr int64_t kPanelMaxM = 64;
 
 bool small_panel_fits(int64_t M, int64_t K);
+// Whether the panel kernel runs its ring variant (A fragments resident in
+// VGPRs, codes through an LDS ring): M <= 16 and K chunks of whole multiples
+// of 8 groups within the LDS bound.
+bool small_panel_ring_fits(int64_t M, int64_t K);
 
 hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *codes,
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,

@@ -1169,6 +1169,11 @@ hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
     return hipGetLastError();
 }
 
+bool small_panel_ring_fits(int64_t M, int64_t K) {
+    if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
+    return plan_ring(M, 16, K, dev_limits(), 0).S > 0;
+}
+
 bool small_panel_fits(int64_t M, int64_t K) {
     if (M < 1 || M > kPanelMaxM || K > kPanelMaxK || K / kGroup < 16) return false;
     // M <= 16: the register-operand kernel's plan (the fallback) must exist

@@ -105,12 +105,14 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
  *   M <= 2        -> GEMV streaming code words into v_dot4 (2-bit planes
  *                    masked out of each 32-bit word, no decode step; each
  *                    word serves every token row);
- *   3 <= M <= 16  -> persistent small-batch kernel on int8 MFMA with the
- *                    activation panel in LDS (PQ2_PATH_PANEL) when N*K > 2^25
- *                    or M >= 8 and the panel fits (2048 <= K <= 18432 and
- *                    the LDS bound below);
- *                    else the GEMV for M <= 4 with N*K > 2^25; else the
- *                    16-token MFMA kernel (K <= 32768);
+ *   3 <= M <= 16  -> persistent small-batch kernel on int8 MFMA
+ *                    (PQ2_PATH_PANEL) whenever 2048 <= K <= 18432 and G is
+ *                    a multiple of 8 (its activation fragments stay in
+ *                    registers, code tiles stream through LDS); for other G
+ *                    runs it when N*K > 2^25 or M >= 8 and the activation panel
+ *                    fits LDS (the bound below); else the GEMV for M <= 4
+ *                    with N*K > 2^25; else the 16-token MFMA kernel
+ *                    (K <= 32768);
  *   17 <= M <= 64 -> the same persistent kernel in 2 or 4 token tiles where
  *                    the panel fits;
  *   otherwise     -> tiled int8 MFMA GEMM (prefill).
