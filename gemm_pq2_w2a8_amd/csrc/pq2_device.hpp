@@ -206,4 +206,34 @@ __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// ---- buffer -> LDS copies (gfx950: 16 bytes per lane) and their waits
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kCopyOob = 0x7ffffff0;         // buffer offset past every range: no memory access
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// One 16-byte buffer -> LDS copy per lane: lane i writes bytes
+// [16 i, 16 i + 16) after lds (wave-uniform); offsets past the range write
+// zeros and read no memory. Counted by vmcnt like a load. (A non-template
+// function: the builtin is device-only, and a template kernel calling it
+// directly gets no host-side launch stub.)
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, 0, 0, 0);
+}
+
+// Block barrier after this wave's LDS accesses have completed. Without the
+// release fence of __syncthreads, which would also wait for every buffer ->
+// LDS copy in flight; the copies a step needs are waited for explicitly.
+__device__ __forceinline__ void ring_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0); vmcnt and expcnt at their maxima
+    asm volatile("s_barrier" ::: "memory");
+}
+
 }  // namespace pq2

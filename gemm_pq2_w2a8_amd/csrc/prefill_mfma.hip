@@ -403,6 +403,287 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
     }
 }
 
+// ---------------------------------------------------------------- ring variant
+//
+// Same tiles, operand mapping and arithmetic, but the per-group operands reach
+// LDS by 16-byte buffer -> LDS copies (no VGPRs held), so R - 1 groups are in
+// flight while one is computed. Every thread issues the same copies per
+// group (lanes past a region read past the buffer range, which moves no
+// memory), so one explicit vmcnt wait per group covers that group's copies.
+// Stage layout (16-byte units; copy instruction i of wave w writes units
+// 256 i + 64 w + lane): code unit 2 row + (half ^ ((row >> 2) & 1)), then q
+// unit 8 token + (piece ^ (token & 7)) -- every 128-byte line is fetched by
+// one instruction, and the 16-lane operand reads hit distinct LDS banks.
+// Scales of groups 8c .. 8c + 7 travel as one chunk: ws unit row (8 halves),
+// s and t units 2 token + h (4 floats each), issued at group 8c - 8 into the
+// other of two chunk slots.
+template <int BN, int BM, int T, bool DOTS>
+struct PfRing {
+    static constexpr int kCodeInst = (2 * BN + T - 1) / T;         // copies per thread, codes
+    static constexpr int kQInst = (8 * BM + T - 1) / T;            // copies per thread, q
+    static constexpr int kStageInst = kCodeInst + kQInst;
+    static constexpr int kQBase = kCodeInst * T;                   // first q unit
+    static constexpr int kStageBytes = kStageInst * T * 16;
+    static constexpr int kWsInst = DOTS ? 0 : (BN + T - 1) / T;
+    static constexpr int kTokInst = (2 * BM + T - 1) / T;          // per s or t table
+    static constexpr int kScaleInst = kWsInst + (DOTS ? 1 : 2) * kTokInst;
+    static constexpr int kSBase = kWsInst * T;                     // first s unit
+    static constexpr int kTBase = kSBase + (DOTS ? 0 : kTokInst * T);
+    static constexpr int kScaleBytes = kScaleInst * T * 16;
+};
+
+template <int WN, int WM, int WAVES_N, int WAVES_M, int R, bool DOTS>
+__global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
+    const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
+    int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
+    using C = PfCfg<WN, WM, WAVES_N, WAVES_M>;
+    constexpr int T = C::kThreads;
+    using L = PfRing<C::BN, C::BM, T, DOTS>;
+    static_assert(R >= 2 && R <= 8, "the scale chunk of group 8c + 8 must land before it");
+    constexpr int CPS = L::kStageInst;
+    constexpr int SI = L::kScaleInst;
+    static_assert((R - 2) * CPS + SI < 64, "vmcnt holds 6 bits");
+    // dynamic LDS: [R] stages, then [2] scale chunks (with static arrays the
+    // compiler sees the copies' target and drains every copy before each read)
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *const ring0 = smem;
+    uint8_t *const scl0 = smem + R * L::kStageBytes;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wn = wave % WAVES_N, wm = wave / WAVES_N;
+    const int r = lane & 15, lg = lane >> 4;
+    const int half = lg & 1;
+    const int sh0 = 2 * (lg >> 1);
+    const int G = (int)(K / kGroup);
+    const int KB = (int)(K / 4);
+
+    const int64_t tiles_n = (N + C::BN - 1) / C::BN;
+    const int64_t tiles_m = (M + C::BM - 1) / C::BM;
+    const int64_t tile = xcd_tile(blockIdx.x, tiles_n * tiles_m);
+    const int64_t n0 = (tile % tiles_n) * C::BN;
+    const int64_t m0 = (tile / tiles_n) * C::BM;
+    const int rows = N - n0 < C::BN ? (int)(N - n0) : C::BN;
+    const int toks = M - m0 < C::BM ? (int)(M - m0) : C::BM;
+
+    const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(codes + n0 * KB, (int64_t)rows * KB);
+    const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + m0 * K, (int64_t)toks * K);
+    const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(t + m0 * G, (int64_t)toks * G * 4);
+    const __amdgpu_buffer_rsrc_t rs_ws = make_rsrc(DOTS ? nullptr : ws + n0 * G, DOTS ? 0 : (int64_t)rows * G * 2);
+    const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(DOTS ? nullptr : s + m0 * G, DOTS ? 0 : (int64_t)toks * G * 4);
+
+    // per-thread copy sources (group 0; group g adds 32 g or 128 g); rows and
+    // tokens past the end read past the range (zeros, never stored)
+    int coff[L::kCodeInst], qoff[L::kQInst];
+#pragma unroll
+    for (int i = 0; i < L::kCodeInst; ++i) {
+        const int u = i * T + tid;
+        const int row = u >> 1;
+        const int h = (u & 1) ^ ((row >> 2) & 1);
+        coff[i] = u < 2 * C::BN && row < rows ? row * KB + 16 * h : kCopyOob;
+    }
+#pragma unroll
+    for (int i = 0; i < L::kQInst; ++i) {
+        const int u = i * T + tid;
+        const int tok = u >> 3;
+        const int piece = (u & 7) ^ (tok & 7);
+        qoff[i] = u < 8 * C::BM && tok < toks ? tok * (int)K + 16 * piece : kCopyOob;
+    }
+    // scale chunk sources (chunk 0; chunk c adds 16 c bytes for ws, 32 c for s / t)
+    int wsoff[L::kWsInst > 0 ? L::kWsInst : 1], toff[L::kTokInst];
+#pragma unroll
+    for (int i = 0; i < L::kWsInst; ++i) {
+        const int u = i * T + tid;
+        wsoff[i] = u < C::BN && u < rows ? 2 * u * G : kCopyOob;
+    }
+#pragma unroll
+    for (int i = 0; i < L::kTokInst; ++i) {
+        const int u = i * T + tid;
+        const int tok = u >> 1;
+        toff[i] = u < 2 * C::BM && tok < toks ? 4 * (tok * G + 4 * (u & 1)) : kCopyOob;
+    }
+
+    auto issue_stage = [&](int g) __attribute__((always_inline)) {
+        const bool live = g < G;
+        uint8_t *st = ring0 + (g % R) * L::kStageBytes;
+#pragma unroll
+        for (int i = 0; i < L::kCodeInst; ++i)
+            copy16_to_lds(rs_codes, st + (i * T + kWave * wave) * 16,
+                          live && coff[i] != kCopyOob ? coff[i] + 32 * g : kCopyOob);
+#pragma unroll
+        for (int i = 0; i < L::kQInst; ++i)
+            copy16_to_lds(rs_q, st + (L::kQBase + i * T + kWave * wave) * 16,
+                          live && qoff[i] != kCopyOob ? qoff[i] + kGroup * g : kCopyOob);
+    };
+    auto issue_scales = [&](int c) __attribute__((always_inline)) {
+        const bool live = 8 * c < G;
+        uint8_t *sc = scl0 + (c & 1) * L::kScaleBytes;
+#pragma unroll
+        for (int i = 0; i < L::kWsInst; ++i)
+            copy16_to_lds(rs_ws, sc + (i * T + kWave * wave) * 16,
+                          live && wsoff[i] != kCopyOob ? wsoff[i] + 16 * c : kCopyOob);
+        if (!DOTS) {
+#pragma unroll
+            for (int i = 0; i < L::kTokInst; ++i)
+                copy16_to_lds(rs_s, sc + (L::kSBase + i * T + kWave * wave) * 16,
+                              live && toff[i] != kCopyOob ? toff[i] + 32 * c : kCopyOob);
+        }
+#pragma unroll
+        for (int i = 0; i < L::kTokInst; ++i)
+            copy16_to_lds(rs_t, sc + (L::kTBase + i * T + kWave * wave) * 16,
+                          live && toff[i] != kCopyOob ? toff[i] + 32 * c : kCopyOob);
+    };
+
+    const int row_base = 16 * WN * wn;
+    const int tok_base = 16 * WM * wm;
+    float acc[WN][WM][4];
+#pragma unroll
+    for (int a = 0; a < WN; ++a)
+#pragma unroll
+        for (int b = 0; b < WM; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
+
+    // a group's operands, read from its stage and scale chunk into VGPRs
+    struct Ops {
+        v4i w[WN], b0[WM], b1[WM];
+        int tt[WM];
+        float sv[WM];
+        uint16_t wsh[WN][4];
+    };
+    auto load_ops = [&](int g, Ops &o) __attribute__((always_inline)) {
+        const uint8_t *st = ring0 + (g % R) * L::kStageBytes;
+        const uint8_t *sc = scl0 + ((g >> 3) & 1) * L::kScaleBytes;
+        const int j = g & 7;
+        const uint16_t *wsl = reinterpret_cast<const uint16_t *>(sc) + j;
+        const float *sl = reinterpret_cast<const float *>(sc + L::kSBase * 16) + j;
+        const int32_t *tl = reinterpret_cast<const int32_t *>(sc + L::kTBase * 16) + j;
+#pragma unroll
+        for (int a = 0; a < WN; ++a) {
+            const int row = row_base + 16 * a + r;
+            o.w[a] = *reinterpret_cast<const v4i *>(st + 16 * (2 * row + (half ^ ((row >> 2) & 1))));
+            if (!DOTS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o.wsh[a][i] = wsl[8 * (row_base + 16 * a + 4 * lg + i)];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < WM; ++b) {
+            const int tok = tok_base + 16 * b + r;
+            const uint8_t *qrow = st + (L::kQBase + 8 * tok) * 16;
+            o.b0[b] = *reinterpret_cast<const v4i *>(qrow + 16 * (lg ^ (tok & 7)));
+            o.b1[b] = *reinterpret_cast<const v4i *>(qrow + 16 * ((lg + 4) ^ (tok & 7)));
+            o.tt[b] = tl[8 * tok];
+            o.sv[b] = DOTS ? 0.0f : sl[8 * tok];
+        }
+    };
+    // plane decode, then per token tile the 2 WN MFMAs and their epilogue (the
+    // compiler overlaps one tile's epilogue with the next tile's MFMAs; issuing
+    // every MFMA of the group before any epilogue measured 1.5-1.9x slower)
+    auto mma = [&](const Ops &o, int g) __attribute__((always_inline)) {
+        v4i a0[WN], a1[WN];
+        float wsf[WN][4];
+#pragma unroll
+        for (int a = 0; a < WN; ++a) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t sh = (uint32_t)o.w[a][k] >> sh0;
+                a0[a][k] = (int)(sh & kPlaneMask);
+                a1[a][k] = (int)((sh >> 4) & kPlaneMask);
+            }
+            if (!DOTS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wsf[a][i] = half_bits_to_float(o.wsh[a][i]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < WM; ++b) {
+            const v4i seed = {-o.tt[b], -o.tt[b], -o.tt[b], -o.tt[b]};
+            v4i c[WN];
+#pragma unroll
+            for (int a = 0; a < WN; ++a) c[a] = mfma16x16x64(a0[a], o.b0[b], seed);
+#pragma unroll
+            for (int a = 0; a < WN; ++a) c[a] = mfma16x16x64(a1[a], o.b1[b], c[a]);
+#pragma unroll
+            for (int a = 0; a < WN; ++a) {
+                if (DOTS) {
+                    const int64_t m = m0 + tok_base + 16 * b + r;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t n = n0 + row_base + 16 * a + 4 * lg + i;
+                        if (m < M && n < N) d[(m * N + n) * G + g] = c[a][i];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[a][b][i] = fmaf((float)c[a][i], o.sv[b] * wsf[a][i], acc[a][b][i]);
+                }
+            }
+        }
+    };
+
+    // prologue: scale chunk 0, then the first R - 1 stages
+    issue_scales(0);
+#pragma unroll
+    for (int p = 0; p < R - 1; ++p) issue_stage(p);
+    for (int g = 0; g < G; ++g) {
+        // copies younger than stage g: stages g + 1 .. g + R - 2, and the
+        // scale chunk issued at the last group 8c in [g - R + 1, g - 1]
+        const bool scale_after = g >= 1 && ((g - 1) & ~7) >= g - R + 1;
+        if (scale_after)
+            wait_vmem<(R - 2) * CPS + SI>();
+        else
+            wait_vmem<(R - 2) * CPS>();
+        ring_barrier();                          // stage g in LDS; stage g - 1 free
+        issue_stage(g + R - 1);
+        if ((g & 7) == 0) issue_scales((g >> 3) + 1);
+        Ops o;
+        load_ops(g, o);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(o, g);
+    }
+    wait_vmem<0>();                              // no copy may land after the block ends
+
+    if (!DOTS) {
+#pragma unroll
+        for (int b = 0; b < WM; ++b) {
+            const int64_t m = m0 + tok_base + 16 * b + r;
+#pragma unroll
+            for (int a = 0; a < WN; ++a) {
+                const int64_t nb = n0 + row_base + 16 * a + 4 * lg;
+                if (m < M) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (nb + i < N) y[m * N + nb + i] = acc[a][b][i];
+                }
+            }
+        }
+    }
+}
+
+template <int WN, int WM, int WAVES_N, int WAVES_M, int R>
+hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream) {
+    using C = PfCfg<WN, WM, WAVES_N, WAVES_M>;
+    const int64_t blocks = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+    if (out.d) {
+        using L = PfRing<C::BN, C::BM, C::kThreads, true>;
+        const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes;
+        hipLaunchKernelGGL((prefill_ring_kernel<WN, WM, WAVES_N, WAVES_M, R, true>),
+                           dim3((unsigned)blocks), dim3(C::kThreads), lds, stream, q, nullptr, t,
+                           codes, nullptr, nullptr, out.d, M, N, K);
+    } else {
+        using L = PfRing<C::BN, C::BM, C::kThreads, false>;
+        const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes;
+        hipLaunchKernelGGL((prefill_ring_kernel<WN, WM, WAVES_N, WAVES_M, R, false>),
+                           dim3((unsigned)blocks), dim3(C::kThreads), lds, stream, q, out.s, t,
+                           codes, out.ws, out.y, nullptr, M, N, K);
+    }
+    return hipGetLastError();
+}
+
 template <int WN, int WM, int WAVES_N, int WAVES_M, int DEPTH>
 hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
                       const GemmOut &out, int64_t M, int64_t N, int64_t K,
@@ -430,20 +711,29 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 //   3:  64 x 128, 2 x 2 waves of 32 x 64, depth 2
 //   4:  32 x 128, 2 x 2 waves of 16 x 64, depth 2
 //   5: 128 x 64,  2 x 2 waves of 64 x 32, depth 2
+//   6: 128 x 128, 2 x 2 waves of 64 x 64, ring of 2 stages (buffer -> LDS copies)
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
     // Largest tile that still gives every CU at least one block.
     auto tiles = [&](int64_t bn, int64_t bm) { return ((N + bn - 1) / bn) * ((M + bm - 1) / bm); };
     constexpr int64_t kCUs = 256;
-    int cfg = tiles(128, 128) >= kCUs ? 0 : tiles(64, 128) >= kCUs ? 3 : 4;
+    // The ring variant of the 128 x 128 tile (configuration 6) needs whole
+    // chunks of 8 groups of scales and 32-bit offsets below its sentinel;
+    // MI355X: 3-6 % faster than configuration 0 at M = 512 / 4096 on the
+    // 5120 / 17408 shapes. Deeper rings, smaller ring tiles and 8-wave tiles
+    // were slower (M = 128 to 4096).
+    const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
+    int cfg = tiles(128, 128) >= kCUs ? (ring ? 6 : 0) : tiles(64, 128) >= kCUs ? 3 : 4;
     PREFILL_TUNE_OVERRIDE
+    if (cfg == 6 && !ring) cfg = 0;
     switch (cfg) {
         case 1: return launch_cfg<2, 8, 4, 1, 1>(q, t, codes, out, M, N, K, stream);
         case 2: return launch_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 3: return launch_cfg<2, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 4: return launch_cfg<1, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 5: return launch_cfg<4, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 6: return launch_ring_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         default: return launch_cfg<4, 4, 2, 2, 1>(q, t, codes, out, M, N, K, stream);
     }
 }

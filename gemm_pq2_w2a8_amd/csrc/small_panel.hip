@@ -577,8 +577,6 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
 
 // ---------------------------------------------------------------- ring variant
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // Code tiles in LDS: one being computed, one in flight. MI355X sweeps over
 // the 5120 / 6144 / 17408 shapes: 2 slots beat 3, 4 and 5 by 5-15 % (more
 // copies in flight per CU made every tile land later), also when only tile 0
@@ -586,22 +584,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kRingSlots = 2;
 constexpr int kRingMaxGs = 6;                // groups per wave: A, seeds, scales and NG MFMA
                                              // chains in at most 256 VGPRs
-constexpr int kRingOob = 0x7ffffff0;         // buffer offset past every range: no memory access
-
-// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
-// One 16-byte buffer -> LDS copy per lane: lane i writes bytes
-// [16 i, 16 i + 16) after lds (wave-uniform); offsets past the range write
-// zeros and read no memory. Counted by vmcnt like a load.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void *lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, 0, 0, 0);
-}
-
 // f(std::integral_constant<int, n>) for the run-time n in [1, NG].
 template <int NG, typename F>
 __device__ __forceinline__ void with_count(int n, F &&f) {
@@ -612,14 +594,6 @@ __device__ __forceinline__ void with_count(int n, F &&f) {
         }
         with_count<NG - 1>(n, f);
     }
-}
-
-// Block barrier after this wave's LDS accesses have completed. Without the
-// release fence of __syncthreads, which would also wait for every buffer ->
-// LDS copy in flight; the copies a tile needs are waited for explicitly.
-__device__ __forceinline__ void ring_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0); vmcnt and expcnt at their maxima
-    asm volatile("s_barrier" ::: "memory");
 }
 
 // LDS bytes of the ring variant: R code slots of CPT * NW / 2 KB and R
@@ -700,9 +674,9 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
         const int u = i * TC + tc;
         const int r = u / rc2;
         const int col = (u - r * rc2) ^ (r & 15);
-        coff[i] = copier && u < ncu ? r * KB + 32 * g0 + 16 * col : kRingOob;
+        coff[i] = copier && u < ncu ? r * KB + 32 * g0 + 16 * col : kCopyOob;
     }
-    int woff = kRingOob;
+    int woff = kCopyOob;
     if (!DOTS && copier && tc < 2 * Gc) {
         const int cpr8 = Gc / 8;
         const int r = tc / cpr8;
@@ -721,11 +695,11 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i)
             copy16_to_lds(rc, ring + slot * SLOT + (i * TC + kWave * cw) * 16,
-                          live ? coff[i] : kRingOob);
+                          live ? coff[i] : kCopyOob);
         if (!DOTS) {
             const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + n0 * G, rows * G * 2);
             uint8_t *dst = ws_wave ? wsr + slot * 2048 + 1024 * cw : sink;
-            copy16_to_lds(rw, dst, live ? woff : kRingOob);
+            copy16_to_lds(rw, dst, live ? woff : kCopyOob);
         }
     };
 
@@ -750,7 +724,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * lg + i;
-                const int toff = m < Mr ? 4 * (m * G + g) : kRingOob;
+                const int toff = m < Mr ? 4 * (m * G + g) : kCopyOob;
                 seed[b][i] = -__builtin_amdgcn_raw_buffer_load_b32(rt, toff, 0, 0);
                 if (!DOTS)
                     sv[b][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, toff, 0, 0));

@@ -188,6 +188,37 @@ def test_group_dots_prefill(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 1024), (2000, 2100, 2048), (2048, 2100, 1152)])
+def test_prefill_large_tiles_sampled(pq2, M, N, K):
+    """Shapes that fill the GPU with 128 x 128 tiles: G a multiple of 8 takes the
+    variant whose stages arrive by buffer -> LDS copies (ragged M and N, scale
+    chunks of 8 groups), G = 9 the register-staged one. Exact sampled group
+    dots, sampled y within tolerance, exact y with unit scales."""
+    print(f"prefill large tiles M={M} N={N} K={K}", flush=True)
+    assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PREFILL
+    x = synth.activations(M, K, M + K, outlier_frac=0.0)
+    w = synth.weights(N, K, synth.matrix_seed(N), synth.PREFILL_CODES)
+    qo, so, to = oracle.quantize(x)
+    qd, sd, td = dev(oracle.plane_order(qo)), dev(so), dev(to)
+    cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    rng = np.random.default_rng(M + N)
+    P = 512
+    mm = np.concatenate([rng.integers(0, M, P - 4), [0, M - 1, 0, M - 1]])
+    nn = np.concatenate([rng.integers(0, N, P - 4), [0, N - 1, N - 1, 0]])
+    d = torch.empty((M, N, K // G), dtype=torch.int32, device="cuda")
+    pq2.pq2_gemm_group_dots(qd, td, cd, d, path=pq2.PATH_PREFILL)
+    ds = host(d[torch.from_numpy(mm).cuda(), torch.from_numpy(nn).cuda()])
+    del d
+    np.testing.assert_array_equal(ds, oracle.group_dots_sampled(qo, w.codes, mm, nn))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(qd, sd, td, cd, wd, y)
+    ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
+    assert oracle.rel_err(host(y)[mm, nn], ys, ts) < TOL
+    ones_w = torch.full((N, K // G), 0x3C00, dtype=torch.int16, device="cuda")
+    pq2.pq2_gemm(qd, torch.ones_like(sd), td, cd, ones_w, y)
+    np.testing.assert_array_equal(host(y)[mm, nn], ds.sum(-1).astype(np.float32))
+
+
 @pytest.mark.parametrize("path,M", [(1, 1), (1, 4), (2, 5), (3, 20), (4, 7)])
 def test_code3_is_plus_two(pq2, path, M):
     """Code 3 is not a PQ2_0 code; both sides decode it as +2."""
