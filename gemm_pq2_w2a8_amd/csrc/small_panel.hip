@@ -803,17 +803,20 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
 
     float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
     // summing wave i (< 4) adds slot i of every lane's partials (token
-    // 4 (lane / 16) + i, row lane % 16) in wave order
-    auto reduce_tile = [&](int j) __attribute__((always_inline)) {
-        if (!DOTS) {
-            const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
-            const float *pr = part + (j & 1) * NW * 4 * kWave + wave * kWave + lane;
-            float v = pr[0];
+    // 4 (lane / 16) + i, row lane % 16) in wave order; the reads go out
+    // before the next tile's compute, the sum and store follow it
+    auto read_partials = [&](int j, float (&pv)[NW]) __attribute__((always_inline)) {
+        const float *pr = part + (j & 1) * NW * 4 * kWave + wave * kWave + lane;
 #pragma unroll
-            for (int w = 1; w < NW; ++w) v += pr[w * 4 * kWave];
-            const int64_t m = 4 * lg + wave, n = n0 + c;
-            if (m < M && n < N) out[m * N + n] = v;
-        }
+        for (int w = 0; w < NW; ++w) pv[w] = pr[w * 4 * kWave];
+    };
+    auto store_sum = [&](int j, const float (&pv)[NW]) __attribute__((always_inline)) {
+        const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
+        float v = pv[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += pv[w];
+        const int64_t m = 4 * lg + wave, n = n0 + c;
+        if (m < M && n < N) out[m * N + n] = v;
     };
 
     static_assert(NW == 8, "four summing waves, one per partial slot");
@@ -829,11 +832,17 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
     } else {
         for (int j = 0; j < cnt; ++j) {
             ring_barrier();
-            if (j > 0) reduce_tile(j - 1);
+            float pv[NW];
+            if (!DOTS && j > 0) read_partials(j - 1, pv);
             with_count<GSG>(ng, [&](auto ngc) { compute_tile(j, ngc); });
+            if (!DOTS && j > 0) store_sum(j - 1, pv);
         }
         ring_barrier();
-        reduce_tile(cnt - 1);
+        if (!DOTS) {
+            float pv[NW];
+            read_partials(cnt - 1, pv);
+            store_sum(cnt - 1, pv);
+        }
     }
 }
 
