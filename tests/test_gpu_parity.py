@@ -153,6 +153,10 @@ PANEL_SHAPES = [(1, 40, 2048), (2, 7, 2048), (3, 300, 2176), (5, 4100, 2304), (8
                 (4, 1030, 17408), (5, 300, 18432), (3, 200, 17536), (16, 700, 17408),
                 (9, 5000, 16384), (16, 33, 18432),
                 (2, 300, 9344), (3, 100, 9344),   # G = 73: the register-operand variant
+                # ring variant: 3 and 12 tokens, N of one tile and one row past a tile,
+                # chunks of 6 and 4 groups per wave (K split in two: 7168 = 32 + 24)
+                (3, 1000, 5120), (12, 2100, 6144), (7, 16, 2048), (13, 17, 4096),
+                (6, 900, 7168),
                 # 2 and 4 token tiles; K split so that the M-row panel fits LDS
                 (17, 300, 2048), (20, 1000, 5120), (24, 4100, 3200), (32, 700, 17408),
                 (33, 500, 2176), (40, 300, 6144), (48, 1030, 16384), (64, 4097, 5120),
