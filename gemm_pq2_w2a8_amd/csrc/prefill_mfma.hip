@@ -712,21 +712,27 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 //   4:  32 x 128, 2 x 2 waves of 16 x 64, depth 2
 //   5: 128 x 64,  2 x 2 waves of 64 x 32, depth 2
 //   6: 128 x 128, 2 x 2 waves of 64 x 64, ring of 2 stages (buffer -> LDS copies)
+//   7:  64 x 64,  2 x 2 waves of 32 x 32, depth 2
+//   8:  64 x 64,  2 x 2 waves of 32 x 32, ring of 2 stages
+//   9:  32 x 32,  2 x 2 waves of 16 x 16, depth 2
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
-    // Largest tile that still gives every CU at least one block.
     auto tiles = [&](int64_t bn, int64_t bm) { return ((N + bn - 1) / bn) * ((M + bm - 1) / bm); };
     constexpr int64_t kCUs = 256;
-    // The ring variant of the 128 x 128 tile (configuration 6) needs whole
-    // chunks of 8 groups of scales and 32-bit offsets below its sentinel;
-    // MI355X: 3-6 % faster than configuration 0 at M = 512 / 4096 on the
-    // 5120 / 17408 shapes. Deeper rings, smaller ring tiles and 8-wave tiles
-    // were slower (M = 128 to 4096).
+    // Tile choice (MI355X sweeps over M = 128 / 512 / 4096 on the 5120 and 17408
+    // shapes): 128 x 128 where that gives at least four tiles per CU, else
+    // 64 x 64 where that gives two, else 32 x 32 -- at these sizes more,
+    // smaller tiles keep more waves per CU busy (M = 128, N = 17408: 42.8 us
+    // against 54.2 with 64 x 128; M = 128, N = 5120: 20.3 against 27.0).
+    // Ring forms (stages and scale chunks by buffer -> LDS copies) where G is
+    // a multiple of 8 and offsets stay below their sentinel: 3-20 % faster.
     const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
-    int cfg = tiles(128, 128) >= kCUs ? (ring ? 6 : 0) : tiles(64, 128) >= kCUs ? 3 : 4;
+    int cfg = tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
+            : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
+                                          : 9;
     PREFILL_TUNE_OVERRIDE
-    if (cfg == 6 && !ring) cfg = 0;
+    if ((cfg == 6 || cfg == 8) && !ring) cfg = cfg == 6 ? 0 : 7;
     switch (cfg) {
         case 1: return launch_cfg<2, 8, 4, 1, 1>(q, t, codes, out, M, N, K, stream);
         case 2: return launch_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
@@ -734,6 +740,9 @@ hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *code
         case 4: return launch_cfg<1, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 5: return launch_cfg<4, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 6: return launch_ring_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 7: return launch_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 8: return launch_ring_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
+        case 9: return launch_cfg<1, 1, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         default: return launch_cfg<4, 4, 2, 2, 1>(q, t, codes, out, M, N, K, stream);
     }
 }

@@ -192,12 +192,14 @@ def test_group_dots_prefill(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 2048, 1024), (2000, 2100, 2048), (2048, 2100, 1152)])
+@pytest.mark.parametrize("M,N,K", [(4000, 4200, 1024), (4096, 4100, 1152), (2000, 2100, 2048),
+                                   (2048, 2100, 1152)])
 def test_prefill_large_tiles_sampled(pq2, M, N, K):
-    """Shapes that fill the GPU with 128 x 128 tiles: G a multiple of 8 takes the
-    variant whose stages arrive by buffer -> LDS copies (ragged M and N, scale
-    chunks of 8 groups), G = 9 the register-staged one. Exact sampled group
-    dots, sampled y within tolerance, exact y with unit scales."""
+    """Shapes that give four 128 x 128 tiles per CU (the first two) or two 64 x 64
+    tiles per CU (the last two): G a multiple of 8 takes the variants whose stages
+    arrive by buffer -> LDS copies (ragged M and N, scale chunks of 8 groups),
+    G = 9 the register-staged ones. Exact sampled group dots, sampled y within
+    tolerance, exact y with unit scales."""
     print(f"prefill large tiles M={M} N={N} K={K}", flush=True)
     assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PREFILL
     x = synth.activations(M, K, M + K, outlier_frac=0.0)
