@@ -411,7 +411,8 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
 // group (lanes past a region read past the buffer range, which moves no
 // memory), so one explicit vmcnt wait per group covers that group's copies.
 // Stage layout (16-byte units; copy instruction i of wave w writes units
-// 256 i + 64 w + lane): code unit 2 row + (half ^ ((row >> 2) & 1)), then q
+// 256 i + 64 w + lane of a region, or a sink when those lie past it): code
+// unit 2 row + (half ^ ((row >> 2) & 1)), then q
 // unit 8 token + (piece ^ (token & 7)) -- every 128-byte line is fetched by
 // one instruction, and the 16-lane operand reads hit distinct LDS banks.
 // Scales of groups 8c .. 8c + 7 travel as one chunk: ws unit row (8 halves),
@@ -419,17 +420,25 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
 // other of two chunk slots.
 template <int BN, int BM, int T, bool DOTS>
 struct PfRing {
-    static constexpr int kCodeInst = (2 * BN + T - 1) / T;         // copies per thread, codes
-    static constexpr int kQInst = (8 * BM + T - 1) / T;            // copies per thread, q
+    // copies per thread; a wave whose units of an instruction all lie past a
+    // region copies into a shared 1 KB sink instead, so each region only
+    // spans its units rounded up to a wave (64 units)
+    static constexpr int kCodeInst = (2 * BN + T - 1) / T;
+    static constexpr int kQInst = (8 * BM + T - 1) / T;
     static constexpr int kStageInst = kCodeInst + kQInst;
-    static constexpr int kQBase = kCodeInst * T;                   // first q unit
-    static constexpr int kStageBytes = kStageInst * T * 16;
+    static constexpr int kCodeUnits = (2 * BN + 63) / 64 * 64;
+    static constexpr int kQUnits = (8 * BM + 63) / 64 * 64;
+    static constexpr int kQBase = kCodeUnits;                      // first q unit
+    static constexpr int kStageBytes = (kCodeUnits + kQUnits) * 16;
     static constexpr int kWsInst = DOTS ? 0 : (BN + T - 1) / T;
     static constexpr int kTokInst = (2 * BM + T - 1) / T;          // per s or t table
     static constexpr int kScaleInst = kWsInst + (DOTS ? 1 : 2) * kTokInst;
-    static constexpr int kSBase = kWsInst * T;                     // first s unit
-    static constexpr int kTBase = kSBase + (DOTS ? 0 : kTokInst * T);
-    static constexpr int kScaleBytes = kScaleInst * T * 16;
+    static constexpr int kWsUnits = DOTS ? 0 : (BN + 63) / 64 * 64;
+    static constexpr int kTokUnits = (2 * BM + 63) / 64 * 64;
+    static constexpr int kSBase = kWsUnits;                        // first s unit
+    static constexpr int kTBase = kSBase + (DOTS ? 0 : kTokUnits);
+    static constexpr int kScaleBytes = (kTBase + kTokUnits) * 16;
+    static constexpr int kSinkBytes = 1024;
 };
 
 template <int WN, int WM, int WAVES_N, int WAVES_M, int R, bool DOTS>
@@ -449,9 +458,16 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *const ring0 = smem;
     uint8_t *const scl0 = smem + R * L::kStageBytes;
+    uint8_t *const sink = scl0 + 2 * L::kScaleBytes;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    // LDS destination of copy instruction i of this wave into a region of
+    // `units` units at `base` (past the region: the sink)
+    auto dst = [&](uint8_t *base, int units, int i) __attribute__((always_inline)) {
+        const int u = i * T + kWave * wave;
+        return u < units ? base + u * 16 : sink;
+    };
     const int wn = wave % WAVES_N, wm = wave / WAVES_N;
     const int r = lane & 15, lg = lane >> 4;
     const int half = lg & 1;
@@ -509,11 +525,11 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
         uint8_t *st = ring0 + (g % R) * L::kStageBytes;
 #pragma unroll
         for (int i = 0; i < L::kCodeInst; ++i)
-            copy16_to_lds(rs_codes, st + (i * T + kWave * wave) * 16,
+            copy16_to_lds(rs_codes, dst(st, L::kCodeUnits, i),
                           live && coff[i] != kCopyOob ? coff[i] + 32 * g : kCopyOob);
 #pragma unroll
         for (int i = 0; i < L::kQInst; ++i)
-            copy16_to_lds(rs_q, st + (L::kQBase + i * T + kWave * wave) * 16,
+            copy16_to_lds(rs_q, dst(st + L::kQBase * 16, L::kQUnits, i),
                           live && qoff[i] != kCopyOob ? qoff[i] + kGroup * g : kCopyOob);
     };
     auto issue_scales = [&](int c) __attribute__((always_inline)) {
@@ -521,17 +537,17 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
         uint8_t *sc = scl0 + (c & 1) * L::kScaleBytes;
 #pragma unroll
         for (int i = 0; i < L::kWsInst; ++i)
-            copy16_to_lds(rs_ws, sc + (i * T + kWave * wave) * 16,
+            copy16_to_lds(rs_ws, dst(sc, L::kWsUnits, i),
                           live && wsoff[i] != kCopyOob ? wsoff[i] + 16 * c : kCopyOob);
         if (!DOTS) {
 #pragma unroll
             for (int i = 0; i < L::kTokInst; ++i)
-                copy16_to_lds(rs_s, sc + (L::kSBase + i * T + kWave * wave) * 16,
+                copy16_to_lds(rs_s, dst(sc + L::kSBase * 16, L::kTokUnits, i),
                               live && toff[i] != kCopyOob ? toff[i] + 32 * c : kCopyOob);
         }
 #pragma unroll
         for (int i = 0; i < L::kTokInst; ++i)
-            copy16_to_lds(rs_t, sc + (L::kTBase + i * T + kWave * wave) * 16,
+            copy16_to_lds(rs_t, dst(sc + L::kTBase * 16, L::kTokUnits, i),
                           live && toff[i] != kCopyOob ? toff[i] + 32 * c : kCopyOob);
     };
 
@@ -670,13 +686,13 @@ hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *cod
     const int64_t blocks = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
     if (out.d) {
         using L = PfRing<C::BN, C::BM, C::kThreads, true>;
-        const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes;
+        const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes + L::kSinkBytes;
         hipLaunchKernelGGL((prefill_ring_kernel<WN, WM, WAVES_N, WAVES_M, R, true>),
                            dim3((unsigned)blocks), dim3(C::kThreads), lds, stream, q, nullptr, t,
                            codes, nullptr, nullptr, out.d, M, N, K);
     } else {
         using L = PfRing<C::BN, C::BM, C::kThreads, false>;
-        const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes;
+        const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes + L::kSinkBytes;
         hipLaunchKernelGGL((prefill_ring_kernel<WN, WM, WAVES_N, WAVES_M, R, false>),
                            dim3((unsigned)blocks), dim3(C::kThreads), lds, stream, q, out.s, t,
                            codes, out.ws, out.y, nullptr, M, N, K);
@@ -723,10 +739,13 @@ hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *code
     // Tile choice (MI355X sweeps over M = 128 / 512 / 4096 on the 5120 and 17408
     // shapes): 128 x 128 where that gives at least four tiles per CU, else
     // 64 x 64 where that gives two, else 32 x 32 -- at these sizes more,
-    // smaller tiles keep more waves per CU busy (M = 128, N = 17408: 42.8 us
-    // against 54.2 with 64 x 128; M = 128, N = 5120: 20.3 against 27.0).
+    // smaller tiles keep more waves per CU busy (M = 128, N = 17408: 43.7 us
+    // against 54.2 with 64 x 128; M = 128, N = 5120: 20.4 against 27.0).
     // Ring forms (stages and scale chunks by buffer -> LDS copies) where G is
-    // a multiple of 8 and offsets stay below their sentinel: 3-20 % faster.
+    // a multiple of 8 and offsets stay below their sentinel: 3-20 % faster;
+    // the 64 x 64 ring (88 VGPRs, 31 KB of LDS) runs five blocks per CU. Ring
+    // forms of the 32 x 32, 64 x 128 tiles and a 3-stage 64 x 64 ring were
+    // slower.
     const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
     int cfg = tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
             : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
