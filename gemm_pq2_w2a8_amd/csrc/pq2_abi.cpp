@@ -44,9 +44,11 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
 // where only its other variants run it wins on large matrices (N*K > 2^25)
 // and, from M = 8, on every size it can hold (K from 2048 to 18432, within
 // LDS); otherwise the dot4 GEMV for M = 3..4 on large matrices with K too
-// large for the panel, else the 16-token MFMA kernel. For
-// 17 <= M <= 64 the panel kernel in 2 or 4 token tiles takes 0.3-0.77 of the
-// tiled GEMM's time on the 5120 / 6144 / 17408 shapes, wherever it has a plan.
+// large for the panel, else the 16-token MFMA kernel. For 17 <= M <= 64 the
+// panel kernel in 2 or 4 token tiles wins where the tiled GEMM has fewer than
+// two blocks per CU (5120 x 6144 at M = 32: 12.9 us against 16.4; 5120 x
+// 17408: 23.0 against 46.1); with more the tiled GEMM wins (17408 x 5120 at
+// M = 32: 21.0 against 24.5).
 #ifndef PQ2_AUTO_OVERRIDE
 #define PQ2_AUTO_OVERRIDE
 #endif
@@ -58,7 +60,8 @@ int auto_path(int64_t M, int64_t N, int64_t K) {
     if (M <= 16 && (large || M >= 8) && pq2::small_panel_fits(M, K)) return PQ2_PATH_PANEL;
     if (M <= pq2::kGemvMaxM && large) return PQ2_PATH_GEMV;
     if (M <= 16 && K <= pq2::kSmallMaxK) return PQ2_PATH_SMALL;
-    if (M <= pq2::kPanelMaxM && pq2::small_panel_fits(M, K)) return PQ2_PATH_PANEL;
+    if (M <= pq2::kPanelMaxM && pq2::prefill_blocks(M, N) < 512 && pq2::small_panel_fits(M, K))
+        return PQ2_PATH_PANEL;
     return PQ2_PATH_PREFILL;
 }
 

@@ -61,6 +61,9 @@ float *split_workspace(size_t bytes, hipStream_t stream);
 hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
                             hipStream_t stream);
 
+// Blocks the tiled prefill kernel launches for M x N (its tile rule).
+int64_t prefill_blocks(int64_t M, int64_t N);
+
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream);

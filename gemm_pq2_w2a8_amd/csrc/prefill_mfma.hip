@@ -731,11 +731,29 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 //   7:  64 x 64,  2 x 2 waves of 32 x 32, depth 2
 //   8:  64 x 64,  2 x 2 waves of 32 x 32, ring of 2 stages
 //   9:  32 x 32,  2 x 2 waves of 16 x 16, depth 2
+namespace {
+
+constexpr int64_t kPrefillCUs = 256;
+
+// The tile rule below as block counts: 128 x 128 tiles where that gives four
+// per CU, else 64 x 64 where that gives two, else 32 x 32.
+int64_t prefill_tiles(int64_t M, int64_t N, int64_t bn, int64_t bm) {
+    return ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+}
+
+}  // namespace
+
+int64_t prefill_blocks(int64_t M, int64_t N) {
+    if (prefill_tiles(M, N, 128, 128) >= 4 * kPrefillCUs) return prefill_tiles(M, N, 128, 128);
+    if (prefill_tiles(M, N, 64, 64) >= 2 * kPrefillCUs) return prefill_tiles(M, N, 64, 64);
+    return prefill_tiles(M, N, 32, 32);
+}
+
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K,
                           hipStream_t stream) {
-    auto tiles = [&](int64_t bn, int64_t bm) { return ((N + bn - 1) / bn) * ((M + bm - 1) / bm); };
-    constexpr int64_t kCUs = 256;
+    auto tiles = [&](int64_t bn, int64_t bm) { return prefill_tiles(M, N, bn, bm); };
+    constexpr int64_t kCUs = kPrefillCUs;
     // Tile choice (MI355X sweeps over M = 128 / 512 / 4096 on the 5120 and 17408
     // shapes): 128 x 128 where that gives at least four tiles per CU, else
     // 64 x 64 where that gives two, else 32 x 32 -- at these sizes more,

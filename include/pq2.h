@@ -114,7 +114,8 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
  *                    with N*K > 2^25; else the 16-token MFMA kernel
  *                    (K <= 32768);
  *   17 <= M <= 64 -> the same persistent kernel in 2 or 4 token tiles where
- *                    the panel fits;
+ *                    the panel fits and the tiled GEMM below would launch
+ *                    fewer than 512 blocks (2 per CU);
  *   otherwise     -> tiled int8 MFMA GEMM (prefill).
  * pq2_gemm_kernel_path reports the choice.
  * Group dots are exact int32; the float32 epilogue sums the G terms in an

@@ -119,6 +119,8 @@ def test_kernel_path_query():
     assert f(2, 17408, 5120) == pq2.PATH_GEMV
     assert f(17, 8, 128) == pq2.PATH_PREFILL
     assert f(16, 8, 32768 + 128) == pq2.PATH_PREFILL
+    # 17..64 rows where the tiled GEMM fills two blocks per CU: the tiled GEMM
+    assert f(32, 17408, 5120) == pq2.PATH_PREFILL
     # without a GPU the panel kernel never fits: the 16-token kernel is chosen
     assert f(8, 5120, 17408) == pq2.PATH_SMALL
 

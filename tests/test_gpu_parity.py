@@ -394,9 +394,16 @@ FULL = [
     ("small_m16_down", 16, 5120, 17408, synth.UNIFORM_CODES, 0.01),
     ("tokens_m32_up", 32, 17408, 5120, synth.UNIFORM_CODES, 0.01),
     ("tokens_m64_down", 64, 5120, 17408, synth.UNIFORM_CODES, 0.01),
+    ("tokens_m32_oproj", 32, 5120, 6144, synth.UNIFORM_CODES, 0.01),
     ("prefill_m512", 512, 5120, 5120, synth.PREFILL_CODES, 0.0),
     ("prefill_m4096_up", 4096, 17408, 5120, synth.PREFILL_CODES, 0.0),
 ]
+
+
+# 17..64 token rows: the panel kernel in token tiles where the tiled GEMM would
+# launch fewer than two blocks per CU, else the tiled GEMM.
+TOKENS_PATH = {"tokens_m32_up": "PATH_PREFILL", "tokens_m64_down": "PATH_PANEL",
+               "tokens_m32_oproj": "PATH_PANEL"}
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (2, 17408, 5120), (4, 5120, 17408)])
@@ -420,8 +427,8 @@ def test_linear_full_size_sampled(pq2, M, N, K):
 @pytest.mark.parametrize("name,M,N,K,probs,outl", FULL, ids=[f[0] for f in FULL])
 def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
     print(f"full {name} M={M} N={N} K={K}", flush=True)
-    if name.startswith("tokens"):
-        assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PANEL   # 2 or 4 token tiles
+    if name in TOKENS_PATH:
+        assert pq2.gemm_kernel_path(M, N, K) == getattr(pq2, TOKENS_PATH[name])
     x = synth.activations(M, K, 0, outlier_frac=outl)
     w = synth.weights(N, K, synth.matrix_seed(0), probs)
     xd, cd, wd = dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))
