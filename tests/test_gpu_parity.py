@@ -294,6 +294,37 @@ def test_gemm_path_y(pq2, path, M, N, K):
     np.testing.assert_array_equal(host(y), D.sum(-1).astype(np.float32))
 
 
+@pytest.mark.parametrize("K", [2048, 2304])
+def test_auto_path_every_m(pq2, K):
+    """pq2_gemm's own kernel choice for every M from 1 to 72 on one weight matrix:
+    the group dots of the chosen path are exact, y is within tolerance, and the
+    sweep crosses every routing boundary (G = 16 takes the ring kernel at 3..16
+    tokens, G = 18 the 16-token kernel at 3..7)."""
+    N = 520
+    w = synth.weights(N, K, synth.matrix_seed(K))
+    cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    x_all = synth.activations(72, K, K, outlier_frac=0.01)
+    seen = set()
+    for M in range(1, 73):
+        path = pq2.gemm_kernel_path(M, N, K)
+        seen.add(path)
+        print(f"auto M={M} N={N} K={K} path={path}", flush=True)
+        x = x_all[:M]
+        qo, so, to = oracle.quantize(x)
+        qd, td = dev(oracle.plane_order(qo)), dev(to)
+        d = torch.empty((M, N, K // G), dtype=torch.int32, device="cuda")
+        pq2.pq2_gemm_group_dots(qd, td, cd, d)
+        np.testing.assert_array_equal(host(d), oracle.group_dots(qo, w.codes))
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        pq2.pq2_gemm(qd, dev(so), td, cd, wd, y)
+        yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+        assert oracle.rel_err(host(y), yo, tabs) < TOL
+    want = {pq2.PATH_GEMV, pq2.PATH_PANEL, pq2.PATH_PREFILL}
+    if K == 2304:
+        want.add(pq2.PATH_SMALL)
+    assert seen == want
+
+
 def test_tiny_workload(pq2):
     wl = synth.tiny()
     w = synth.weights(wl.n, wl.k, 0)
