@@ -20,8 +20,9 @@
 //    (one 16-byte LDS read). The accumulator is seeded with -t, so the two
 //    MFMAs give the exact group dot; the float32 epilogue
 //    acc += D * (s[m] * ws[n]) follows per group.
-//  * The float epilogue (convert, scale product, FMA per output and group)
-//    is the VALU work that bounds this kernel, so everything else is kept
+//  * The float epilogue (convert, scale product, FMA per output and group;
+//    the product widens the half scale inside one mixed-precision FMA) is
+//    the VALU work that bounds this kernel, so everything else is kept
 //    off the VALU: MFMA results stay in VGPRs (no accumulator-register
 //    copies), global addresses are a uniform 64-bit base plus a fixed 32-bit
 //    per-lane offset, and a lane's A operands are formed once per group and
@@ -54,6 +55,13 @@ constexpr int kNumXcd = 8;
 // dimension of the [rows][G] scale arrays, so one load instruction touches a
 // few cache lines instead of one line per lane.
 constexpr int kScaleChunk = 8;
+
+// s * ws for the epilogue as one mixed-precision FMA that widens the half
+// scale itself (v_fma_mix_f32): the float32 product s * (float)ws with +0
+// added, one instruction where a conversion and a multiply would be two.
+__device__ __forceinline__ float scale_product(float sv, _Float16 w) {
+    return fmaf(sv, (float)w, 0.0f);
+}
 
 // Bijection from dispatch order to tile order: dispatch slot b runs on XCD
 // b % 8; XCD x receives the x-th contiguous run of tile numbers.
@@ -149,7 +157,7 @@ __device__ __forceinline__ void compute_group(const Stage &cur, const uint16_t *
     }
     __builtin_amdgcn_sched_barrier(0);
     v4i a0[WN], a1[WN];
-    float wsf[WN][4];
+    _Float16 wsh[WN][4];
 #pragma unroll
     for (int a = 0; a < WN; ++a) {
 #pragma unroll
@@ -159,10 +167,10 @@ __device__ __forceinline__ void compute_group(const Stage &cur, const uint16_t *
             a1[a][j] = (int)((sh >> 4) & kPlaneMask);
         }
         if (!DOTS) {
-            wsf[a][0] = half_bits_to_float((uint16_t)(wsw[a].x & 0xffff));
-            wsf[a][1] = half_bits_to_float((uint16_t)(wsw[a].x >> 16));
-            wsf[a][2] = half_bits_to_float((uint16_t)(wsw[a].y & 0xffff));
-            wsf[a][3] = half_bits_to_float((uint16_t)(wsw[a].y >> 16));
+            wsh[a][0] = __builtin_bit_cast(_Float16, (uint16_t)(wsw[a].x & 0xffff));
+            wsh[a][1] = __builtin_bit_cast(_Float16, (uint16_t)(wsw[a].x >> 16));
+            wsh[a][2] = __builtin_bit_cast(_Float16, (uint16_t)(wsw[a].y & 0xffff));
+            wsh[a][3] = __builtin_bit_cast(_Float16, (uint16_t)(wsw[a].y >> 16));
         }
     }
 #pragma unroll
@@ -185,7 +193,7 @@ __device__ __forceinline__ void compute_group(const Stage &cur, const uint16_t *
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc[a][b][i] = fmaf((float)c[a][i], sv[b] * wsf[a][i], acc[a][b][i]);
+                    acc[a][b][i] = fmaf((float)c[a][i], scale_product(sv[b], wsh[a][i]), acc[a][b][i]);
             }
         }
     }
@@ -599,7 +607,7 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
     // every MFMA of the group before any epilogue measured 1.5-1.9x slower)
     auto mma = [&](const Ops &o, int g) __attribute__((always_inline)) {
         v4i a0[WN], a1[WN];
-        float wsf[WN][4];
+        _Float16 wsh[WN][4];
 #pragma unroll
         for (int a = 0; a < WN; ++a) {
 #pragma unroll
@@ -610,7 +618,7 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
             }
             if (!DOTS) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) wsf[a][i] = half_bits_to_float(o.wsh[a][i]);
+                for (int i = 0; i < 4; ++i) wsh[a][i] = __builtin_bit_cast(_Float16, o.wsh[a][i]);
             }
         }
 #pragma unroll
@@ -633,7 +641,8 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc[a][b][i] = fmaf((float)c[a][i], o.sv[b] * wsf[a][i], acc[a][b][i]);
+                        acc[a][b][i] = fmaf((float)c[a][i], scale_product(o.sv[b], wsh[a][i]),
+                                            acc[a][b][i]);
                 }
             }
         }
