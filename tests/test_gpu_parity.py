@@ -437,6 +437,52 @@ TOKENS_PATH = {"tokens_m32_up": "PATH_PREFILL", "tokens_m64_down": "PATH_PANEL",
                "tokens_m32_oproj": "PATH_PANEL"}
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (4, 300, 17408), (2, 1000, 2048), (3, 70, 128)])
+def test_linear_back_to_back_and_streams(pq2, M, N, K):
+    """Calls of pq2_linear issued back to back with no host synchronisation, on
+    one stream and alternating over two, each give y bit-identical to
+    pq2_quantize_act + the GEMV path on their own input; so do a larger call
+    (K doubled, four rows) and a smaller one after it."""
+    print(f"linear back-to-back M={M} N={N} K={K}", flush=True)
+    w = synth.weights(N, K, synth.matrix_seed(K + M))
+    cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    xs, ys = [], []
+    for i in range(12):
+        x = dev(synth.activations(M, K, 100 + i, outlier_frac=0.01))
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        xs.append(x)
+        ys.append(y)
+    torch.cuda.synchronize()
+    for i in range(6):                       # one stream, back to back
+        pq2.pq2_linear(xs[i], cd, wd, ys[i])
+    for i in range(6, 12):                   # two streams, interleaved
+        st = streams[i % 2]
+        with torch.cuda.stream(st):
+            pq2.pq2_linear(xs[i], cd, wd, ys[i], stream=st)
+    torch.cuda.synchronize()
+    for i in range(12):
+        q, s, t = pq2.quantize_act(xs[i])
+        yr = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        pq2.pq2_gemm_path(q, s, t, cd, wd, yr, pq2.PATH_GEMV)
+        np.testing.assert_array_equal(host(ys[i]), host(yr), err_msg=f"call {i}")
+    # a larger call, then a smaller one
+    xb = dev(synth.activations(4, 2 * K, 7, outlier_frac=0.01))
+    wb = synth.weights(N, 2 * K, synth.matrix_seed(2 * K))
+    cb, wbd = dev(wb.codes), dev(wb.wscale_bits.view(np.int16))
+    yb = torch.empty((4, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_linear(xb, cb, wbd, yb)
+    pq2.pq2_linear(xs[0], cd, wd, ys[0])
+    q, s, t = pq2.quantize_act(xb)
+    yr = torch.empty((4, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm_path(q, s, t, cb, wbd, yr, pq2.PATH_GEMV)
+    np.testing.assert_array_equal(host(yb), host(yr))
+    q, s, t = pq2.quantize_act(xs[0])
+    yr = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm_path(q, s, t, cd, wd, yr, pq2.PATH_GEMV)
+    np.testing.assert_array_equal(host(ys[0]), host(yr))
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (2, 17408, 5120), (4, 5120, 17408)])
 def test_linear_full_size_sampled(pq2, M, N, K):
     """pq2_linear at the decode and small-batch sizes against sampled oracle outputs."""
