@@ -564,6 +564,73 @@ def test_small_multi_tile_blocks(pq2, M, N, K):
     assert oracle.rel_err(y[mm, nn], ys, ts) < TOL
 
 
+# Shapes whose code bytes or outputs lie past 2^31 (byte or element offsets), one
+# per kernel path: 2.7 GB of codes for the GEMV, 16-token and panel kernels,
+# 4.3 G outputs (17 GB of y) for the tiled GEMM.
+BIG = [("gemv", 1, (1 << 21) + (1 << 19) + 3, 4096, "PATH_GEMV"),
+       ("small", 5, (1 << 21) + (1 << 19) + 3, 4096, "PATH_SMALL"),
+       ("panel", 16, (1 << 21) + (1 << 19) + 3, 4096, "PATH_PANEL"),
+       ("prefill", 4096, (1 << 20) + 37, 1024, "PATH_PREFILL")]
+
+
+@pytest.mark.parametrize("name,M,N,K,path", BIG, ids=[b[0] for b in BIG])
+def test_offsets_beyond_2_31(pq2, name, M, N, K, path):
+    """Random codes, scales and activations drawn on the GPU (seeded); sampled
+    outputs, including the last rows and tokens, against the oracle."""
+    print(f"big {name} M={M} N={N} K={K}", flush=True)
+    G_ = K // G
+    gen = torch.Generator(device="cuda").manual_seed(M + N)
+    codes = torch.randint(0, 256, (N, K // 4), dtype=torch.uint8, device="cuda", generator=gen)
+    wsc = (torch.rand((N, G_), device="cuda", generator=gen) * 0.09 + 0.01).half().view(torch.int16)
+    x = torch.randn((M, K), device="cuda", generator=gen)
+    q, s, t = pq2.quantize_act(x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pid = getattr(pq2, path)
+    if path == "PATH_SMALL":
+        pq2.pq2_gemm_path(q, s, t, codes, wsc, y, pid)
+    else:
+        assert pq2.gemm_kernel_path(M, N, K) == pid
+        pq2.pq2_gemm(q, s, t, codes, wsc, y)
+    rng = np.random.default_rng(5)
+    P = 256
+    mm = np.concatenate([rng.integers(0, M, P - 4), [M - 1, M - 1, 0, M // 2]])
+    nn = np.concatenate([rng.integers(0, N, P - 4), [N - 1, N - 2, N - 1, N - 3]])
+    if name == "prefill":       # outputs past 2^31 elements: the upper half of the tokens
+        mm[: P // 2] = rng.integers(M // 2, M, P // 2)
+    else:                       # code bytes past 2^31: rows from 2^21 on
+        nn[: P // 2] = rng.integers(1 << 21, N, P // 2)
+    ys = y[torch.from_numpy(mm).cuda(), torch.from_numpy(nn).cuda()].cpu().numpy()
+    um, im = np.unique(mm, return_inverse=True)
+    un, inn = np.unique(nn, return_inverse=True)
+    xs = x[torch.from_numpy(um).cuda()].cpu().numpy()
+    cs = codes[torch.from_numpy(un).cuda()].cpu().numpy()
+    ws_h = wsc[torch.from_numpy(un).cuda()].cpu().numpy()
+    del codes, wsc, x, q, s, t, y
+    torch.cuda.empty_cache()
+    qo, so, _ = oracle.quantize(xs)
+    yo, tabs = oracle.gemm_f64_sampled(qo, so, cs, ws_h, im, inn)
+    assert oracle.rel_err(ys, yo, tabs) < TOL
+
+
+def test_quantize_beyond_2_31(pq2):
+    """The quantiser over 2^32 + 2^14 activations (17 GB of x): sampled rows on
+    both sides of element 2^31 bit-exact against the oracle."""
+    M, K = (1 << 18) + 1, 16384
+    print(f"big quantize M={M} K={K}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn((M, K), device="cuda", generator=gen)
+    q, s, t = pq2.quantize_act(x)
+    rows = np.array([0, 1, (1 << 17) - 1, 1 << 17, (1 << 17) + 5, M - 2, M - 1])
+    ri = torch.from_numpy(rows).cuda()
+    xs, qs, ss, ts = (a[ri].cpu().numpy() for a in (x, q, s, t))
+    del x, q, s, t
+    torch.cuda.empty_cache()
+    qo, so, to = oracle.quantize(xs)
+    np.testing.assert_array_equal(qs, oracle.plane_order(qo))
+    np.testing.assert_array_equal(ss.view(np.uint32), so.view(np.uint32))
+    np.testing.assert_array_equal(ts, to)
+
+
 def test_split_k_streams_and_workspace_growth(pq2):
     """Split-K y (K = 17408 at M = 16: three chunks through the library's
     workspace) is identical on repeated calls, on two streams running
