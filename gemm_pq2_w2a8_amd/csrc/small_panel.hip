@@ -864,13 +864,12 @@ struct DevLimits {
 };
 
 // Compute units and LDS limits of the current device, read once per device.
-const DevLimits &dev_limits() {
+DevLimits dev_limits() {
     static DevLimits cache[64];
+    static std::mutex mu;             // host threads may plan launches concurrently
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-        static DevLimits none;
-        return none;
-    }
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DevLimits();
+    std::lock_guard<std::mutex> lock(mu);
     DevLimits &l = cache[dev];
     if (l.cus == 0) {
         DevLimits v;
