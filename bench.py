@@ -406,8 +406,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the PQ2_0 path is measured on a "
-              "single MI355X (--gpus 1).", file=sys.stderr)
+        print("bench.py: the PQ2_0 path is measured on a single MI355X; run with --gpus 1 "
+              "(no multi-GPU path is built).", file=sys.stderr)
         sys.exit(2)
 
     import torch
