@@ -318,8 +318,11 @@ def report_gemm(args, wl, r, torch):
     return line
 
 
-def run_layers(args, m, torch, pq2):
-    """64-layer synthetic decode step: 5 PQ2_0 projections per layer, back to back."""
+def layer_step(m, torch, pq2, stream):
+    """The 64-layer synthetic decode step as a list of launches on `stream`:
+    returns (step, shares_input); step(after=None) enqueues every projection
+    (quantise where the input is new, then pq2_gemm) and calls after() behind
+    each projection's GEMM."""
     import pq2_synth as synth
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
@@ -334,7 +337,6 @@ def run_layers(args, m, torch, pq2):
                        torch.empty((m, k // GROUP), dtype=torch.int32, device=dev))
     ys = {n: torch.empty((m, n), dtype=torch.float32, device=dev) for (n, _) in synth.LAYER_SHAPES}
     lib = pq2.lib
-    stream = torch.cuda.current_stream(dev).cuda_stream
     # the gate and up projections (the two 5120 -> 17408 ones) read the same
     # activations, so one quantisation serves both; every other projection
     # quantises its own input
@@ -348,12 +350,23 @@ def run_layers(args, m, torch, pq2):
                           t.data_ptr(), codes.data_ptr(), ws.data_ptr(), ys[n].data_ptr(), n, k))
     quant, gemm = lib.pq2_quantize_act, lib.pq2_gemm
 
-    def step():
+    def step(after=None):
         for (qz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
             if qz:
                 quant(xp, qp, sp, tp, m, k, stream)
             gemm(qp, sp, tp, cp, wp, yp, m, n, k, stream)
+            if after is not None:
+                after()
 
+    step.buffers = (layers, xs, bufs, ys)     # the launches hold raw pointers into these
+    return step, shares_input
+
+
+def run_layers(args, m, torch, pq2):
+    """64-layer synthetic decode step: 5 PQ2_0 projections per layer, back to back."""
+    import pq2_synth as synth
+    stream = torch.cuda.current_stream(torch.device("cuda:0")).cuda_stream
+    step, shares_input = layer_step(m, torch, pq2, stream)
     for _ in range(2):
         step()
     torch.cuda.synchronize()
@@ -390,6 +403,60 @@ def run_layers(args, m, torch, pq2):
                          "note": "whole step incl. quantise launches and launch gaps"}}
 
 
+# The pages' power proxy: a low-power spin after every projection stands in for
+# the decode step's other work (norms, attention, recurrent updates, sampling),
+# so that a replay of the projections runs at the clock and power state of
+# serving rather than of back-to-back memory-bound kernels. The pages set the
+# spin from a serving trace: 25 to 55 thousand cycles for 2 to 16 tokens, at
+# about 1.5 cycles per nanosecond of measured other work (page "Making a
+# ternary reasoning model fast in vLLM", section "A power proxy for the rest
+# of the model"). Here the spin is given as that much time per projection.
+def proxy_spin_us(m):
+    cycles = 25000.0 + (min(max(m, 2), 16) - 2) * (55000.0 - 25000.0) / 14.0
+    return cycles / 1.5 / 1000.0
+
+
+def run_proxy(args, m, torch, pq2):
+    """The 64-layer step with a spin after every projection, captured once in a
+    HIP graph and replayed back to back for --proxy-seconds. Kernel durations
+    under the proxy come from a kernel trace of this run (the spin's wall time
+    follows the clock, so the step time mixes the two); this line reports the
+    replay itself."""
+    dev = torch.device("cuda:0")
+    cap = torch.cuda.Stream(dev)
+    spin_us = proxy_spin_us(m) if args.proxy_spin_us is None else args.proxy_spin_us
+    cyc_per_ms = spin_cycles_per_ms(torch)
+    spin = int(cyc_per_ms * spin_us / 1000.0)
+    step, _ = layer_step(m, torch, pq2, cap.cuda_stream)
+    after = (lambda: torch.cuda._sleep(spin)) if spin > 0 else None
+    with torch.cuda.stream(cap):
+        step(after)                 # eager first: any per-stream workspace exists before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step(after)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    replays, t0 = 0, time.perf_counter()
+    a.record()
+    while time.perf_counter() - t0 < args.proxy_seconds:
+        for _ in range(10):
+            g.replay()
+        replays += 10
+        torch.cuda.synchronize()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / replays
+    return {"proxy": {"workload": f"layer64_m{m}", "M": m, "spin_us_per_projection": spin_us,
+                      "spin_cycles": spin, "projections_per_step": 5 * 64,
+                      "replays": replays, "ms_per_replay": ms,
+                      "note": "HIP-graph replay of the 64-layer step with a spin after every "
+                              "projection; GEMM kernel durations from a kernel trace of this run"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -399,6 +466,12 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="one line per configuration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--proxy", type=int, default=0, metavar="M",
+                    help="power-proxy replay of the 64-layer step at M token rows "
+                         "(one JSON line of its own, not the bench line)")
+    ap.add_argument("--proxy-seconds", type=float, default=5.0)
+    ap.add_argument("--proxy-spin-us", type=float, default=None,
+                    help="spin per projection (default: the pages' calibration for M; 0: none)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise kernel (y = 2x, float32) over MIB MiB, "
                          "the calibration for HBM byte counters")
@@ -428,6 +501,10 @@ def main():
         return
 
     import gemm_pq2_w2a8_amd as pq2
+
+    if args.proxy:
+        print(json.dumps(run_proxy(args, args.proxy, torch, pq2)), flush=True)
+        return
 
     wls = workload_list()
     names = list(wls) if args.sweep else [args.workload]

@@ -325,6 +325,55 @@ def test_auto_path_every_m(pq2, K):
     assert seen == want
 
 
+def test_graph_replay_with_spins(pq2):
+    """The power-proxy replay's pattern: quantise + pq2_gemm for projections on
+    every kernel path (GEMV, panel ring, panel with split K and its workspace,
+    token tiles, tiled GEMM and its ring form), each followed by a spin kernel, captured in one
+    HIP graph. Three replays, with eager work and synchronisations between
+    them, each give y bit-identical to the eager calls."""
+    shapes = [(1, 300, 2048), (4, 520, 2048), (16, 300, 17408), (40, 200, 2048), (130, 260, 1024),
+              (256, 8192, 1024)]
+    cap = torch.cuda.Stream()
+    bufs = []
+    for i, (M, N, K) in enumerate(shapes):
+        w = synth.weights(N, K, synth.matrix_seed(500 + i))
+        x = dev(synth.activations(M, K, 500 + i, outlier_frac=0.01))
+        G_ = K // G
+        bufs.append((M, N, K, x, dev(w.codes), dev(w.wscale_bits.view(np.int16)),
+                     torch.empty((M, K), dtype=torch.int8, device="cuda"),
+                     torch.empty((M, G_), dtype=torch.float32, device="cuda"),
+                     torch.empty((M, G_), dtype=torch.int32, device="cuda"),
+                     torch.empty((M, N), dtype=torch.float32, device="cuda")))
+
+    def step():
+        for (M, N, K, x, cd, wd, q, s, t, y) in bufs:
+            pq2.pq2_quantize_act(x, q, s, t, stream=cap)
+            pq2.pq2_gemm(q, s, t, cd, wd, y, stream=cap)
+            torch.cuda._sleep(1000)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cap):
+        step()                                   # eager: also creates the split-K workspace
+    torch.cuda.synchronize()
+    ref = [host(b[-1]).copy() for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        step()
+    torch.cuda.synchronize()
+    other = torch.empty((16, 300), dtype=torch.float32, device="cuda")
+    for rep in range(3):
+        for b in bufs:                           # eager work between replays
+            b[-1].fill_(float("nan"))
+        M, N, K, x, cd, wd, q, s, t, _ = bufs[2]
+        pq2.pq2_gemm(q, s, t, cd, wd, other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, b in enumerate(bufs):
+            print(f"graph replay {rep} shape {shapes[i]}", flush=True)
+            np.testing.assert_array_equal(host(b[-1]), ref[i])
+
+
 def test_tiny_workload(pq2):
     wl = synth.tiny()
     w = synth.weights(wl.n, wl.k, 0)
