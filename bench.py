@@ -406,11 +406,12 @@ def run_layers(args, m, torch, pq2):
 # The pages' power proxy: a low-power spin after every projection stands in for
 # the decode step's other work (norms, attention, recurrent updates, sampling),
 # so that a replay of the projections runs at the clock and power state of
-# serving rather than of back-to-back memory-bound kernels. The pages set the
-# spin from a serving trace: 25 to 55 thousand cycles for 2 to 16 tokens, at
-# about 1.5 cycles per nanosecond of measured other work (page "Making a
-# ternary reasoning model fast in vLLM", section "A power proxy for the rest
-# of the model"). Here the spin is given as that much time per projection.
+# serving rather than of back-to-back memory-bound kernels. The pages sized
+# the spin from a serving trace (page "Making a ternary reasoning model fast
+# in vLLM", section "A power proxy for the rest of the model"): 25k cycles at
+# 2 tokens rising to 55k at 16, which they relate to the non-GEMM time of the
+# trace at roughly 1.5 spin cycles per ns. Here the spin is that much time
+# per projection.
 def proxy_spin_us(m):
     cycles = 25000.0 + (min(max(m, 2), 16) - 2) * (55000.0 - 25000.0) / 14.0
     return cycles / 1.5 / 1000.0
