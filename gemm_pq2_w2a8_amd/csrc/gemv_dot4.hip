@@ -3,8 +3,8 @@
 // Algorithm (page "Making a ternary reasoning model fast in vLLM", section
 // "One token at a time: plain Triton is enough"): activations are in plane
 // order, so plane s of a 32-bit code word -- the 2-bit fields at bits 2s of
-// its four bytes -- lines up with four consecutive activation bytes and one
-// int8 dot4 consumes them with no decode step; the -1 offset of the ternary
+// its four bytes -- pairs with four adjacent plane-order activation bytes, and
+// one int8 dot4 takes both with no decode step; the -1 offset of the ternary
 // code is one subtraction of sum(q) per 128-weight group; the group dot is
 // then scaled by s[g] * ws[n][g] in float32 and summed over groups. The page
 // also found independent dot4 accumulators and a one-stage loop best for one

@@ -3,9 +3,10 @@
 // Plane dot products become arithmetic-bound from about three tokens (page
 // "Making a ternary reasoning model fast in vLLM", section "One token at a
 // time", last paragraph); the small-batch path instead places code bytes
-// directly in the matrix-instruction operand registers and extracts each
-// plane with a shift and a mask (section "Small batches: make the register
-// layout explicit"), and loads every weight once for all token rows.
+// directly in the matrix-instruction operand registers, where a shift and a
+// mask per register pull one 2-bit plane out (section "Small batches: make
+// the register layout explicit"), and loads every weight once for all token
+// rows.
 //
 // gfx950 mapping (v_mfma_i32_16x16x64_i8, tokens padded to 16):
 //  * A block owns 16*TILES weight rows and all tokens; its NW waves split the
