@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpq2.so")
 
 GROUP = 128
 PATH_AUTO, PATH_GEMV, PATH_SMALL, PATH_PREFILL, PATH_PANEL = 0, 1, 2, 3, 4
+ACT_BF16, ACT_F16 = 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python gemm_pq2_w2a8_amd/build.py`")
@@ -35,6 +36,8 @@ lib.pq2_status_str.restype = ctypes.c_char_p
 lib.pq2_status_str.argtypes = [ctypes.c_int]
 lib.pq2_quantize_act.restype = ctypes.c_int
 lib.pq2_quantize_act.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
+lib.pq2_quantize_act_16.restype = ctypes.c_int
+lib.pq2_quantize_act_16.argtypes = [_P, ctypes.c_int, _P, _P, _P, _I64, _I64, _P]
 lib.pq2_gemm.restype = ctypes.c_int
 lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.pq2_gemm_kernel_path.restype = ctypes.c_int
@@ -105,13 +108,20 @@ def _mk(x: torch.Tensor) -> Tuple[int, int]:
 
 def pq2_quantize_act(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, t: torch.Tensor,
                      stream=None) -> None:
-    """x float32 [M][K] -> q int8 [M][K] (plane order), s float32 [M][G], t int32 [M][G]."""
+    """x float32, bfloat16 or float16 [M][K] -> q int8 [M][K] (plane order),
+    s float32 [M][G], t int32 [M][G]; 16-bit x is widened exactly first."""
     M, K = _mk(x)
     G = K // GROUP
-    _need(x, "x", torch.float32, (M, K))
     _need(q, "q", torch.int8, (M, K))
     _need(s, "s", torch.float32, (M, G))
     _need(t, "t", torch.int32, (M, G))
+    if x.dtype in (torch.bfloat16, torch.float16):
+        _need(x, "x", x.dtype, (M, K))
+        fmt = ACT_BF16 if x.dtype == torch.bfloat16 else ACT_F16
+        _check(lib.pq2_quantize_act_16(x.data_ptr(), fmt, q.data_ptr(), s.data_ptr(),
+                                       t.data_ptr(), M, K, _stream(x, stream)))
+        return
+    _need(x, "x", torch.float32, (M, K))
     _check(lib.pq2_quantize_act(x.data_ptr(), q.data_ptr(), s.data_ptr(), t.data_ptr(), M, K,
                                 _stream(x, stream)))
 
@@ -198,12 +208,13 @@ def quantize_act(x: torch.Tensor, stream=None):
 
 def linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor,
            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Whole path, y float32 [M][N]: one pq2_linear launch for M <= LINEAR_MAX_M,
-    else pq2_quantize_act into torch-allocated q/s/t followed by pq2_gemm."""
+    """Whole path, y float32 [M][N]: one pq2_linear launch for float32 x with
+    M <= LINEAR_MAX_M, else pq2_quantize_act (float32, bfloat16 or float16 x)
+    into torch-allocated q/s/t followed by pq2_gemm."""
     M = int(x.shape[0])
     N = int(codes.shape[0])
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
-    if M <= LINEAR_MAX_M:
+    if M <= LINEAR_MAX_M and x.dtype == torch.float32:
         pq2_linear(x, codes, wscale, y, stream)
         return y
     q, s, t = quantize_act(x, stream)

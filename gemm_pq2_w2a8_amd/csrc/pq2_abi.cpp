@@ -88,7 +88,7 @@ const char *pq2_status_str(int status) {
         case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128, K <= 2^24";
         case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
         case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
-        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M, or M too large for pq2_linear";
+        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M, M too large for pq2_linear, or unknown activation format";
         default: return "PQ2 unknown status";
     }
 }
@@ -100,7 +100,19 @@ pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t, int
     if (st != PQ2_OK) return st;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 4) || !aligned(t, 4))
         return PQ2_ERR_ALIGN;
-    return from_hip(pq2::launch_quantize(x, q, s, t, M, K, static_cast<hipStream_t>(hip_stream)));
+    return from_hip(pq2::launch_quantize(x, 0, q, s, t, M, K, static_cast<hipStream_t>(hip_stream)));
+}
+
+pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float *s, int32_t *t,
+                               int64_t M, int64_t K, void *hip_stream) {
+    if (!x || !q || !s || !t) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, 1, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(x, 8) || !aligned(q, 16) || !aligned(s, 4) || !aligned(t, 4))
+        return PQ2_ERR_ALIGN;
+    if (x_format != PQ2_ACT_BF16 && x_format != PQ2_ACT_F16) return PQ2_ERR_ARG;
+    return from_hip(pq2::launch_quantize(x, x_format, q, s, t, M, K,
+                                         static_cast<hipStream_t>(hip_stream)));
 }
 
 pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,

@@ -16,8 +16,9 @@ struct GemmOut {
     const uint16_t *ws;  // [N][G], unused when d is set
 };
 
-hipError_t launch_quantize(const float *x, int8_t *q, float *s, int32_t *t, int64_t M,
-                           int64_t K, hipStream_t stream);
+// format 0: float32 x; 1: bfloat16; 2: IEEE binary16 (each widened exactly).
+hipError_t launch_quantize(const void *x, int format, int8_t *q, float *s, int32_t *t,
+                           int64_t M, int64_t K, hipStream_t stream);
 
 // The dot4 GEMV runs 1 to kGemvMaxM token rows.
 constexpr int64_t kGemvMaxM = 4;

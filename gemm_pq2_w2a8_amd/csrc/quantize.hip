@@ -24,8 +24,31 @@ namespace {
 constexpr int kQuantThreads = 256;
 constexpr int kGroupsPerBlock = kQuantThreads / 32;
 
+// Four activations of one lane as float32: float32 input as is; bfloat16 and
+// binary16 input (FMT 1, 2) widened exactly, so the quantisation is that of
+// the float32 values they represent.
+template <int FMT>
+__device__ __forceinline__ float4 load4(const void *x, int64_t i) {
+    if constexpr (FMT == 0) {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + i);
+    } else {
+        const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + i);
+        const uint32_t h[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (FMT == 1)
+                f[e] = __builtin_bit_cast(float, h[e] << 16);
+            else
+                f[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)h[e]);
+        }
+        return make_float4(f[0], f[1], f[2], f[3]);
+    }
+}
+
+template <int FMT>
 __global__ __launch_bounds__(kQuantThreads) void quantize_plane_kernel(
-    const float *__restrict__ x, int8_t *__restrict__ q, float *__restrict__ s,
+    const void *__restrict__ x, int8_t *__restrict__ q, float *__restrict__ s,
     int32_t *__restrict__ t, int64_t MG, int64_t G, int64_t K) {
     const int lane32 = threadIdx.x & 31;
     const int64_t grp = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 5);
@@ -35,7 +58,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_plane_kernel(
     const int64_t g = gg - m * G;
     const int64_t base = m * K + g * kGroup;
 
-    const float4 v[1] = {*reinterpret_cast<const float4 *>(x + base + 4 * lane32)};
+    const float4 v[1] = {load4<FMT>(x, base + 4 * lane32)};
     uint32_t word[1];
     float sc[1];
     int sum[1];
@@ -53,13 +76,20 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_plane_kernel(
 
 }  // namespace
 
-hipError_t launch_quantize(const float *x, int8_t *q, float *s, int32_t *t, int64_t M,
-                           int64_t K, hipStream_t stream) {
+hipError_t launch_quantize(const void *x, int format, int8_t *q, float *s, int32_t *t,
+                           int64_t M, int64_t K, hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t MG = M * G;
     const int64_t blocks = (MG + kGroupsPerBlock - 1) / kGroupsPerBlock;
-    hipLaunchKernelGGL(quantize_plane_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0,
-                       stream, x, q, s, t, MG, G, K);
+    if (format == 1)
+        hipLaunchKernelGGL(quantize_plane_kernel<1>, dim3((unsigned)blocks), dim3(kQuantThreads),
+                           0, stream, x, q, s, t, MG, G, K);
+    else if (format == 2)
+        hipLaunchKernelGGL(quantize_plane_kernel<2>, dim3((unsigned)blocks), dim3(kQuantThreads),
+                           0, stream, x, q, s, t, MG, G, K);
+    else
+        hipLaunchKernelGGL(quantize_plane_kernel<0>, dim3((unsigned)blocks), dim3(kQuantThreads),
+                           0, stream, x, q, s, t, MG, G, K);
     return hipGetLastError();
 }
 

@@ -41,8 +41,9 @@
  *                PQ2_MAX_DIM, or K above PQ2_MAX_K (the kernels address a
  *                block's rows with 32-bit offsets);
  *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above;
- *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), or M above
- *                PQ2_LINEAR_MAX_M (pq2_linear);
+ *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), M above
+ *                PQ2_LINEAR_MAX_M (pq2_linear), or an unknown activation
+ *                format (pq2_quantize_act_16);
  *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
  * Nothing is enqueued when a status other than PQ2_OK is returned, except for
  * PQ2_ERR_HIP. A fault during execution surfaces at the caller's next
@@ -99,6 +100,23 @@ const char *pq2_status_str(int status);
  */
 pq2_status pq2_quantize_act(const float *x, int8_t *q, float *s, int32_t *t,
                             int64_t M, int64_t K, void *hip_stream);
+
+/*
+ * pq2_quantize_act for 16-bit activations, as a model running in bfloat16 or
+ * float16 holds them (the pages' projections take the activation dtype; see
+ * the page "Making a ternary reasoning model fast in vLLM", section "Prompt
+ * processing: check configuration and launch costs", for the quantiser's
+ * place in the step). Every element is first widened exactly to float32
+ * (bfloat16: its bits are the upper half of the float32's; binary16: the IEEE
+ * conversion, subnormals included), then quantised by the rule above, so q,
+ * s and t are those pq2_quantize_act gives for the widened x.
+ *   x_format  PQ2_ACT_BF16 or PQ2_ACT_F16 (else PQ2_ERR_ARG);
+ *   x         uint16 bit patterns [M][K], 8-byte aligned; q, s, t as above.
+ */
+#define PQ2_ACT_BF16 1
+#define PQ2_ACT_F16 2
+pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float *s, int32_t *t,
+                               int64_t M, int64_t K, void *hip_stream);
 
 /*
  * y = the PQ2_0 product defined above. The kernel depends on M:

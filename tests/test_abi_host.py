@@ -73,6 +73,19 @@ def test_gemm_validation():
     assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
 
 
+def test_quantize_16bit_validation():
+    f = pq2.lib.pq2_quantize_act_16
+    BF, F16 = pq2.ACT_BF16, pq2.ACT_F16
+    assert f(None, BF, P, P, P, 1, 128, None) == ERR_NULL
+    assert f(P, F16, P, None, P, 1, 128, None) == ERR_NULL
+    assert f(P, BF, P, P, P, 0, 128, None) == ERR_SHAPE
+    assert f(P, BF, P, P, P, 1, 200, None) == ERR_SHAPE
+    assert f(P + 4, BF, P, P, P, 1, 128, None) == ERR_ALIGN      # x needs 8 B
+    assert f(P, F16, P + 8, P, P, 1, 128, None) == ERR_ALIGN     # q needs 16 B
+    assert f(P, 0, P, P, P, 1, 128, None) == ERR_ARG              # float32 goes to pq2_quantize_act
+    assert f(P, 3, P, P, P, 1, 128, None) == ERR_ARG
+
+
 def test_linear_validation():
     f = pq2.lib.pq2_linear
     assert f(None, P, P, P, 1, 8, 128, None) == ERR_NULL

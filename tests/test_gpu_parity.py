@@ -104,6 +104,38 @@ def test_quantize_bitexact(pq2, case):
 
 # ---------------------------------------------------------------- exact group dots
 
+def edge_rows_16(dtype):
+    """Values a 16-bit activation can hold at the ends of its range."""
+    x = np.zeros((3, 384), np.float32)
+    if dtype == torch.float16:
+        x[0, 0:6] = [6e-8, -6e-8, 65504.0, -65504.0, 1e-5, 0.5]    # subnormal, max, tie-prone
+        x[1, 128:256] = np.float32(6e-8) * np.arange(128)         # a group of subnormals
+    else:
+        x[0, 0:4] = [3.0e38, -3.0e38, 1e-38, 126.5]
+        x[1, 128:256] = np.float32(1e-30) * np.arange(128)
+    x[2, :] = np.sin(np.arange(384, dtype=np.float32)) * 1000
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("case", ["decode", "small_outliers", "ragged", "edge"])
+def test_quantize_16bit_bitexact(pq2, dtype, case):
+    """bfloat16 / float16 activations: q, s, t bit for bit those the oracle gives
+    for the same values widened to float32 (the widening is exact)."""
+    print(f"quantize 16-bit {dtype} {case}", flush=True)
+    if case == "edge":
+        xf = edge_rows_16(dtype)
+    else:
+        xf = QUANT_CASES[case]()
+    x16 = torch.from_numpy(xf).to(dtype)
+    xw = x16.float().numpy()                      # exact widening, on the CPU
+    q, s, t = pq2.quantize_act(x16.cuda())
+    qo, so, to = oracle.quantize(xw)
+    np.testing.assert_array_equal(host(q), oracle.plane_order(qo))
+    np.testing.assert_array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    np.testing.assert_array_equal(host(t), to)
+
+
 GEMV_SHAPES = [(1, 128), (7, 384), (64, 512), (300, 640), (33, 2048), (130, 5120), (257, 6144),
                (65, 8192)]
 
