@@ -14,6 +14,9 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 pq2_status check_mnk(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || K < PQ2_GROUP || K % PQ2_GROUP != 0) return PQ2_ERR_SHAPE;
     if (M > PQ2_MAX_DIM || N > PQ2_MAX_DIM || K > PQ2_MAX_K) return PQ2_ERR_SHAPE;
+    // no buffer beyond 2^40 elements (every grid then stays below 2^31 blocks)
+    if (M * N > PQ2_MAX_ELEMS || M * K > PQ2_MAX_ELEMS || N * (K / 4) > PQ2_MAX_ELEMS)
+        return PQ2_ERR_SHAPE;
     return PQ2_OK;
 }
 

@@ -38,8 +38,10 @@
  * ERRORS: arguments are validated on the host before anything is enqueued:
  *  PQ2_ERR_NULL  a required pointer is NULL;
  *  PQ2_ERR_SHAPE M < 1, N < 1, K < 128, K % 128 != 0, M or N above
- *                PQ2_MAX_DIM, or K above PQ2_MAX_K (the kernels address a
- *                block's rows with 32-bit offsets);
+ *                PQ2_MAX_DIM, K above PQ2_MAX_K (the kernels address a
+ *                block's rows with 32-bit offsets), or M*N, M*K or N*K/4
+ *                above PQ2_MAX_ELEMS (larger than any device memory; keeps
+ *                every launch grid below 2^31 blocks);
  *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above;
  *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), M above
  *                PQ2_LINEAR_MAX_M (pq2_linear), or an unknown activation
@@ -62,6 +64,7 @@ extern "C" {
 #define PQ2_GROUP 128
 #define PQ2_MAX_DIM (1LL << 30)
 #define PQ2_MAX_K (1LL << 24)
+#define PQ2_MAX_ELEMS (1LL << 40)
 
 typedef enum {
     PQ2_OK = 0,

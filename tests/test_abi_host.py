@@ -68,6 +68,9 @@ def test_gemm_validation():
     assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
     assert f(P, P, P, P, P, P, 1, 8, (1 << 24) + 128, None) == ERR_SHAPE
     assert f(P, P, P, P, P, P, 1, (1 << 30) + 1, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1 << 30, 1 << 30, 128, None) == ERR_SHAPE        # M*N > 2^40
+    assert f(P, P, P, P, P, P, 1 << 20, 8, 1 << 21, None) == ERR_SHAPE         # M*K > 2^40
+    assert f(P, P, P, P, P, P, 1, 1 << 30, 1 << 14, None) == ERR_SHAPE         # N*K/4 > 2^40
     assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
     assert f(P, P, P, P, P + 1, P, 1, 8, 128, None) == ERR_ALIGN   # wscale needs 2 B
     assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
