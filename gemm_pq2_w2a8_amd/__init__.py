@@ -40,6 +40,8 @@ lib.pq2_quantize_act_16.restype = ctypes.c_int
 lib.pq2_quantize_act_16.argtypes = [_P, ctypes.c_int, _P, _P, _P, _I64, _I64, _P]
 lib.pq2_gemm.restype = ctypes.c_int
 lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.pq2_gemm_bf16.restype = ctypes.c_int
+lib.pq2_gemm_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.pq2_gemm_kernel_path.restype = ctypes.c_int
 lib.pq2_gemm_kernel_path.argtypes = [_I64, _I64, _I64]
 lib.pq2_gemm_path.restype = ctypes.c_int
@@ -128,7 +130,8 @@ def pq2_quantize_act(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, t: torch
 
 def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
              wscale: torch.Tensor, y: torch.Tensor, stream=None) -> None:
-    """y float32 [M][N] = PQ2_0 product of plane-order q/s/t and codes/wscale."""
+    """y [M][N] = PQ2_0 product of plane-order q/s/t and codes/wscale; y float32,
+    or bfloat16 (pq2_gemm_bf16: the float32 result rounded to nearest-even)."""
     M, K = _mk(q)
     N = int(codes.shape[0])
     G = K // GROUP
@@ -139,6 +142,11 @@ def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Ten
     if wscale.dtype == torch.float16:
         wscale = wscale.view(torch.int16)
     _need(wscale, "wscale", torch.int16, (N, G))
+    if y.dtype == torch.bfloat16:
+        _need(y, "y", torch.bfloat16, (M, N))
+        _check(lib.pq2_gemm_bf16(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
+                                 wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
+        return
     _need(y, "y", torch.float32, (M, N))
     _check(lib.pq2_gemm(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
                         wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))

@@ -94,11 +94,12 @@ struct GemvShape {
 // LDS bytes per group and token of a window: q (128), s (4), t (4).
 constexpr int64_t kLdsPerGroup = kGroup + 8;
 
-template <int LOG_CL, int RP, int MT, bool DOTS, bool FUSED>
+template <int LOG_CL, int RP, int MT, bool DOTS, bool FUSED, bool Y16>
 __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
     const float *__restrict__ x, const int8_t *__restrict__ q, const float *__restrict__ s,
     const int32_t *__restrict__ t, const uint8_t *__restrict__ codes,
-    const uint16_t *__restrict__ ws, float *__restrict__ y, int32_t *__restrict__ d, int64_t M,
+    const uint16_t *__restrict__ ws, float *__restrict__ y, uint16_t *__restrict__ y16,
+    int32_t *__restrict__ d, int64_t M,
     int64_t N, int64_t K, int64_t window) {
     static_assert(!(FUSED && DOTS), "the fused variant writes y");
     using S = GemvShape<LOG_CL, RP>;
@@ -355,7 +356,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const float v = segment_sum<CL>(facc[r][m]);
-                    if (cs == 0 && m < M && row < N) y[m * N + row] = v;
+                    if (cs == 0 && m < M && row < N) {
+                        if constexpr (Y16)
+                            y16[m * N + row] = bf16_rne(v);
+                        else
+                            y[m * N + row] = v;
+                    }
                     facc[r][m] = 0.0f;
                 }
             }
@@ -437,17 +443,21 @@ hipError_t launch_cfg(const float *x, const int8_t *q, const int32_t *t, const u
     const int64_t blocks = K <= window ? (n_rg < kPersistBlocks ? n_rg : kPersistBlocks) : n_rg;
     const size_t lds = (size_t)(MT * (window / kGroup) * kLdsPerGroup);
     if (x) {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, true>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, true, false>), dim3((unsigned)blocks),
                            dim3(kGemvThreads), lds, stream, x, nullptr, nullptr, nullptr, codes,
-                           out.ws, out.y, nullptr, M, N, K, window);
+                           out.ws, out.y, nullptr, nullptr, M, N, K, window);
     } else if (out.d) {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true, false>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true, false, false>), dim3((unsigned)blocks),
                            dim3(kGemvThreads), lds, stream, nullptr, q, nullptr, t, codes,
-                           nullptr, nullptr, out.d, M, N, K, window);
-    } else {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false>), dim3((unsigned)blocks),
+                           nullptr, nullptr, nullptr, out.d, M, N, K, window);
+    } else if (out.y16) {
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false, true>), dim3((unsigned)blocks),
                            dim3(kGemvThreads), lds, stream, nullptr, q, out.s, t, codes, out.ws,
-                           out.y, nullptr, M, N, K, window);
+                           nullptr, out.y16, nullptr, M, N, K, window);
+    } else {
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false, false>), dim3((unsigned)blocks),
+                           dim3(kGemvThreads), lds, stream, nullptr, q, out.s, t, codes, out.ws,
+                           out.y, nullptr, nullptr, M, N, K, window);
     }
     return hipGetLastError();
 }

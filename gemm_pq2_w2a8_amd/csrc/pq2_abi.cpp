@@ -131,6 +131,20 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uin
     return run_path(auto_path(M, N, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
 }
 
+pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
+                         const uint16_t *wscale, uint16_t *y, int64_t M, int64_t N, int64_t K,
+                         void *hip_stream) {
+    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, N, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
+        !aligned(wscale, 2) || !aligned(y, 2))
+        return PQ2_ERR_ALIGN;
+    pq2::GemmOut out{nullptr, nullptr, s, wscale};
+    out.y16 = y;
+    return run_path(auto_path(M, N, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+}
+
 int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K) {
     if (check_mnk(M, N, K) != PQ2_OK) return -1;
     return auto_path(M, N, K);

@@ -40,6 +40,21 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// float32 -> bfloat16 bits, rounded to nearest, ties to even (infinities and
+// NaN stay infinities and NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Output element i: float32 into y, or bfloat16 into y16 when that is given.
+__device__ __forceinline__ void store_y(float *y, uint16_t *y16, int64_t i, float v) {
+    if (y16)
+        y16[i] = bf16_rne(v);
+    else
+        y[i] = v;
+}
+
 // The four 2-bit planes of a code word as four int8x4 words (plane s holds
 // the codes at bits 2s..2s+1 of each byte, moved down to bits 0..1).
 __device__ __forceinline__ v4i planes_of(uint32_t w) {

@@ -14,6 +14,7 @@ struct GemmOut {
     int32_t *d;      // [M][N][G] or nullptr
     const float *s;  // [M][G], unused when d is set
     const uint16_t *ws;  // [N][G], unused when d is set
+    uint16_t *y16 = nullptr;  // bfloat16 [M][N] instead of y, when set
 };
 
 // format 0: float32 x; 1: bfloat16; 2: IEEE binary16 (each widened exactly).
@@ -59,7 +60,7 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
 // kept (nullptr if allocation fails); and y = sum over the chunks of
 // part[c][M*N], added in chunk order.
 float *split_workspace(size_t bytes, hipStream_t stream);
-hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
+hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t MN, int splits,
                             hipStream_t stream);
 
 // Blocks the tiled prefill kernel launches for M x N (its tile rule).

@@ -203,7 +203,7 @@ template <int WN, int WM, int WAVES_N, int WAVES_M, int DEPTH, bool DOTS>
 __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
+    uint16_t *__restrict__ y16, int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
     using C = PfCfg<WN, WM, WAVES_N, WAVES_M>;
     using Stage = typename C::Stage;
     using Scales = typename C::Scales;
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_mfma_kernel(
                 if (m < M) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (nb + i < N) y[m * N + nb + i] = acc[a][b][i];
+                        if (nb + i < N) store_y(y, y16, m * N + nb + i, acc[a][b][i]);
                 }
             }
         }
@@ -453,7 +453,7 @@ template <int WN, int WM, int WAVES_N, int WAVES_M, int R, bool DOTS>
 __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
+    uint16_t *__restrict__ y16, int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
     using C = PfCfg<WN, WM, WAVES_N, WAVES_M>;
     constexpr int T = C::kThreads;
     using L = PfRing<C::BN, C::BM, T, DOTS>;
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
                 if (m < M) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (nb + i < N) y[m * N + nb + i] = acc[a][b][i];
+                        if (nb + i < N) store_y(y, y16, m * N + nb + i, acc[a][b][i]);
                 }
             }
         }
@@ -698,13 +698,13 @@ hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *cod
         const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes + L::kSinkBytes;
         hipLaunchKernelGGL((prefill_ring_kernel<WN, WM, WAVES_N, WAVES_M, R, true>),
                            dim3((unsigned)blocks), dim3(C::kThreads), lds, stream, q, nullptr, t,
-                           codes, nullptr, nullptr, out.d, M, N, K);
+                           codes, nullptr, nullptr, nullptr, out.d, M, N, K);
     } else {
         using L = PfRing<C::BN, C::BM, C::kThreads, false>;
         const size_t lds = (size_t)R * L::kStageBytes + 2 * L::kScaleBytes + L::kSinkBytes;
         hipLaunchKernelGGL((prefill_ring_kernel<WN, WM, WAVES_N, WAVES_M, R, false>),
                            dim3((unsigned)blocks), dim3(C::kThreads), lds, stream, q, out.s, t,
-                           codes, out.ws, out.y, nullptr, M, N, K);
+                           codes, out.ws, out.y, out.y16, nullptr, M, N, K);
     }
     return hipGetLastError();
 }
@@ -718,11 +718,11 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
     if (out.d) {
         hipLaunchKernelGGL((prefill_mfma_kernel<WN, WM, WAVES_N, WAVES_M, DEPTH, true>),
                            dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, q, nullptr, t,
-                           codes, nullptr, nullptr, out.d, M, N, K);
+                           codes, nullptr, nullptr, nullptr, out.d, M, N, K);
     } else {
         hipLaunchKernelGGL((prefill_mfma_kernel<WN, WM, WAVES_N, WAVES_M, DEPTH, false>),
                            dim3((unsigned)blocks), dim3(C::kThreads), 0, stream, q, out.s, t,
-                           codes, out.ws, out.y, nullptr, M, N, K);
+                           codes, out.ws, out.y, out.y16, nullptr, M, N, K);
     }
     return hipGetLastError();
 }

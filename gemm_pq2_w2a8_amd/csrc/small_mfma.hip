@@ -55,6 +55,7 @@ template <int NW, int TILES, int GB, int PER, bool DOTS>
 __global__ __launch_bounds__(NW * kWave) void small_mfma_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
+    uint16_t *__restrict__ y16,
     int32_t *__restrict__ d, int64_t M, int64_t N, int64_t K) {
     extern __shared__ float sm[];
     constexpr int T = NW * kWave;      // threads per block
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(NW * kWave) void small_mfma_kernel(
                 float v = part[lane * 4 * TILES + 4 * ti + i];
                 for (int w = 1; w < NW; ++w) v += part[(w * kWave + lane) * 4 * TILES + 4 * ti + i];
                 const int64_t n = n0 + 16 * ti + 4 * lg + i;
-                if (mvalid && n < N) y[(int64_t)r * N + n] = v;
+                if (mvalid && n < N) store_y(y, y16, (int64_t)r * N + n, v);
             }
         }
     }
@@ -231,11 +232,11 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
     if (out.d) {
         hipLaunchKernelGGL((small_mfma_kernel<NW, TILES, GB, PER, true>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, nullptr, t, codes, nullptr, nullptr,
-                           out.d, M, N, K);
+                           nullptr, out.d, M, N, K);
     } else {
         hipLaunchKernelGGL((small_mfma_kernel<NW, TILES, GB, PER, false>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, M, N, K);
+                           out.y16, nullptr, M, N, K);
     }
     return hipGetLastError();
 }

@@ -76,7 +76,8 @@ template <int NW, int GS, int R, bool DOTS>
 __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M, int64_t N, int64_t K,
+    uint16_t *__restrict__ y16, int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M,
+    int64_t N, int64_t K,
     int gsplit, int bps) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int T = NW * kWave;
@@ -287,6 +288,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
     };
 
     float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
+    uint16_t *out16 = part_out ? nullptr : y16;   // partial sums stay float32
     auto reduce_tile = [&](int j) __attribute__((always_inline)) {
         if (!DOTS && tid < 256) {
             const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_kernel(
 #pragma unroll
             for (int w = 1; w < NW; ++w) v += pb[w * kWave * 4 + at];
             const int64_t n = n0 + cc;
-            if (m < M && n < N) out[(int64_t)m * N + n] = v;
+            if (m < M && n < N) store_y(out, out16, (int64_t)m * N + n, v);
         }
     };
 
@@ -342,7 +344,8 @@ template <int NW, int GSG, int CPT, int TT, bool DOTS>
 __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M, int64_t N, int64_t K,
+    uint16_t *__restrict__ y16, int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M,
+    int64_t N, int64_t K,
     int gsplit, int bps) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int T = NW * kWave;
@@ -546,6 +549,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
     };
 
     float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
+    uint16_t *out16 = part_out ? nullptr : y16;   // partial sums stay float32
     auto reduce_tile = [&](int j) __attribute__((always_inline)) {
         if (!DOTS) {
             const int64_t n0 = (int64_t)(bl + (int64_t)j * bps) * 16;
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_sc_kernel(
 #pragma unroll
                 for (int w = 1; w < KW; ++w) v += part[w * TT * kWave * 4 + at];
                 const int64_t m = 16 * u + ml, n = n0 + cc;
-                if (m < M && n < N) out[m * N + n] = v;
+                if (m < M && n < N) store_y(out, out16, m * N + n, v);
             }
         }
     };
@@ -624,7 +628,8 @@ template <int NW, int GSG, int CPT, bool DOTS>
 __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
-    int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M, int64_t N, int64_t K,
+    uint16_t *__restrict__ y16, int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M,
+    int64_t N, int64_t K,
     int gsplit, int bps) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     constexpr int T = NW * kWave;
@@ -802,6 +807,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
     };
 
     float *out = part_out ? part_out + (int64_t)sidx * M * N : y;
+    uint16_t *out16 = part_out ? nullptr : y16;   // partial sums stay float32
     // summing wave i (< 4) adds slot i of every lane's partials (token
     // 4 (lane / 16) + i, row lane % 16) in wave order; the reads go out
     // before the next tile's compute, the sum and store follow it
@@ -816,7 +822,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
 #pragma unroll
         for (int w = 1; w < NW; ++w) v += pv[w];
         const int64_t m = 4 * lg + wave, n = n0 + c;
-        if (m < M && n < N) out[m * N + n] = v;
+        if (m < M && n < N) store_y(out, out16, m * N + n, v);
     };
 
     static_assert(NW == 8, "four summing waves, one per partial slot");
@@ -848,13 +854,14 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
 
 // y = sum over the S chunks of part[s] (fixed order s = 0, 1, ...).
 __global__ __launch_bounds__(256) void panel_split_sum_kernel(const float *__restrict__ part,
-                                                              float *__restrict__ y, int64_t MN,
+                                                              float *__restrict__ y,
+                                                              uint16_t *__restrict__ y16, int64_t MN,
                                                               int S) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= MN) return;
     float v = part[i];
     for (int k = 1; k < S; ++k) v += part[(int64_t)k * MN + i];
-    y[i] = v;
+    store_y(y, y16, i, v);
 }
 
 struct DevLimits {
@@ -891,11 +898,11 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
     if (out.d) {
         hipLaunchKernelGGL((small_panel_kernel<NW, GS, R, true>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, nullptr, t, codes, nullptr, nullptr,
-                           out.d, nullptr, M, N, K, gsplit, bps);
+                           nullptr, out.d, nullptr, M, N, K, gsplit, bps);
     } else {
         hipLaunchKernelGGL((small_panel_kernel<NW, GS, R, false>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, part, M, N, K, gsplit, bps);
+                           out.y16, nullptr, part, M, N, K, gsplit, bps);
     }
     return hipGetLastError();
 }
@@ -934,11 +941,11 @@ hipError_t launch_sc_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes
     if (out.d) {
         hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, TT, true>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, nullptr, t, codes, nullptr, nullptr,
-                           out.d, nullptr, M, N, K, gsplit, bps);
+                           nullptr, out.d, nullptr, M, N, K, gsplit, bps);
     } else {
         hipLaunchKernelGGL((small_panel_sc_kernel<NW, GSG, CPT, TT, false>), dim3((unsigned)blocks),
                            dim3(NW * kWave), lds, stream, q, out.s, t, codes, out.ws, out.y,
-                           nullptr, part, M, N, K, gsplit, bps);
+                           out.y16, nullptr, part, M, N, K, gsplit, bps);
     }
     return hipGetLastError();
 }
@@ -973,7 +980,8 @@ hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *cod
     constexpr int CPT = GSG;     // 32 * 8 GSG code units over the 256 copy threads, NW = 8
     hipLaunchKernelGGL((small_panel_ring_kernel<NW, GSG, CPT, DOTS>), dim3((unsigned)blocks),
                        dim3(NW * kWave), lds, stream, q, DOTS ? nullptr : out.s, t, codes,
-                       DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y, out.d, part, M, N, K,
+                       DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y, DOTS ? nullptr : out.y16,
+                       out.d, part, M, N, K,
                        gsplit, bps);
     return hipGetLastError();
 }
@@ -1144,10 +1152,10 @@ float *split_workspace(size_t bytes, hipStream_t stream) {
     return static_cast<float *>(b.ptr);
 }
 
-hipError_t launch_split_sum(const float *part, float *y, int64_t MN, int splits,
+hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t MN, int splits,
                             hipStream_t stream) {
     hipLaunchKernelGGL(panel_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
-                       stream, part, y, MN, splits);
+                       stream, part, y, y16, MN, splits);
     return hipGetLastError();
 }
 
@@ -1206,7 +1214,7 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
         e = launch_gs<kPanelWaves, 2>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
                                       plan.bps, blocks, plan.lds, stream);
     if (e != hipSuccess || !part) return e;
-    return launch_split_sum(part, out.y, M * N, plan.S, stream);
+    return launch_split_sum(part, out.y, out.y16, M * N, plan.S, stream);
 }
 
 }  // namespace pq2

@@ -156,6 +156,21 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
                     int64_t M, int64_t N, int64_t K, void *hip_stream);
 
 /*
+ * pq2_gemm with a bfloat16 output, for callers whose activations are bfloat16
+ * (the pages' projections return the activation dtype; page "Making a ternary
+ * reasoning model fast in vLLM", section "One token at a time: plain Triton
+ * is enough"): the same kernels and the same float32 accumulation as
+ * pq2_gemm, each output rounded to nearest-even bfloat16 at its final store
+ * (split-K partial sums stay float32 until the summing launch), so y is
+ * exactly pq2_gemm's y rounded to bfloat16.
+ *   y  bfloat16 bit patterns [M][N], 2-byte aligned, overwritten.
+ * Everything else as for pq2_gemm.
+ */
+pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t,
+                         const uint8_t *codes, const uint16_t *wscale, uint16_t *y,
+                         int64_t M, int64_t N, int64_t K, void *hip_stream);
+
+/*
  * Quantise and multiply in one launch, for decode batches of 1 to 4 token
  * rows (PQ2_LINEAR_MAX_M): y = the PQ2_0 product of x quantised exactly as
  * pq2_quantize_act would (page "Making a ternary reasoning model fast in

@@ -76,6 +76,15 @@ def test_gemm_validation():
     assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
 
 
+def test_gemm_bf16_validation():
+    f = pq2.lib.pq2_gemm_bf16
+    assert f(None, P, P, P, P, P, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
+    assert f(P, P, P, P, P, P + 1, 1, 8, 128, None) == ERR_ALIGN   # y needs 2 B
+
+
 def test_quantize_16bit_validation():
     f = pq2.lib.pq2_quantize_act_16
     BF, F16 = pq2.ACT_BF16, pq2.ACT_F16

@@ -406,6 +406,28 @@ def test_graph_replay_with_spins(pq2):
             np.testing.assert_array_equal(host(b[-1]), ref[i])
 
 
+BF16_OUT = [(1, 300, 2048), (2, 5120, 6144), (4, 520, 2048), (5, 70, 2304), (16, 300, 17408),
+            (40, 200, 2048), (130, 260, 1024), (256, 8192, 1024), (300, 129, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", BF16_OUT)
+def test_gemm_bf16_output(pq2, M, N, K):
+    """pq2_gemm_bf16 on every kernel path (GEMV, 16-token kernel, panel with and
+    without split K, token tiles, tiled GEMM and its ring form): y is exactly
+    pq2_gemm's float32 y rounded to nearest-even bfloat16."""
+    print(f"gemm bf16 out M={M} N={N} K={K} path={pq2.gemm_kernel_path(M, N, K)}", flush=True)
+    x = synth.activations(M, K, M + N + K, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(N + 2 * K))
+    q, s, t = pq2.quantize_act(dev(x))
+    cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    pq2.pq2_gemm(q, s, t, cd, wd, y32)
+    pq2.pq2_gemm(q, s, t, cd, wd, y16)
+    ref = y32.cpu().to(torch.bfloat16).view(torch.int16).numpy()   # RNE on the CPU
+    np.testing.assert_array_equal(host(y16.view(torch.int16)), ref)
+
+
 def test_tiny_workload(pq2):
     wl = synth.tiny()
     w = synth.weights(wl.n, wl.k, 0)
