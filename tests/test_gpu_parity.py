@@ -428,6 +428,39 @@ def test_gemm_bf16_output(pq2, M, N, K):
     np.testing.assert_array_equal(host(y16.view(torch.int16)), ref)
 
 
+def random_shapes(seed, count=24, budget=1.5e9):
+    """Log-uniform M in [1, 300], N in [1, 3000], K = 128 g with g in [1, 160],
+    at most `budget` multiply-adds (the oracle's share), from a fixed seed."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        M = int(np.exp(rng.uniform(0, np.log(300))))
+        N = int(np.exp(rng.uniform(0, np.log(3000))))
+        K = 128 * int(rng.integers(1, 161))
+        if M * N * K <= budget:
+            out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(11))
+def test_random_shapes_auto_path(pq2, M, N, K):
+    """Seeded random shapes (single weight rows, single tokens, K up to 20480,
+    nothing a multiple of any tile) through pq2_gemm's own kernel choice: exact
+    group dots and y within tolerance."""
+    print(f"random M={M} N={N} K={K} path={pq2.gemm_kernel_path(M, N, K)}", flush=True)
+    x = synth.activations(M, K, M * 7 + N, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(N * 3 + K))
+    qo, so, to = oracle.quantize(x)
+    qd, td, cd = dev(oracle.plane_order(qo)), dev(to), dev(w.codes)
+    d = torch.empty((M, N, K // G), dtype=torch.int32, device="cuda")
+    pq2.pq2_gemm_group_dots(qd, td, cd, d)
+    np.testing.assert_array_equal(host(d), oracle.group_dots(qo, w.codes))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(qd, dev(so), td, cd, dev(w.wscale_bits.view(np.int16)), y)
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(host(y), yo, tabs) < TOL
+
+
 def test_tiny_workload(pq2):
     wl = synth.tiny()
     w = synth.weights(wl.n, wl.k, 0)
