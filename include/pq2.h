@@ -147,9 +147,11 @@ pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float
  * buffer of chunks * M * N floats (at most 16 chunks) that the library
  * allocates on first need, one per device and stream, grows when a larger
  * one is needed (hipFree of the old one waits for the device) and keeps
- * until the process ends. hipMalloc
- * makes such a first call unsafe under graph capture. A second small launch
- * sums the chunks in a fixed order. PQ2_ERR_HIP if it cannot allocate.
+ * until the process ends. hipMalloc makes such a first call unsafe under
+ * graph capture: one call of the same or a larger shape on the stream before
+ * capture creates the buffer, after which captured calls replay correctly.
+ * A second small launch sums the chunks in a fixed order. PQ2_ERR_HIP if it
+ * cannot allocate.
  */
 pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
                     const uint8_t *codes, const uint16_t *wscale, float *y,
