@@ -38,14 +38,18 @@ lib.pq2_quantize_act.restype = ctypes.c_int
 lib.pq2_quantize_act.argtypes = [_P, _P, _P, _P, _I64, _I64, _P]
 lib.pq2_quantize_act_16.restype = ctypes.c_int
 lib.pq2_quantize_act_16.argtypes = [_P, ctypes.c_int, _P, _P, _P, _I64, _I64, _P]
+_SZ = ctypes.c_size_t
+lib.pq2_gemm_workspace_bytes.restype = _SZ
+lib.pq2_gemm_workspace_bytes.argtypes = [_I64, _I64, _I64]
 lib.pq2_gemm.restype = ctypes.c_int
-lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 lib.pq2_gemm_bf16.restype = ctypes.c_int
-lib.pq2_gemm_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.pq2_gemm_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 lib.pq2_gemm_kernel_path.restype = ctypes.c_int
-lib.pq2_gemm_kernel_path.argtypes = [_I64, _I64, _I64]
+lib.pq2_gemm_kernel_path.argtypes = [_I64, _I64, _I64, _SZ]
 lib.pq2_gemm_path.restype = ctypes.c_int
-lib.pq2_gemm_path.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
+lib.pq2_gemm_path.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _SZ,
+                              _P]
 lib.pq2_gemm_group_dots.restype = ctypes.c_int
 lib.pq2_gemm_group_dots.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
 lib.pq2_linear.restype = ctypes.c_int
@@ -54,16 +58,26 @@ lib.pq2_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
 LINEAR_MAX_M = 4    # PQ2_LINEAR_MAX_M
 
 # Every extern "C" symbol declared in include/pq2.h.
-ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_gemm",
-               "pq2_gemm_kernel_path", "pq2_gemm_path", "pq2_linear", "pq2_gemm_group_dots")
+ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_quantize_act_16",
+               "pq2_gemm_workspace_bytes", "pq2_gemm", "pq2_gemm_bf16", "pq2_gemm_kernel_path",
+               "pq2_gemm_path", "pq2_linear", "pq2_gemm_group_dots")
 
 PATH_NAMES = {PATH_GEMV: "gemv_dot4", PATH_SMALL: "small_mfma", PATH_PREFILL: "prefill_mfma",
               PATH_PANEL: "small_panel"}
 
 
-def gemm_kernel_path(M: int, N: int, K: int) -> int:
-    """PATH_* that pq2_gemm takes for this shape on the current device (-1: bad shape)."""
-    return int(lib.pq2_gemm_kernel_path(M, N, K))
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes of pq2_gemm's fastest plan for this shape (0: none needed)."""
+    return int(lib.pq2_gemm_workspace_bytes(M, N, K))
+
+
+def gemm_kernel_path(M: int, N: int, K: int, workspace_bytes: Optional[int] = None) -> int:
+    """PATH_* that pq2_gemm takes for this shape on the current device given a
+    workspace of that many bytes (None: the size gemm_workspace_bytes asks
+    for); -1 for a bad shape."""
+    if workspace_bytes is None:
+        workspace_bytes = gemm_workspace_bytes(M, N, K)
+    return int(lib.pq2_gemm_kernel_path(M, N, K, int(workspace_bytes)))
 
 
 class PQ2Error(RuntimeError):
@@ -128,10 +142,38 @@ def pq2_quantize_act(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, t: torch
                                 _stream(x, stream)))
 
 
+def _workspace(workspace, M: int, N: int, K: int, device, stream) -> Tuple[int, int, object]:
+    """(pointer, bytes, keep-alive) of the split-K workspace argument: "auto"
+    allocates the size pq2_gemm_workspace_bytes asks for with torch (none when
+    0), None passes no workspace, a device tensor passes its storage. An
+    "auto" buffer is tied to the launch stream, so torch's allocator does not
+    hand it out again before the kernels on that stream are done with it."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be "auto", None or a device tensor')
+        n = gemm_workspace_bytes(M, N, K)
+        if n == 0:
+            return 0, 0, None
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        if stream is not None:
+            st = stream if isinstance(stream, torch.cuda.Stream) else \
+                torch.cuda.ExternalStream(int(stream), device=device)
+            workspace.record_stream(st)
+    if workspace is None:
+        return 0, 0, None
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a GPU tensor")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+
+
 def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
-             wscale: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+             wscale: torch.Tensor, y: torch.Tensor, workspace="auto", stream=None) -> None:
     """y [M][N] = PQ2_0 product of plane-order q/s/t and codes/wscale; y float32,
-    or bfloat16 (pq2_gemm_bf16: the float32 result rounded to nearest-even)."""
+    or bfloat16 (pq2_gemm_bf16: the float32 result rounded to nearest-even).
+    workspace: "auto" (torch allocates what the fastest plan needs), None (no
+    workspace: plans that do not split K) or a device tensor."""
     M, K = _mk(q)
     N = int(codes.shape[0])
     G = K // GROUP
@@ -142,19 +184,22 @@ def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Ten
     if wscale.dtype == torch.float16:
         wscale = wscale.view(torch.int16)
     _need(wscale, "wscale", torch.int16, (N, G))
+    wp, wn, _keep = _workspace(workspace, M, N, K, q.device, stream)
     if y.dtype == torch.bfloat16:
         _need(y, "y", torch.bfloat16, (M, N))
         _check(lib.pq2_gemm_bf16(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
-                                 wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
+                                 wscale.data_ptr(), y.data_ptr(), M, N, K, wp, wn,
+                                 _stream(q, stream)))
         return
     _need(y, "y", torch.float32, (M, N))
     _check(lib.pq2_gemm(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
-                        wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
+                        wscale.data_ptr(), y.data_ptr(), M, N, K, wp, wn, _stream(q, stream)))
 
 
 def pq2_gemm_path(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
-                  wscale: torch.Tensor, y: torch.Tensor, path: int, stream=None) -> None:
-    """pq2_gemm through the selected kernel path (PATH_*)."""
+                  wscale: torch.Tensor, y: torch.Tensor, path: int, workspace="auto",
+                  stream=None) -> None:
+    """pq2_gemm through the selected kernel path (PATH_*); workspace as for pq2_gemm."""
     M, K = _mk(q)
     N = int(codes.shape[0])
     G = K // GROUP
@@ -166,8 +211,9 @@ def pq2_gemm_path(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torc
         wscale = wscale.view(torch.int16)
     _need(wscale, "wscale", torch.int16, (N, G))
     _need(y, "y", torch.float32, (M, N))
+    wp, wn, _keep = _workspace(workspace, M, N, K, q.device, stream)
     _check(lib.pq2_gemm_path(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
-                             wscale.data_ptr(), y.data_ptr(), M, N, K, int(path),
+                             wscale.data_ptr(), y.data_ptr(), M, N, K, int(path), wp, wn,
                              _stream(q, stream)))
 
 
@@ -226,5 +272,5 @@ def linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor,
         pq2_linear(x, codes, wscale, y, stream)
         return y
     q, s, t = quantize_act(x, stream)
-    pq2_gemm(q, s, t, codes, wscale, y, stream)
+    pq2_gemm(q, s, t, codes, wscale, y, stream=stream)
     return y

@@ -1,6 +1,8 @@
 // pq2_abi.cpp -- the C ABI declared in include/pq2.h: host-side argument
 // validation and dispatch to the gfx950 kernels. Validation happens before
-// anything is enqueued; the library keeps no mutable state.
+// anything is enqueued; the library allocates nothing and keeps no mutable
+// state (the device-limit cache of the panel planner is written once per
+// device and read-only after that).
 #include "../../include/pq2.h"
 
 #include <hip/hip_runtime.h>
@@ -22,9 +24,21 @@ pq2_status check_mnk(int64_t M, int64_t N, int64_t K) {
 
 pq2_status from_hip(hipError_t e) { return e == hipSuccess ? PQ2_OK : PQ2_ERR_HIP; }
 
+// K chunks the caller's workspace allows the panel kernel: S chunks need
+// S * M * N float32 partial sums; no workspace means unsplit plans only.
+int splits_for_bytes(size_t work_bytes, int64_t M, int64_t N) {
+    const uint64_t per = (uint64_t)M * (uint64_t)N * sizeof(float);
+    const uint64_t s = work_bytes / per;
+    return s < 1 ? 1 : s > (uint64_t)pq2::kPanelMaxSplits ? pq2::kPanelMaxSplits : (int)s;
+}
+
+int max_splits(const void *work, size_t work_bytes, int64_t M, int64_t N) {
+    return work ? splits_for_bytes(work_bytes, M, N) : 1;
+}
+
 pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *codes,
-                    const pq2::GemmOut &out, int64_t M, int64_t N, int64_t K,
-                    hipStream_t stream) {
+                    const pq2::GemmOut &out, int64_t M, int64_t N, int64_t K, int max_s,
+                    float *work, hipStream_t stream) {
     switch (path) {
         case PQ2_PATH_GEMV:
             return from_hip(pq2::launch_gemv(q, t, codes, out, M, N, K, stream));
@@ -33,7 +47,8 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
         case PQ2_PATH_PREFILL:
             return from_hip(pq2::launch_prefill(q, t, codes, out, M, N, K, stream));
         case PQ2_PATH_PANEL:
-            return from_hip(pq2::launch_small_panel(q, t, codes, out, M, N, K, stream));
+            return from_hip(pq2::launch_small_panel(q, t, codes, out, M, N, K, max_s, work,
+                                                    stream));
         default:
             return PQ2_ERR_ARG;
     }
@@ -51,30 +66,50 @@ pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *
 // panel kernel in 2 or 4 token tiles wins where the tiled GEMM has fewer than
 // two blocks per CU (5120 x 6144 at M = 32: 12.9 us against 16.4; 5120 x
 // 17408: 23.0 against 46.1); with more the tiled GEMM wins (17408 x 5120 at
-// M = 32: 21.0 against 24.5).
-#ifndef PQ2_AUTO_OVERRIDE
-#define PQ2_AUTO_OVERRIDE
-#endif
-int auto_path(int64_t M, int64_t N, int64_t K) {
-    PQ2_AUTO_OVERRIDE
+// M = 32: 21.0 against 24.5). Plans that split K count only where the
+// caller's workspace holds their partial sums (max_s chunks).
+int auto_path(int64_t M, int64_t N, int64_t K, int max_s) {
     if (M <= 2) return PQ2_PATH_GEMV;
-    if (M <= 16 && pq2::small_panel_ring_fits(M, K)) return PQ2_PATH_PANEL;
+    if (M <= 16 && pq2::small_panel_ring_fits(M, K, max_s)) return PQ2_PATH_PANEL;
     const bool large = N * K > (int64_t(1) << 25);
-    if (M <= 16 && (large || M >= 8) && pq2::small_panel_fits(M, K)) return PQ2_PATH_PANEL;
+    if (M <= 16 && (large || M >= 8) && pq2::small_panel_fits(M, K, max_s)) return PQ2_PATH_PANEL;
     if (M <= pq2::kGemvMaxM && large) return PQ2_PATH_GEMV;
     if (M <= 16 && K <= pq2::kSmallMaxK) return PQ2_PATH_SMALL;
-    if (M <= pq2::kPanelMaxM && pq2::prefill_blocks(M, N) < 512 && pq2::small_panel_fits(M, K))
+    if (M <= pq2::kPanelMaxM && pq2::prefill_blocks(M, N) < 512 &&
+        pq2::small_panel_fits(M, K, max_s))
         return PQ2_PATH_PANEL;
     return PQ2_PATH_PREFILL;
 }
 
 // Resolves PQ2_PATH_AUTO and rejects a path that cannot run this shape.
-pq2_status resolve_path(int &path, int64_t M, int64_t N, int64_t K) {
-    if (path == PQ2_PATH_AUTO) path = auto_path(M, N, K);
+pq2_status resolve_path(int &path, int64_t M, int64_t N, int64_t K, int max_s) {
+    if (path == PQ2_PATH_AUTO) path = auto_path(M, N, K, max_s);
     if (path == PQ2_PATH_GEMV && M > pq2::kGemvMaxM) return PQ2_ERR_ARG;
     if (path == PQ2_PATH_SMALL && (M > 16 || K > pq2::kSmallMaxK)) return PQ2_ERR_ARG;
-    if (path == PQ2_PATH_PANEL && !pq2::small_panel_fits(M, K)) return PQ2_ERR_ARG;
+    if (path == PQ2_PATH_PANEL && !pq2::small_panel_fits(M, K, max_s)) return PQ2_ERR_ARG;
     if (path < PQ2_PATH_GEMV || path > PQ2_PATH_PANEL) return PQ2_ERR_ARG;
+    return PQ2_OK;
+}
+
+// Bytes of partial sums pq2_gemm's plan for this shape writes when the
+// workspace is large enough (0: its plan does not split K).
+size_t workspace_need(int64_t M, int64_t N, int64_t K) {
+    if (auto_path(M, N, K, pq2::kPanelMaxSplits) != PQ2_PATH_PANEL) return 0;
+    const int S = pq2::small_panel_splits(M, N, K, pq2::kPanelMaxSplits);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+// Checks shared by the GEMM entries (y: float32 needs 4-byte, bfloat16
+// 2-byte alignment; the workspace 16 bytes when given).
+pq2_status check_gemm(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
+                      const uint16_t *wscale, const void *y, uintptr_t y_align, const void *work,
+                      int64_t M, int64_t N, int64_t K) {
+    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
+    pq2_status st = check_mnk(M, N, K);
+    if (st != PQ2_OK) return st;
+    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
+        !aligned(wscale, 2) || !aligned(y, y_align) || (work && !aligned(work, 16)))
+        return PQ2_ERR_ALIGN;
     return PQ2_OK;
 }
 
@@ -91,7 +126,7 @@ const char *pq2_status_str(int status) {
         case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128, K <= 2^24";
         case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
         case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
-        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this M, M too large for pq2_linear, or unknown activation format";
+        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this shape and workspace, M too large for pq2_linear, or unknown activation format";
         default: return "PQ2 unknown status";
     }
 }
@@ -118,51 +153,50 @@ pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float
                                          static_cast<hipStream_t>(hip_stream)));
 }
 
+size_t pq2_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_mnk(M, N, K) != PQ2_OK) return 0;
+    return workspace_need(M, N, K);
+}
+
 pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
                     const uint16_t *wscale, float *y, int64_t M, int64_t N, int64_t K,
-                    void *hip_stream) {
-    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
-    pq2_status st = check_mnk(M, N, K);
+                    void *workspace, size_t workspace_bytes, void *hip_stream) {
+    pq2_status st = check_gemm(q, s, t, codes, wscale, y, 4, workspace, M, N, K);
     if (st != PQ2_OK) return st;
-    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
-        !aligned(wscale, 2) || !aligned(y, 4))
-        return PQ2_ERR_ALIGN;
+    const int max_s = max_splits(workspace, workspace_bytes, M, N);
     const pq2::GemmOut out{y, nullptr, s, wscale};
-    return run_path(auto_path(M, N, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+    return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s,
+                    static_cast<float *>(workspace), static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
                          const uint16_t *wscale, uint16_t *y, int64_t M, int64_t N, int64_t K,
-                         void *hip_stream) {
-    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
-    pq2_status st = check_mnk(M, N, K);
+                         void *workspace, size_t workspace_bytes, void *hip_stream) {
+    pq2_status st = check_gemm(q, s, t, codes, wscale, y, 2, workspace, M, N, K);
     if (st != PQ2_OK) return st;
-    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
-        !aligned(wscale, 2) || !aligned(y, 2))
-        return PQ2_ERR_ALIGN;
+    const int max_s = max_splits(workspace, workspace_bytes, M, N);
     pq2::GemmOut out{nullptr, nullptr, s, wscale};
     out.y16 = y;
-    return run_path(auto_path(M, N, K), q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+    return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s,
+                    static_cast<float *>(workspace), static_cast<hipStream_t>(hip_stream));
 }
 
-int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K) {
+int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K, size_t workspace_bytes) {
     if (check_mnk(M, N, K) != PQ2_OK) return -1;
-    return auto_path(M, N, K);
+    return auto_path(M, N, K, splits_for_bytes(workspace_bytes, M, N));
 }
 
 pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
                          const uint16_t *wscale, float *y, int64_t M, int64_t N, int64_t K,
-                         int path, void *hip_stream) {
-    if (!q || !s || !t || !codes || !wscale || !y) return PQ2_ERR_NULL;
-    pq2_status st = check_mnk(M, N, K);
+                         int path, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    pq2_status st = check_gemm(q, s, t, codes, wscale, y, 4, workspace, M, N, K);
     if (st != PQ2_OK) return st;
-    if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(s, 4) || !aligned(t, 4) ||
-        !aligned(wscale, 2) || !aligned(y, 4))
-        return PQ2_ERR_ALIGN;
-    st = resolve_path(path, M, N, K);
+    const int max_s = max_splits(workspace, workspace_bytes, M, N);
+    st = resolve_path(path, M, N, K, max_s);
     if (st != PQ2_OK) return st;
     const pq2::GemmOut out{y, nullptr, s, wscale};
-    return run_path(path, q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+    return run_path(path, q, t, codes, out, M, N, K, max_s, static_cast<float *>(workspace),
+                    static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
@@ -186,10 +220,13 @@ pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t 
     if (st != PQ2_OK) return st;
     if (!aligned(q, 16) || !aligned(codes, 16) || !aligned(t, 4) || !aligned(d, 4))
         return PQ2_ERR_ALIGN;
-    st = resolve_path(path, M, N, K);
+    // the exact dots of each K chunk go straight to d: no workspace needed,
+    // so every chunk count is open to the planner
+    st = resolve_path(path, M, N, K, pq2::kPanelMaxSplits);
     if (st != PQ2_OK) return st;
     const pq2::GemmOut out{nullptr, d, nullptr, nullptr};
-    return run_path(path, q, t, codes, out, M, N, K, static_cast<hipStream_t>(hip_stream));
+    return run_path(path, q, t, codes, out, M, N, K, pq2::kPanelMaxSplits, nullptr,
+                    static_cast<hipStream_t>(hip_stream));
 }
 
 }  // extern "C"

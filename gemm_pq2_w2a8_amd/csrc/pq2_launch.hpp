@@ -40,26 +40,30 @@ hipError_t launch_small(const int8_t *q, const int32_t *t, const uint8_t *codes,
 
 // The persistent small-batch kernel keeps the M x K activation panel (or a
 // K chunk of it) in LDS: K <= kPanelMaxK, K >= 16 * 128, M <= kPanelMaxM,
-// and a split of K into at most 16 chunks whose panel plus tables fit the
-// device's LDS per block (small_panel_fits checks all of it).
+// and a split of K into at most kPanelMaxSplits chunks whose panel plus
+// tables fit the device's LDS per block (small_panel_fits checks all of it).
+// A split into S > 1 chunks writes S * M * N float32 partial sums to a
+// caller-owned workspace, so every planner takes the largest chunk count
+// the caller's workspace allows (max_splits >= 1; 1 = unsplit only).
 constexpr int64_t kPanelMaxK = 18432;
 constexpr int64_t kPanelMaxM = 64;
+constexpr int kPanelMaxSplits = 16;
 
-bool small_panel_fits(int64_t M, int64_t K);
+bool small_panel_fits(int64_t M, int64_t K, int max_splits);
 // Whether the panel kernel runs its ring variant (A fragments resident in
 // VGPRs, codes through an LDS ring): M <= 16 and K chunks of whole multiples
 // of 8 groups within the LDS bound.
-bool small_panel_ring_fits(int64_t M, int64_t K);
+bool small_panel_ring_fits(int64_t M, int64_t K, int max_splits);
+// K chunks of the plan launch_small_panel takes (0: none fits).
+int small_panel_splits(int64_t M, int64_t N, int64_t K, int max_splits);
 
+// work: device buffer of at least small_panel_splits(...) * M * N floats when
+// that is above 1 and out.d is not set (the chunks' partial sums), else unused.
 hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *codes,
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
-                              hipStream_t stream);
+                              int max_splits, float *work, hipStream_t stream);
 
-// Split-K support shared by the panel and prefill kernels: a device buffer
-// of at least `bytes`, one per (device, stream), allocated on first need and
-// kept (nullptr if allocation fails); and y = sum over the chunks of
-// part[c][M*N], added in chunk order.
-float *split_workspace(size_t bytes, hipStream_t stream);
+// y = sum over the chunks of part[c][M*N], added in chunk order.
 hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t MN, int splits,
                             hipStream_t stream);
 

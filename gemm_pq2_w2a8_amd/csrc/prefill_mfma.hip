@@ -44,10 +44,6 @@ namespace pq2 {
 
 namespace {
 
-#ifndef PREFILL_TUNE_OVERRIDE
-#define PREFILL_TUNE_OVERRIDE
-#endif
-
 constexpr int kCodeStride = 48;          // LDS bytes per code row (32 + pad)
 constexpr int kQStride = 144;            // LDS bytes per token row (128 + pad)
 constexpr int kNumXcd = 8;
@@ -731,11 +727,6 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 
 // Tile configurations (rows x tokens, waves, prefetch depth):
 //   0: 128 x 128, 2 x 2 waves of 64 x 64, depth 1
-//   1: 128 x 128, 4 x 1 waves of 32 x 128, depth 1
-//   2: 128 x 128, 2 x 2 waves of 64 x 64, depth 2
-//   3:  64 x 128, 2 x 2 waves of 32 x 64, depth 2
-//   4:  32 x 128, 2 x 2 waves of 16 x 64, depth 2
-//   5: 128 x 64,  2 x 2 waves of 64 x 32, depth 2
 //   6: 128 x 128, 2 x 2 waves of 64 x 64, ring of 2 stages (buffer -> LDS copies)
 //   7:  64 x 64,  2 x 2 waves of 32 x 32, depth 2
 //   8:  64 x 64,  2 x 2 waves of 32 x 32, ring of 2 stages
@@ -774,17 +765,10 @@ hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *code
     // forms of the 32 x 32, 64 x 128 tiles and a 3-stage 64 x 64 ring were
     // slower.
     const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
-    int cfg = tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
-            : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
-                                          : 9;
-    PREFILL_TUNE_OVERRIDE
-    if ((cfg == 6 || cfg == 8) && !ring) cfg = cfg == 6 ? 0 : 7;
+    const int cfg = tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
+                  : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
+                                                : 9;
     switch (cfg) {
-        case 1: return launch_cfg<2, 8, 4, 1, 1>(q, t, codes, out, M, N, K, stream);
-        case 2: return launch_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
-        case 3: return launch_cfg<2, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
-        case 4: return launch_cfg<1, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
-        case 5: return launch_cfg<4, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 6: return launch_ring_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 7: return launch_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 8: return launch_ring_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);

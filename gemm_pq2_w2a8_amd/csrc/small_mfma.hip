@@ -38,10 +38,6 @@ namespace pq2 {
 
 namespace {
 
-#ifndef SMALL_TUNE_OVERRIDE
-#define SMALL_TUNE_OVERRIDE
-#endif
-
 // LDS words: weight scales [16*TILES][GP], token s and t [16][GP] (GP = G + 1,
 // odd, so the 16 lanes of a lane group read 16 different rows without bank
 // conflicts); reused for the wave partials [NW][64][4*TILES] after compute.
@@ -289,7 +285,6 @@ hipError_t launch_small(const int8_t *q, const int32_t *t, const uint8_t *codes,
     while (tiles > 1 && small_lds_words((int)G, tiles, 8) * 4 > 65536) tiles /= 2;
     while (nw > 1 && nw > G) nw /= 2;
     while (nw * 1024 < 16 * tiles * G) nw *= 2;
-    SMALL_TUNE_OVERRIDE
     if (tiles == 2) return launch_tiles<2>(nw, q, t, codes, out, M, N, K, stream);
     return launch_tiles<1>(nw, q, t, codes, out, M, N, K, stream);
 }

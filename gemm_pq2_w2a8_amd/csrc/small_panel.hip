@@ -44,18 +44,12 @@
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
-#include <map>
 #include <type_traits>
 #include <mutex>
-#include <utility>
 
 namespace pq2 {
 
 namespace {
-
-#ifndef PANEL_TUNE_OVERRIDE
-#define PANEL_TUNE_OVERRIDE
-#endif
 
 constexpr int kPanelPad = 16;       // LDS row stride of the panel: K + 16 bytes
 
@@ -1009,7 +1003,6 @@ hipError_t launch_ring(int64_t gs, const int8_t *q, const int32_t *t, const uint
 }
 
 constexpr int kPanelWaves = 8;
-constexpr int kPanelMaxSplits = 16;
 constexpr int kPanelMaxGs = 9;
 
 // 16-token tiles of the staged-codes kernel: 1, 2 or 4 (M <= 16, 32, 64;
@@ -1068,15 +1061,15 @@ PanelPlan plan_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits &l, b
 // tile count saves), K = 17408 in three chunks (14.3-15.8 us against 15.6-17.4
 // for two or four, 17.0 unsplit where it fits). The count nearest to G / 48
 // that fits, preferring more chunks.
-PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s,
+PanelPlan plan_panel(int64_t M, int64_t N, int64_t K, const DevLimits &l, int max_splits,
                      bool sc) {
     PanelPlan none;
-    if (l.cus <= 0 || M < 1 || M > (sc ? kPanelMaxM : 16)) return none;
-    if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_for(force_s, M, N, K, l, sc) : none;
+    if (l.cus <= 0 || M < 1 || M > (sc ? kPanelMaxM : 16) || max_splits < 1) return none;
+    const int cap = max_splits < kPanelMaxSplits ? max_splits : kPanelMaxSplits;
     const int64_t G = K / kGroup;
     int target = (int)((G + 24) / 48);
-    target = target < 1 ? 1 : target > kPanelMaxSplits ? kPanelMaxSplits : target;
-    for (int S = target; S <= kPanelMaxSplits; ++S) {
+    target = target < 1 ? 1 : target > cap ? cap : target;
+    for (int S = target; S <= cap; ++S) {
         const PanelPlan p = plan_for(S, M, N, K, l, sc);
         if (p.S) return p;
     }
@@ -1111,14 +1104,14 @@ PanelPlan plan_ring_for(int S, int64_t M, int64_t N, int64_t K, const DevLimits 
     return p;
 }
 
-PanelPlan plan_ring(int64_t M, int64_t N, int64_t K, const DevLimits &l, int force_s) {
+PanelPlan plan_ring(int64_t M, int64_t N, int64_t K, const DevLimits &l, int max_splits) {
     PanelPlan none;
-    if (l.cus <= 0 || M < 1 || M > 16) return none;
-    if (force_s > 0) return force_s <= kPanelMaxSplits ? plan_ring_for(force_s, M, N, K, l) : none;
+    if (l.cus <= 0 || M < 1 || M > 16 || max_splits < 1) return none;
+    const int cap = max_splits < kPanelMaxSplits ? max_splits : kPanelMaxSplits;
     const int64_t G = K / kGroup;
     int target = (int)((G + 24) / 48);
-    target = target < 1 ? 1 : target > kPanelMaxSplits ? kPanelMaxSplits : target;
-    for (int S = target; S <= kPanelMaxSplits; ++S) {
+    target = target < 1 ? 1 : target > cap ? cap : target;
+    for (int S = target; S <= cap; ++S) {
         const PanelPlan p = plan_ring_for(S, M, N, K, l);
         if (p.S) return p;
     }
@@ -1127,31 +1120,6 @@ PanelPlan plan_ring(int64_t M, int64_t N, int64_t K, const DevLimits &l, int for
 
 }  // namespace
 
-// Device workspace for split partials, one per (device, stream): work on one
-// stream is ordered, so calls on different streams never share a buffer.
-// Grown on demand (hipFree of the old buffer waits for the device), kept
-// until the process ends.
-float *split_workspace(size_t bytes, hipStream_t stream) {
-    struct Buf {
-        void *ptr = nullptr;
-        size_t size = 0;
-    };
-    static std::mutex mu;
-    static std::map<std::pair<int, hipStream_t>, Buf> bufs;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    Buf &b = bufs[{dev, stream}];
-    if (b.size < bytes) {
-        if (b.ptr && hipFree(b.ptr) != hipSuccess) return nullptr;
-        b.ptr = nullptr;
-        b.size = 0;
-        if (hipMalloc(&b.ptr, bytes) != hipSuccess) return nullptr;
-        b.size = bytes;
-    }
-    return static_cast<float *>(b.ptr);
-}
-
 hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t MN, int splits,
                             hipStream_t stream) {
     hipLaunchKernelGGL(panel_split_sum_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0,
@@ -1159,15 +1127,48 @@ hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t 
     return hipGetLastError();
 }
 
-bool small_panel_ring_fits(int64_t M, int64_t K) {
+bool small_panel_ring_fits(int64_t M, int64_t K, int max_splits) {
     if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
-    return plan_ring(M, 16, K, dev_limits(), 0).S > 0;
+    return plan_ring(M, 16, K, dev_limits(), max_splits).S > 0;
 }
 
-bool small_panel_fits(int64_t M, int64_t K) {
+bool small_panel_fits(int64_t M, int64_t K, int max_splits) {
     if (M < 1 || M > kPanelMaxM || K > kPanelMaxK || K / kGroup < 16) return false;
     // M <= 16: the register-operand kernel's plan (the fallback) must exist
-    return plan_panel(M, 16, K, dev_limits(), 0, M > 16).S > 0;
+    return plan_panel(M, 16, K, dev_limits(), max_splits, M > 16).S > 0;
+}
+
+namespace {
+
+// The plan launch_small_panel runs: the ring variant where it has a plan,
+// else the staged-codes kernel (MI355X sweeps: 2-14 % faster than the
+// register-operand kernel on five of the nine 5120 / 6144 / 17408 shapes at
+// M = 4, 8, 16, slower on one; one tile of register prefetch beat two on all
+// nine), else the register-operand kernel.
+enum class PanelKind { kNone, kRing, kStaged, kRegs };
+
+PanelPlan choose_panel(int64_t M, int64_t N, int64_t K, int max_splits, PanelKind &kind) {
+    const DevLimits l = dev_limits();
+    PanelPlan plan = plan_ring(M, N, K, l, max_splits);
+    kind = PanelKind::kRing;
+    if (plan.S == 0) {
+        plan = plan_panel(M, N, K, l, max_splits, true);
+        kind = PanelKind::kStaged;
+    }
+    if (plan.S == 0) {
+        plan = plan_panel(M, N, K, l, max_splits, false);
+        kind = PanelKind::kRegs;
+    }
+    if (plan.S == 0) kind = PanelKind::kNone;
+    return plan;
+}
+
+}  // namespace
+
+int small_panel_splits(int64_t M, int64_t N, int64_t K, int max_splits) {
+    if (!small_panel_fits(M, K, max_splits)) return 0;
+    PanelKind kind;
+    return choose_panel(M, N, K, max_splits, kind).S;
 }
 
 // One block of 8 waves per CU (two when two panels fit in a CU's LDS and K
@@ -1176,25 +1177,17 @@ bool small_panel_fits(int64_t M, int64_t K) {
 // 5120 / 6144 / 17408 shapes.
 hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *codes,
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
-                              hipStream_t stream) {
-    int force_s = 0;
-    // the staged-codes kernel when it has a plan (MI355X sweeps: 2-14 %
-    // faster than the register-operand kernel on five of the nine 5120 /
-    // 6144 / 17408 shapes at M = 4, 8, 16, slower on one; one tile of
-    // register prefetch beat two on all nine)
-    int staged = 1;
-    int ring = 1;
-    PANEL_TUNE_OVERRIDE
-    PanelPlan plan = ring ? plan_ring(M, N, K, dev_limits(), force_s) : PanelPlan();
-    const bool rg = plan.S != 0;
-    if (!rg) plan = plan_panel(M, N, K, dev_limits(), force_s, staged != 0);
-    const bool sc = !rg && staged != 0 && plan.S != 0;
-    if (!rg && !sc) plan = plan_panel(M, N, K, dev_limits(), force_s, false);
-    if (plan.S == 0) return hipErrorInvalidValue;
+                              int max_splits, float *work, hipStream_t stream) {
+    PanelKind kind;
+    const PanelPlan plan = choose_panel(M, N, K, max_splits, kind);
+    if (kind == PanelKind::kNone) return hipErrorInvalidValue;
+    const bool rg = kind == PanelKind::kRing, sc = kind == PanelKind::kStaged;
+    // the exact group dots go straight to d per chunk; float partials need
+    // the caller's workspace
     float *part = nullptr;
     if (plan.S > 1 && !out.d) {
-        part = split_workspace((size_t)plan.S * M * N * sizeof(float), stream);
-        if (!part) return hipErrorOutOfMemory;
+        if (!work) return hipErrorInvalidValue;
+        part = work;
     }
     const int64_t blocks = (int64_t)plan.bps * plan.S;
     hipError_t e;

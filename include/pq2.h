@@ -16,10 +16,12 @@
  *              = sum_{k in group g} (code[n][k] - 1) * q[m][k]
  *
  * G = K / 128. All arrays are dense and row-major, in device memory, owned
- * by the caller. Every call only enqueues kernels on the given stream (NULL =
- * the null stream) and never synchronises. The one allocation: pq2_gemm's
- * split-K workspace (see pq2_gemm), one buffer per device and stream, created
- * on first need. Inputs must not overlap outputs. Calls are thread-safe.
+ * by the caller, and so is the optional split-K workspace (see pq2_gemm).
+ * Every call only enqueues kernels on the given stream (NULL = the null
+ * stream); the library never allocates, frees or synchronises and keeps no
+ * mutable state (a per-device cache of device limits is filled once, under a
+ * lock, and only read after that), so calls are thread-safe and may be
+ * captured in HIP graphs. Inputs must not overlap outputs or the workspace.
  *
  * LAYOUTS (fixed):
  *  codes   uint8 [N][K/4]. The 2-bit code of weight k of row n (code c means
@@ -42,7 +44,8 @@
  *                block's rows with 32-bit offsets), or M*N, M*K or N*K/4
  *                above PQ2_MAX_ELEMS (larger than any device memory; keeps
  *                every launch grid below 2^31 blocks);
- *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above;
+ *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above (a
+ *                workspace, when given, must be 16-byte aligned);
  *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), M above
  *                PQ2_LINEAR_MAX_M (pq2_linear), or an unknown activation
  *                format (pq2_quantize_act_16);
@@ -54,13 +57,14 @@
 #ifndef PQ2_H
 #define PQ2_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define PQ2_ABI_VERSION 1
+#define PQ2_ABI_VERSION 2
 #define PQ2_GROUP 128
 #define PQ2_MAX_DIM (1LL << 30)
 #define PQ2_MAX_K (1LL << 24)
@@ -77,7 +81,7 @@ typedef enum {
 
 /* Kernel path selectors for pq2_gemm_group_dots. */
 enum {
-    PQ2_PATH_AUTO = 0,      /* same choice as pq2_gemm */
+    PQ2_PATH_AUTO = 0,      /* pq2_gemm's choice for the given workspace */
     PQ2_PATH_GEMV = 1,      /* M <= 4 only: the v_dot4 GEMV */
     PQ2_PATH_SMALL = 2,     /* M <= 16, K <= 32768: the small-batch MFMA kernel */
     PQ2_PATH_PREFILL = 3,   /* any M: the tiled MFMA GEMM */
@@ -122,6 +126,20 @@ pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float
                                int64_t M, int64_t K, void *hip_stream);
 
 /*
+ * Device workspace, in bytes, that pq2_gemm (and pq2_gemm_bf16) needs to run
+ * its fastest plan for this shape: the persistent small-batch kernel splits
+ * K into S chunks for some shapes (K = 17408 at 3..16 token rows: S = 3;
+ * 17..64 rows: most K) and writes S * M * N float32 partial sums, which a
+ * second small launch adds in chunk order. 0 when that plan does not split
+ * K, or when the shape is invalid. Pure host query; enqueues nothing. (The
+ * page "Making a ternary reasoning model fast in vLLM", section "Measure at
+ * the clock speeds used in serving", counts the split-K reduction launches;
+ * its section "Speed up a small unquantised projection" sums splits in a
+ * fixed order and rounds once.)
+ */
+size_t pq2_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * y = the PQ2_0 product defined above. The kernel depends on M:
  *   M <= 2        -> GEMV streaming code words into v_dot4 (2-bit planes
  *                    masked out of each 32-bit word, no decode step; each
@@ -142,20 +160,21 @@ pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float
  * Group dots are exact int32; the float32 epilogue sums the G terms in an
  * order that differs from a sequential sum only by float32 rounding (a fixed
  * order: repeated calls give identical y).
- * Workspace: when the panel kernel splits K into chunks (K = 17408 and other
- * K above ~8000; at M > 16 most K) the chunks' partial sums go to a device
- * buffer of chunks * M * N floats (at most 16 chunks) that the library
- * allocates on first need, one per device and stream, grows when a larger
- * one is needed (hipFree of the old one waits for the device) and keeps
- * until the process ends. hipMalloc makes such a first call unsafe under
- * graph capture: one call of the same or a larger shape on the stream before
- * capture creates the buffer, after which captured calls replay correctly.
- * A second small launch sums the chunks in a fixed order. PQ2_ERR_HIP if it
- * cannot allocate.
+ * Workspace: a caller-owned device buffer of workspace_bytes bytes, 16-byte
+ * aligned, or NULL. Plans that split K into S chunks are taken only when
+ * S * M * N * 4 <= workspace_bytes (the largest chunk count that fits, at
+ * most 16); pq2_gemm_workspace_bytes gives the size of the fastest plan.
+ * With NULL, or a buffer too small for any split, pq2_gemm takes a plan that
+ * does not split K (same result up to float32 summation order; slower on
+ * some shapes, e.g. K = 17408 at 3..16 rows). The workspace's contents
+ * before and after a call are unspecified; calls that may run concurrently
+ * (different streams) need different workspaces, calls on one stream may
+ * share one.
  */
 pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
                     const uint8_t *codes, const uint16_t *wscale, float *y,
-                    int64_t M, int64_t N, int64_t K, void *hip_stream);
+                    int64_t M, int64_t N, int64_t K,
+                    void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
  * pq2_gemm with a bfloat16 output, for callers whose activations are bfloat16
@@ -166,11 +185,12 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
  * (split-K partial sums stay float32 until the summing launch), so y is
  * exactly pq2_gemm's y rounded to bfloat16.
  *   y  bfloat16 bit patterns [M][N], 2-byte aligned, overwritten.
- * Everything else as for pq2_gemm.
+ * Everything else, the workspace included, as for pq2_gemm.
  */
 pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t,
                          const uint8_t *codes, const uint16_t *wscale, uint16_t *y,
-                         int64_t M, int64_t N, int64_t K, void *hip_stream);
+                         int64_t M, int64_t N, int64_t K,
+                         void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
  * Quantise and multiply in one launch, for decode batches of 1 to 4 token
@@ -195,25 +215,31 @@ pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wsca
 
 /*
  * The PQ2_PATH_* kernel path pq2_gemm takes for this shape on the current
- * device, or -1 when pq2_gemm would reject the shape (PQ2_ERR_SHAPE). Pure
- * host query; enqueues nothing.
+ * device when given a workspace of workspace_bytes bytes (0: none), or -1
+ * when pq2_gemm would reject the shape (PQ2_ERR_SHAPE). Pure host query;
+ * enqueues nothing.
  */
-int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K);
+int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K, size_t workspace_bytes);
 
 /*
  * Test and tuning entry: pq2_gemm through the selected kernel path instead of
- * pq2_gemm's own choice. Arguments, layouts and results as for pq2_gemm; path
- * is one of PQ2_PATH_* with the limits listed for pq2_gemm_group_dots
- * (PQ2_ERR_ARG otherwise).
+ * pq2_gemm's own choice. Arguments, layouts, workspace and results as for
+ * pq2_gemm; path is one of PQ2_PATH_* with the limits listed for
+ * pq2_gemm_group_dots, where the panel kernel's K chunks are limited by the
+ * workspace as in pq2_gemm (PQ2_ERR_ARG when no plan runs).
  */
 pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t,
                          const uint8_t *codes, const uint16_t *wscale, float *y,
-                         int64_t M, int64_t N, int64_t K, int path, void *hip_stream);
+                         int64_t M, int64_t N, int64_t K, int path,
+                         void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
  * Test and diagnostic entry: runs the main loop of the selected kernel path
  * but stores the exact per-group dots instead of the float epilogue:
  *   d int32 [M][N][G],  d[m][n][g] = D[m][n][g] as defined above.
+ * Every K chunk writes its own groups of d, so no workspace is involved:
+ * PQ2_PATH_AUTO is pq2_gemm's choice with a workspace of
+ * pq2_gemm_workspace_bytes(M, N, K) bytes.
  * path is one of PQ2_PATH_*; PQ2_PATH_GEMV requires M <= 4,
  * PQ2_PATH_SMALL requires M <= 16 and K <= 32768, PQ2_PATH_PANEL requires
  * M <= 64, 2048 <= K <= 18432 and a device whose LDS per block holds the

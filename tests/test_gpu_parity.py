@@ -359,62 +359,85 @@ def test_auto_path_every_m(pq2, K):
 
 def test_graph_replay_with_spins(pq2):
     """The power-proxy replay's pattern: quantise + pq2_gemm for projections on
-    every kernel path (GEMV, panel ring, panel with split K and its workspace,
-    token tiles, tiled GEMM and its ring form), each followed by a spin kernel, captured in one
-    HIP graph. Three replays, with eager work and synchronisations between
-    them, each give y bit-identical to the eager calls."""
+    every kernel path (GEMV, panel ring, panel with split K and the caller's
+    workspace, token tiles, tiled GEMM and its ring form), each followed by a
+    spin kernel, captured in one HIP graph with no eager call before the
+    capture. Three replays, with eager work (a larger split-K call on another
+    workspace, poisoned outputs) and synchronisations between them: every
+    replay's y is within tolerance of the oracle, and identical to the eager
+    calls made afterwards."""
     shapes = [(1, 300, 2048), (4, 520, 2048), (16, 300, 17408), (40, 200, 2048), (130, 260, 1024),
               (256, 8192, 1024)]
     cap = torch.cuda.Stream()
-    bufs = []
+    bufs, refs = [], []
     for i, (M, N, K) in enumerate(shapes):
         w = synth.weights(N, K, synth.matrix_seed(500 + i))
-        x = dev(synth.activations(M, K, 500 + i, outlier_frac=0.01))
+        xh = synth.activations(M, K, 500 + i, outlier_frac=0.01)
+        yo, tabs, _ = oracle.forward(xh, w.codes, w.wscale)
+        refs.append((yo, tabs))
         G_ = K // G
-        bufs.append((M, N, K, x, dev(w.codes), dev(w.wscale_bits.view(np.int16)),
+        bufs.append((M, N, K, dev(xh), dev(w.codes), dev(w.wscale_bits.view(np.int16)),
                      torch.empty((M, K), dtype=torch.int8, device="cuda"),
                      torch.empty((M, G_), dtype=torch.float32, device="cuda"),
                      torch.empty((M, G_), dtype=torch.int32, device="cuda"),
                      torch.empty((M, N), dtype=torch.float32, device="cuda")))
+    wsz = max(pq2.gemm_workspace_bytes(M, N, K) for (M, N, K) in shapes)
+    assert wsz > 0                               # the K = 17408 projection splits K
+    work = torch.empty(wsz, dtype=torch.uint8, device="cuda")
 
     def step():
         for (M, N, K, x, cd, wd, q, s, t, y) in bufs:
             pq2.pq2_quantize_act(x, q, s, t, stream=cap)
-            pq2.pq2_gemm(q, s, t, cd, wd, y, stream=cap)
+            pq2.pq2_gemm(q, s, t, cd, wd, y, workspace=work, stream=cap)
             torch.cuda._sleep(1000)
 
     torch.cuda.synchronize()
-    with torch.cuda.stream(cap):
-        step()                                   # eager: also creates the split-K workspace
-    torch.cuda.synchronize()
-    ref = [host(b[-1]).copy() for b in bufs]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
         step()
     torch.cuda.synchronize()
-    other = torch.empty((16, 300), dtype=torch.float32, device="cuda")
+    # a larger split-K problem, eager, on a workspace of its own
+    wb = synth.weights(2048, 17408, synth.matrix_seed(599))
+    qb, sb, tb = pq2.quantize_act(dev(synth.activations(16, 17408, 599)))
+    cb, wbd = dev(wb.codes), dev(wb.wscale_bits.view(np.int16))
+    yb = torch.empty((16, 2048), dtype=torch.float32, device="cuda")
+    outs = []
     for rep in range(3):
         for b in bufs:                           # eager work between replays
             b[-1].fill_(float("nan"))
-        M, N, K, x, cd, wd, q, s, t, _ = bufs[2]
-        pq2.pq2_gemm(q, s, t, cd, wd, other)
+        pq2.pq2_gemm(qb, sb, tb, cb, wbd, yb)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        outs.append([host(b[-1]).copy() for b in bufs])
         for i, b in enumerate(bufs):
             print(f"graph replay {rep} shape {shapes[i]}", flush=True)
-            np.testing.assert_array_equal(host(b[-1]), ref[i])
+            assert oracle.rel_err(outs[-1][i], *refs[i]) < TOL
+            np.testing.assert_array_equal(outs[-1][i], outs[0][i])
+    with torch.cuda.stream(cap):
+        step()
+    torch.cuda.synchronize()
+    for i, b in enumerate(bufs):
+        np.testing.assert_array_equal(host(b[-1]), outs[0][i])
 
 
 BF16_OUT = [(1, 300, 2048), (2, 5120, 6144), (4, 520, 2048), (5, 70, 2304), (16, 300, 17408),
             (40, 200, 2048), (130, 260, 1024), (256, 8192, 1024), (300, 129, 640)]
 
 
+def bf16_half_ulp(v):
+    """Half a bfloat16 ulp at magnitude v (8 significand bits; v > 0), float64."""
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
 @pytest.mark.parametrize("M,N,K", BF16_OUT)
 def test_gemm_bf16_output(pq2, M, N, K):
     """pq2_gemm_bf16 on every kernel path (GEMV, 16-token kernel, panel with and
-    without split K, token tiles, tiled GEMM and its ring form): y is exactly
-    pq2_gemm's float32 y rounded to nearest-even bfloat16."""
+    without split K, token tiles, tiled GEMM and its ring form), against the
+    oracle: |y - y*| <= half a bfloat16 ulp at |y*| + the float32 bound, plus
+    the float32 bound itself (1e-5 of sum_g |term_g|). Also, as the header
+    states, y is exactly pq2_gemm's float32 y rounded to nearest-even."""
     print(f"gemm bf16 out M={M} N={N} K={K} path={pq2.gemm_kernel_path(M, N, K)}", flush=True)
     x = synth.activations(M, K, M + N + K, outlier_frac=0.01)
     w = synth.weights(N, K, synth.matrix_seed(N + 2 * K))
@@ -424,6 +447,12 @@ def test_gemm_bf16_output(pq2, M, N, K):
     y16 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     pq2.pq2_gemm(q, s, t, cd, wd, y32)
     pq2.pq2_gemm(q, s, t, cd, wd, y16)
+    yb = host(y16.float()).astype(np.float64)
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    f32_bound = TOL * tabs
+    bound = bf16_half_ulp(np.abs(yo) + f32_bound) + f32_bound
+    over = np.abs(yb - yo) - bound
+    assert (over <= 0).all(), f"worst excess {over.max():.3g} at {np.unravel_index(over.argmax(), over.shape)}"
     ref = y32.cpu().to(torch.bfloat16).view(torch.int16).numpy()   # RNE on the CPU
     np.testing.assert_array_equal(host(y16.view(torch.int16)), ref)
 
@@ -767,40 +796,76 @@ def test_quantize_beyond_2_31(pq2):
     np.testing.assert_array_equal(ts, to)
 
 
-def test_split_k_streams_and_workspace_growth(pq2):
-    """Split-K y (K = 17408 at M = 16: three chunks through the library's
-    workspace) is identical on repeated calls, on two streams running
-    concurrently with different inputs (one workspace per stream), and after
-    the workspace grows for a larger N."""
+# K = 17408 at 3..16 rows: the ring plan in 3 chunks; 40 and 64 rows: the
+# token-tiled plan in 3 chunks (one or two chunks exceed LDS or the groups a
+# wave can hold)
+WS_SHAPES = [(16, 300, 17408), (4, 5120, 17408), (8, 1000, 17408), (12, 2100, 17408),
+             (40, 300, 6144), (64, 700, 5120)]
+
+
+@pytest.mark.parametrize("M,N,K", WS_SHAPES)
+def test_workspace_size_and_fallbacks(pq2, M, N, K):
+    """The size query matches the plan: pq2_gemm_workspace_bytes is a whole
+    number (2..16) of M x N float32 partial-sum planes; a workspace of exactly
+    that size gives y bit-identical to a larger one; a byte less, a NULL
+    workspace and a misaligned-size buffer take plans with fewer or no K
+    chunks (pq2_gemm_kernel_path reports them). Every result within
+    tolerance of the oracle, exact dots through the split and unsplit plans."""
+    wsz = pq2.gemm_workspace_bytes(M, N, K)
+    plane = M * N * 4
+    print(f"workspace M={M} N={N} K={K} bytes={wsz} path={pq2.gemm_kernel_path(M, N, K)} "
+          f"no-ws path={pq2.gemm_kernel_path(M, N, K, 0)}", flush=True)
+    assert wsz % plane == 0 and 2 <= wsz // plane <= 16
+    assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PANEL
+    x = synth.activations(M, K, M + N, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(N + M))
+    q, s, t = pq2.quantize_act(dev(x))
+    cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    yo, tabs, (qo, _, _) = oracle.forward(x, w.codes, w.wscale)
+    outs = {}
+    for name, nbytes in (("exact", wsz), ("larger", 2 * wsz + 48), ("short", wsz - 1),
+                         ("one_plane", plane), ("none", None)):
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        work = None if nbytes is None else torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        pq2.pq2_gemm(q, s, t, cd, wd, y, workspace=work)
+        outs[name] = host(y)
+        assert oracle.rel_err(outs[name], yo, tabs) < TOL, name
+    np.testing.assert_array_equal(outs["exact"], outs["larger"])
+    # the unsplit plan's kernel, read through its exact group dots
+    p0 = pq2.gemm_kernel_path(M, N, K, 0)
+    d = torch.empty((M, N, K // G), dtype=torch.int32, device="cuda")
+    pq2.pq2_gemm_group_dots(q, t, cd, d, path=p0)
+    np.testing.assert_array_equal(host(d), oracle.group_dots(qo, w.codes))
+
+
+def test_workspace_two_streams(pq2):
+    """Split-K calls on two streams at once, each with its own workspace,
+    different inputs: y identical to the same calls run one at a time."""
     M, K = 16, 17408
-    outs = []
-    for N in (300, 700, 300):     # grows, then a smaller call reuses the buffer
+    probs = []
+    for N in (700, 300):
         assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PANEL
+        assert pq2.gemm_workspace_bytes(M, N, K) > 0
         x = synth.activations(M, K, N, outlier_frac=0.01)
         w = synth.weights(N, K, synth.matrix_seed(N))
         q, s, t = pq2.quantize_act(dev(x))
         cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         pq2.pq2_gemm(q, s, t, cd, wd, y)
+        yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
         y0 = host(y)
-        pq2.pq2_gemm(q, s, t, cd, wd, y)
-        np.testing.assert_array_equal(host(y), y0)
-        qo, so, to = oracle.quantize(x)
-        mm = np.repeat(np.arange(M), 24)
-        nn = np.random.default_rng(N).integers(0, N, M * 24)
-        ys, ts = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
-        assert oracle.rel_err(y0[mm, nn], ys, ts) < TOL
-        outs.append((q, s, t, cd, wd, y0))
-    # the two 700- and 300-row problems at once on two streams
+        assert oracle.rel_err(y0, yo, tabs) < TOL
+        work = torch.empty(pq2.gemm_workspace_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+        probs.append((q, s, t, cd, wd, work, y0, N))
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    torch.cuda.synchronize()
     ya = torch.empty((M, 700), dtype=torch.float32, device="cuda")
     yb = torch.empty((M, 300), dtype=torch.float32, device="cuda")
-    for _ in range(3):
-        with torch.cuda.stream(sa):
-            pq2.pq2_gemm(*outs[1][:5], ya, stream=sa)
-        with torch.cuda.stream(sb):
-            pq2.pq2_gemm(*outs[0][:5], yb, stream=sb)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(ya), outs[1][5])
-    np.testing.assert_array_equal(host(yb), outs[0][5])
+    for _ in range(3):
+        (q, s, t, cd, wd, work, _, _) = probs[0]
+        pq2.pq2_gemm(q, s, t, cd, wd, ya, workspace=work, stream=sa)
+        (q, s, t, cd, wd, work, _, _) = probs[1]
+        pq2.pq2_gemm(q, s, t, cd, wd, yb, workspace=work, stream=sb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(ya), probs[0][6])
+    np.testing.assert_array_equal(host(yb), probs[1][6])
