@@ -189,13 +189,144 @@ def spin_cycles_per_ms(torch):
     return 2_000_000 / max(a.elapsed_time(b), 1e-3)
 
 
-def queue_ahead(torch, host_ms, cyc_per_ms):
-    """Hold the stream with a spin kernel long enough for the host to enqueue
-    the whole timed region, so HIP events time the GPU and not Python."""
-    torch.cuda._sleep(int(cyc_per_ms * (2.0 * host_ms + 5.0)))
+class Timer:
+    """HIP events around `steps` calls of a body on the current stream. The
+    stream is first held by a spin kernel long enough for the host to enqueue
+    the whole region, so the events time the GPU and not Python. Each call of
+    the body takes its own weight matrix from a running index (the bodies keep
+    it), so no pass re-reads a matrix sooner than a whole rotation later."""
+
+    def __init__(self, torch, steps):
+        self.torch = torch
+        self.steps = steps
+        self.cyc_per_ms = spin_cycles_per_ms(torch)
+
+    def host_ms(self, body):
+        t0 = time.perf_counter()
+        for _ in range(self.steps):
+            body()
+        self.torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    def run(self, body, host_ms, side=None):
+        """GPU ms of `steps` calls of body; side(event) is called right after
+        the first event is recorded (work for another stream that waits for
+        that event, so it runs alongside the timed region)."""
+        torch = self.torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(self.cyc_per_ms * (2.0 * host_ms + 5.0)))
+        a.record()
+        if side is not None:
+            side(a)
+        for _ in range(self.steps):
+            body()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
 
 
-def run_gemm(args, wl, torch, pq2):
+def median(v):
+    return float(np.median(np.asarray(v, dtype=np.float64)))
+
+
+class Probes:
+    """The measurement probes (libpq2_probe.so): streaming-read and int8 MFMA
+    ceilings, and the shader clock read in-band while other work runs."""
+
+    def __init__(self, torch):
+        import ctypes
+        self.torch = torch
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "gemm_pq2_w2a8_amd",
+                            "libpq2_probe.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python gemm_pq2_w2a8_amd/build.py`")
+        lib = ctypes.CDLL(path)
+        P, SZ = ctypes.c_void_p, ctypes.c_size_t
+        lib.pq2_probe_stream_read.argtypes = [P, SZ, P, ctypes.c_int, P]
+        lib.pq2_probe_mfma_i8.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        lib.pq2_probe_clock.argtypes = [P, ctypes.c_uint64, P]
+        for f in (lib.pq2_probe_stream_read, lib.pq2_probe_mfma_i8, lib.pq2_probe_clock):
+            f.restype = ctypes.c_int
+        self.lib = lib
+        dev = torch.device("cuda:0")
+        self.sink = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+        self.clk = torch.zeros(2, dtype=torch.int64, device=dev)
+        self.side = torch.cuda.Stream(dev)
+        props = torch.cuda.get_device_properties(dev)
+        self.cus = props.multi_processor_count
+        # wall clock counter rate (hipDeviceAttributeWallClockRate): 100 MHz on CDNA
+        self.wall_mhz = 100.0
+
+    def _ok(self, st, what):
+        if st != 0:
+            raise RuntimeError(f"probe {what} failed with status {st}")
+
+    def clock_side(self, ms):
+        """A side(event) for Timer.run: the clock probe on a side stream (default
+        priority), started when the timed region starts and spinning ~ms."""
+        side = self.side
+        ticks = max(1, min(int(ms * 1e3 * self.wall_mhz), (1 << 28)))
+
+        def go(event):
+            side.wait_event(event)
+            self._ok(self.lib.pq2_probe_clock(self.clk.data_ptr(), ticks, side.cuda_stream),
+                     "clock")
+        return go
+
+    def sclk_mhz(self):
+        self.torch.cuda.synchronize()
+        cyc, wall = (int(v) for v in self.clk.cpu())
+        return cyc / wall * self.wall_mhz if wall > 0 else None
+
+    def stream_read(self, nbytes, rotate_bytes, calls, trials=5):
+        """Best time per launch (median over trials, best over launch shapes)
+        of a plain read of nbytes, the slices cycling through a buffer of
+        rotate_bytes (above the Infinity Cache, like the rotating weights)."""
+        torch = self.torch
+        n16 = (nbytes + 15) // 16 * 16
+        slices = max(2, rotate_bytes // n16)
+        buf = torch.empty(slices * n16, dtype=torch.uint8, device="cuda:0")
+        buf.fill_(1)
+        stream = torch.cuda.current_stream().cuda_stream
+        tm = Timer(torch, calls)
+        best = None
+        for blocks in (self.cus * 2, self.cus * 4, self.cus * 8):
+            ctr = [0]
+
+            def body():
+                off = (ctr[0] % slices) * n16
+                ctr[0] += 1
+                self._ok(self.lib.pq2_probe_stream_read(buf.data_ptr() + off, n16,
+                                                        self.sink.data_ptr(), blocks, stream),
+                         "stream_read")
+            h = tm.host_ms(body)
+            us = median([tm.run(body, h) for _ in range(trials)]) / calls * 1e3
+            if best is None or us < best[0]:
+                best = (us, blocks)
+        del buf
+        return {"bytes": n16, "us": best[0], "GB/s": n16 / (best[0] * 1e-6) / 1e9,
+                "blocks": best[1], "rotating_bytes": slices * n16}
+
+    def mfma_i8(self, trials=5):
+        torch = self.torch
+        stream = torch.cuda.current_stream().cuda_stream
+        blocks, iters = self.cus * 8, 2000
+        tm = Timer(torch, 4)
+
+        def body():
+            self._ok(self.lib.pq2_probe_mfma_i8(self.sink.data_ptr(), iters, blocks, stream),
+                     "mfma")
+        h = tm.host_ms(body)
+        ms = median([tm.run(body, h) for _ in range(trials)]) / 4
+        ops = blocks * 4 * iters * 8 * 2 * 16 * 16 * 64
+        return {"TOP/s": ops / (ms * 1e-3) / 1e12, "us": ms * 1e3, "blocks": blocks,
+                "waves_per_cu": 4 * blocks // self.cus,
+                "instruction": "v_mfma_i32_16x16x64_i8, 8 independent chains per wave"}
+
+
+def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
     dev = torch.device("cuda:0")
     import pq2_synth as synth
     codes, scales = make_weight_set(wl, torch, dev)
@@ -206,70 +337,81 @@ def run_gemm(args, wl, torch, pq2):
     s = torch.empty((M, G), dtype=torch.float32, device=dev)
     t = torch.empty((M, G), dtype=torch.int32, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    wsz = pq2.gemm_workspace_bytes(M, N, K)
+    work = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
     R = len(codes)
     # raw pointers: the timed loop calls the C ABI directly (no per-call checks)
     lib = pq2.lib
     stream = torch.cuda.current_stream(dev).cuda_stream
     xp, qp, sp, tp, yp = x.data_ptr(), q.data_ptr(), s.data_ptr(), t.data_ptr(), y.data_ptr()
+    wkp = work.data_ptr() if wsz else None
     cps = [c.data_ptr() for c in codes]
     wps = [w.data_ptr() for w in scales]
     quant, gemm, linear = lib.pq2_quantize_act, lib.pq2_gemm, lib.pq2_linear
     fused = M <= LINEAR_MAX_M
+    ctr = [0]          # one running matrix index over every pass
 
-    def step_unfused(i):
+    def nxt():
+        i = ctr[0] % R
+        ctr[0] += 1
+        return i
+
+    def step():
+        i = nxt()
         st1 = quant(xp, qp, sp, tp, M, K, stream)
-        st2 = gemm(qp, sp, tp, cps[i % R], wps[i % R], yp, M, N, K, stream)
+        st2 = gemm(qp, sp, tp, cps[i], wps[i], yp, M, N, K, wkp, wsz, stream)
         if st1 or st2:
             raise pq2.PQ2Error(st1 or st2)
 
-    def step_fused(i):
-        st = linear(xp, cps[i % R], wps[i % R], yp, M, N, K, stream)
+    def gemm_only():
+        i = nxt()
+        st = gemm(qp, sp, tp, cps[i], wps[i], yp, M, N, K, wkp, wsz, stream)
         if st:
             raise pq2.PQ2Error(st)
 
-    step = step_unfused
-    for i in range(args.warmup):
-        step(i)
+    def step_fused():
+        i = nxt()
+        st = linear(xp, cps[i], wps[i], yp, M, N, K, stream)
+        if st:
+            raise pq2.PQ2Error(st)
+
+    for _ in range(args.warmup):
+        step()
         if fused:
-            step_fused(i)
+            step_fused()
     torch.cuda.synchronize()
-    cyc_per_ms = spin_cycles_per_ms(torch)
-
-    def timed(body):
-        """Run body(i) for the K timed iterations between two HIP events, with
-        the stream held by a spin kernel while the host enqueues them."""
-        h0 = time.perf_counter()
-        for i in range(args.steps):
-            body(i)
-        torch.cuda.synchronize()
-        host_ms = (time.perf_counter() - h0) * 1e3
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        queue_ahead(torch, host_ms, cyc_per_ms)
-        a.record()
-        h0 = time.perf_counter()
-        for i in range(args.steps):
-            body(i)
-        enq_ms = (time.perf_counter() - h0) * 1e3
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b), enq_ms, host_ms
-
-    # the whole step
+    tm = Timer(torch, steps)
+    h_step = tm.host_ms(step)
+    h_gemm = tm.host_ms(gemm_only)
+    h_fused = tm.host_ms(step_fused) if fused else 0.0
+    step_ms, gemm_ms, fused_ms, sclk = [], [], [], []
     wall0 = time.perf_counter()
-    total_ms, enq_ms, _ = timed(step)
+    for _ in range(trials):
+        step_ms.append(tm.run(step, h_step))
+        # the clock probe spins for about half of the step region just timed,
+        # which is shorter than the GEMM-only region
+        side = probes.clock_side(0.5 * step_ms[-1]) if probes is not None else None
+        gemm_ms.append(tm.run(gemm_only, h_gemm, side))
+        if probes is not None:
+            sclk.append(probes.sclk_mhz())
+        if fused:
+            fused_ms.append(tm.run(step_fused, h_fused))
     wall = time.perf_counter() - wall0
-    # pq2_gemm alone, back to back on the same stream (average launch duration
-    # including the dispatch gap between launches)
-    gemm_total, _, _ = timed(lambda i: gemm(qp, sp, tp, cps[i % R], wps[i % R], yp, M, N, K, stream))
-    out = dict(ms_step=total_ms / args.steps, gemm_ms=gemm_total / args.steps, wall=wall,
-               path=pq2.PATH_NAMES[pq2.gemm_kernel_path(M, N, K)],
-               M=M, N=N, K=K, host_enqueue_ms=enq_ms, gpu_ms=total_ms, fused=fused)
+    per = lambda v: median(v) / steps
+    wbytes = N * K // 4 + 2 * N * G          # one matrix: codes + float16 scales
+    out = dict(ms_step=per(step_ms), gemm_ms=per(gemm_ms), wall=wall,
+               path=pq2.PATH_NAMES[pq2.gemm_kernel_path(M, N, K)], M=M, N=N, K=K,
+               host_enqueue_ms=h_step, fused=fused, trials=trials, steps=steps,
+               workspace_bytes=wsz,
+               trial_step_us=[v / steps * 1e3 for v in step_ms],
+               trial_gemm_us=[v / steps * 1e3 for v in gemm_ms],
+               bytes_between_reuse=(R - 1) * wbytes if R > 1 else None,
+               rotate=R)
     out["kernel_ms"] = out["gemm_ms"]
+    if sclk and all(v is not None for v in sclk):
+        out["sclk_mhz"] = median(sclk)
     if fused:
-        fus_total, _, _ = timed(step_fused)
-        out["fused_ms_step"] = fus_total / args.steps
+        out["fused_ms_step"] = per(fused_ms)
     return out
 
 
@@ -291,27 +433,36 @@ def report_gemm(args, wl, r, torch):
         achieved = gemm_bytes(M, N, K) / (r["kernel_ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
+    roof["traffic"] = traffic_record(f"{path}_{wl.name}")
     roof["kernel"] = path
     roof["kernel_us"] = r["kernel_ms"] * 1e3
-    roof["timing"] = ("HIP events around K back-to-back pq2_gemm launches (rotating weights); the "
+    roof["timing"] = (f"HIP events around {r['steps']} back-to-back pq2_gemm launches, median "
+                      f"of {r['trials']} trials; one running matrix index over every pass; the "
                       "stream is held by a spin kernel while the host enqueues, so the events see "
                       "GPU time; includes the dispatch gap between launches")
-    roof["traffic"] = traffic_record(f"{path}_{wl.name}")
+    cfg = {"workload": wl.name, "M": M, "N": N, "K": K, "rotating_matrices": r["rotate"],
+           "bytes_between_matrix_reuse": r["bytes_between_reuse"],
+           "step": "pq2_quantize_act + pq2_gemm",
+           "algorithmic_bytes_per_step": sbytes,
+           "gemm_bytes_per_call": gemm_bytes(M, N, K),
+           "gemm_int_ops_per_call": gemm_ops(M, N, K),
+           "workspace_bytes": r["workspace_bytes"],
+           "trials": r["trials"], "steps_per_trial": r["steps"],
+           "trial_step_us": [round(v, 3) for v in r["trial_step_us"]],
+           "trial_pq2_gemm_us": [round(v, 3) for v in r["trial_gemm_us"]],
+           "host_enqueue_ms": r["host_enqueue_ms"],
+           "pq2_gemm_us": r["gemm_ms"] * 1e3}
+    if "sclk_mhz" in r:
+        cfg["sclk_mhz_during_pq2_gemm"] = r["sclk_mhz"]
     line = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": r["steps"],
         "warmup": args.warmup, "ms_per_step": r["ms_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
-        "config": {"workload": wl.name, "M": M, "N": N, "K": K, "rotating_matrices": wl.rotate,
-                   "step": "pq2_quantize_act + pq2_gemm",
-                   "algorithmic_bytes_per_step": sbytes,
-                   "gemm_bytes_per_call": gemm_bytes(M, N, K),
-                   "gemm_int_ops_per_call": gemm_ops(M, N, K),
-                   "host_enqueue_ms": r["host_enqueue_ms"], "gpu_ms": r["gpu_ms"],
-                   "pq2_gemm_us": r["gemm_ms"] * 1e3},
+        "config": cfg,
         "roofline": roof,
     }
     if fused:
-        line["config"]["fused_step_us"] = r["fused_ms_step"] * 1e3
+        cfg["fused_step_us"] = r["fused_ms_step"] * 1e3
     if not args.no_cpu:
         line["cpu_baseline"] = (cpu_baseline_prefill(wl, args.cpu_seconds) if prefill
                                 else cpu_baseline(wl, args.cpu_seconds))
@@ -336,6 +487,10 @@ def layer_step(m, torch, pq2, stream):
                        torch.empty((m, k // GROUP), dtype=torch.float32, device=dev),
                        torch.empty((m, k // GROUP), dtype=torch.int32, device=dev))
     ys = {n: torch.empty((m, n), dtype=torch.float32, device=dev) for (n, _) in synth.LAYER_SHAPES}
+    # one split-K workspace serves every projection: they run in order on one stream
+    wsz = max(pq2.gemm_workspace_bytes(m, n, k) for (n, k) in synth.LAYER_SHAPES)
+    work = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+    wkp = work.data_ptr() if wsz else None
     lib = pq2.lib
     # the gate and up projections (the two 5120 -> 17408 ones) read the same
     # activations, so one quantisation serves both; every other projection
@@ -354,37 +509,28 @@ def layer_step(m, torch, pq2, stream):
         for (qz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
             if qz:
                 quant(xp, qp, sp, tp, m, k, stream)
-            gemm(qp, sp, tp, cp, wp, yp, m, n, k, stream)
+            gemm(qp, sp, tp, cp, wp, yp, m, n, k, wkp, wsz, stream)
             if after is not None:
                 after()
 
-    step.buffers = (layers, xs, bufs, ys)     # the launches hold raw pointers into these
+    step.buffers = (layers, xs, bufs, ys, work)   # the launches hold raw pointers into these
+    step.workspace_bytes = wsz
     return step, shares_input
 
 
-def run_layers(args, m, torch, pq2):
-    """64-layer synthetic decode step: 5 PQ2_0 projections per layer, back to back."""
+def run_layers(args, m, torch, pq2, steps, trials):
+    """64-layer synthetic decode step: 5 PQ2_0 projections per layer, back to
+    back on one stream (every weight matrix is read once per step, 5.6 GB)."""
     import pq2_synth as synth
     stream = torch.cuda.current_stream(torch.device("cuda:0")).cuda_stream
     step, shares_input = layer_step(m, torch, pq2, stream)
     for _ in range(2):
         step()
     torch.cuda.synchronize()
-    steps = max(1, args.steps // 20)
-    cyc_per_ms = spin_cycles_per_ms(torch)
-    h0 = time.perf_counter()
-    step()
-    host_ms = (time.perf_counter() - h0) * 1e3 * steps
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    queue_ahead(torch, host_ms, cyc_per_ms)
-    a.record()
-    for _ in range(steps):
-        step()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    tm = Timer(torch, steps)
+    h = tm.host_ms(step)
+    runs = [tm.run(step, h) for _ in range(trials)]
+    ms = median(runs) / steps
     total = 0
     for i, (n, k) in enumerate(synth.LAYER_SHAPES):
         total += gemm_bytes(m, n, k) + (0 if shares_input[i] else quant_bytes(m, k))
@@ -397,7 +543,9 @@ def run_layers(args, m, torch, pq2):
                        "gemms_per_step": 5 * synth.N_LAYERS,
                        "quantisations_per_step": (5 - sum(shares_input)) * synth.N_LAYERS,
                        "projection": "pq2_quantize_act + pq2_gemm (gate and up share one quantisation)",
-                       "algorithmic_bytes_per_step": total},
+                       "algorithmic_bytes_per_step": total, "trials": trials,
+                       "trial_ms": [round(v / steps, 4) for v in runs],
+                       "workspace_bytes": step.workspace_bytes},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                          "note": "whole step incl. quantise launches and launch gaps"}}
@@ -431,7 +579,7 @@ def run_proxy(args, m, torch, pq2):
     step, _ = layer_step(m, torch, pq2, cap.cuda_stream)
     after = (lambda: torch.cuda._sleep(spin)) if spin > 0 else None
     with torch.cuda.stream(cap):
-        step(after)                 # eager first: any per-stream workspace exists before capture
+        step(after)                 # eager run before capture (checks the launches)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=cap):
@@ -458,6 +606,56 @@ def run_proxy(args, m, torch, pq2):
                               "projection; GEMM kernel durations from a kernel trace of this run"}}
 
 
+def run_ceiling(torch):
+    """Practical ceilings of one MI355X: a plain streaming read at several
+    sizes (slices cycling through 1 GiB) and the int8 MFMA loop."""
+    probes = Probes(torch)
+    reads = []
+    for mib in (8, 24, 64, 256):
+        nbytes = mib << 20
+        print(f"# stream read {mib} MiB", file=sys.stderr, flush=True)
+        reads.append(probes.stream_read(nbytes, 1 << 30, calls=max(4, 800 // mib)))
+    print("# int8 MFMA loop", file=sys.stderr, flush=True)
+    mf = probes.mfma_i8()
+    return {"ceiling": {"stream_read": reads, "mfma_i8": mf,
+                        "hbm_peak_GB/s": HBM_PEAK_GBS, "i8_peak_TOP/s": I8_PEAK_TOPS}}
+
+
+def extras(args, wl, r, torch, pq2, probes):
+    """Figures the default line carries beside its own workload: the prefill
+    half of the metric (M = 4096, N = 17408, K = 5120, int8 TOP/s), the
+    64-layer decode step at one token row (whole-step HBM GB/s), and the
+    practical ceilings the kernels are compared with."""
+    import pq2_synth as synth
+    out = {}
+    print("# extras: prefill m4096 n17408", file=sys.stderr, flush=True)
+    pw = synth.prefill(4096, 17408, 5120)
+    pr = run_gemm(args, pw, torch, pq2, max(1, min(args.steps, 20)), args.trials, probes)
+    ops = gemm_ops(pw.m, pw.n, pw.k)
+    tops = ops / (pr["kernel_ms"] * 1e-3) / 1e12
+    out[pw.name] = {"pq2_gemm_us": pr["kernel_ms"] * 1e3, "kernel": pr["path"],
+                    "TOP/s": tops, "frac_i8_peak": tops / I8_PEAK_TOPS,
+                    "step_us": pr["ms_step"] * 1e3,
+                    "sclk_mhz_during_pq2_gemm": pr.get("sclk_mhz"),
+                    "trial_pq2_gemm_us": [round(v, 2) for v in pr["trial_gemm_us"]]}
+    torch.cuda.empty_cache()
+    print("# extras: layer64 m1", file=sys.stderr, flush=True)
+    lr = run_layers(args, 1, torch, pq2, 5, args.trials)
+    out["layer64_m1"] = {"ms_per_step": lr["ms_per_step"], "GB/s": lr["value"],
+                         "frac_hbm_peak": lr["value"] / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_step": lr["config"]["algorithmic_bytes_per_step"],
+                         "trial_ms": lr["config"]["trial_ms"]}
+    torch.cuda.empty_cache()
+    if r is not None and r["M"] <= 16:
+        print("# extras: ceilings", file=sys.stderr, flush=True)
+        nb = gemm_bytes(r["M"], r["N"], r["K"])
+        sr = probes.stream_read(nb, 1 << 30, calls=max(20, min(args.steps, 200)))
+        sr["pq2_gemm_time_over_read_time"] = r["kernel_ms"] * 1e3 / sr["us"]
+        out["stream_read_same_bytes"] = sr
+    out["mfma_i8_loop"] = probes.mfma_i8()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -476,7 +674,15 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise kernel (y = 2x, float32) over MIB MiB, "
                          "the calibration for HBM byte counters")
+    ap.add_argument("--trials", type=int, default=5, help="timed trials (the median is reported)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default line only: skip the prefill, 64-layer and ceiling figures")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only print the practical ceilings: streaming reads of several sizes "
+                         "and the int8 MFMA loop (libpq2_probe.so)")
     args = ap.parse_args()
+    if args.steps < 1 or args.trials < 1 or args.warmup < 0:
+        ap.error("--steps and --trials must be positive, --warmup not negative")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -501,6 +707,10 @@ def main():
                                          "write_bytes_per_launch": 4 * n, "launches": reps}}))
         return
 
+    if args.ceiling:
+        print(json.dumps(run_ceiling(torch)), flush=True)
+        return
+
     import gemm_pq2_w2a8_amd as pq2
 
     if args.proxy:
@@ -509,14 +719,19 @@ def main():
 
     wls = workload_list()
     names = list(wls) if args.sweep else [args.workload]
+    probes = Probes(torch)
     for name in names:
         kind, wl = wls[name]
         print(f"# running {name}", file=sys.stderr, flush=True)
         if kind == "gemm":
-            r = run_gemm(args, wl, torch, pq2)
+            r = run_gemm(args, wl, torch, pq2, args.steps, args.trials, probes)
             line = report_gemm(args, wl, r, torch)
         else:
-            line = run_layers(args, wl, torch, pq2)
+            line = run_layers(args, wl, torch, pq2, max(1, args.steps // 40), args.trials)
+        torch.cuda.empty_cache()
+        if not args.sweep and not args.no_extras:
+            line["config"]["also"] = extras(args, wl, r if kind == "gemm" else None, torch, pq2,
+                                            probes)
         print(json.dumps(line), flush=True)
         torch.cuda.empty_cache()
 

@@ -1,8 +1,10 @@
-"""Build ``libpq2.so`` (the C-ABI library of include/pq2.h) for gfx950 with hipcc.
+"""Build ``libpq2.so`` (the C-ABI library of include/pq2.h) and
+``libpq2_probe.so`` (the measurement probes of include/pq2_probe.h) for gfx950
+with hipcc.
 
 Run ``python gemm_pq2_w2a8_amd/build.py`` (or call :func:`build`); as a script it
 does not import the package, which needs a built library. Objects go to
-``gemm_pq2_w2a8_amd/_build/``; the library is written next to this file.
+``gemm_pq2_w2a8_amd/_build/``; the libraries are written next to this file.
 """
 
 from __future__ import annotations
@@ -16,10 +18,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpq2.so")
+PROBE_LIB = os.path.join(HERE, "libpq2_probe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["pq2_abi.cpp", "quantize.hip", "gemv_dot4.hip", "small_mfma.hip", "small_panel.hip",
            "prefill_mfma.hip"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -51,18 +55,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

@@ -19,7 +19,7 @@ P = 0x100000  # a fake, 256-byte-aligned non-null address; never dereferenced
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(pq2_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(pq2_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_symbols_exported():
@@ -60,29 +60,30 @@ def test_quantize_validation():
 
 def test_gemm_validation():
     f = pq2.lib.pq2_gemm
-    assert f(None, P, P, P, P, P, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, P, P, None, P, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, P, P, P, None, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, P, P, P, P, 1, 0, 128, None) == ERR_SHAPE
-    assert f(P, P, P, P, P, P, 0, 8, 128, None) == ERR_SHAPE
-    assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
-    assert f(P, P, P, P, P, P, 1, 8, (1 << 24) + 128, None) == ERR_SHAPE
-    assert f(P, P, P, P, P, P, 1, (1 << 30) + 1, 128, None) == ERR_SHAPE
-    assert f(P, P, P, P, P, P, 1 << 30, 1 << 30, 128, None) == ERR_SHAPE        # M*N > 2^40
-    assert f(P, P, P, P, P, P, 1 << 20, 8, 1 << 21, None) == ERR_SHAPE         # M*K > 2^40
-    assert f(P, P, P, P, P, P, 1, 1 << 30, 1 << 14, None) == ERR_SHAPE         # N*K/4 > 2^40
-    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
-    assert f(P, P, P, P, P + 1, P, 1, 8, 128, None) == ERR_ALIGN   # wscale needs 2 B
-    assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
+    assert f(None, P, P, P, P, P, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, None, P, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 0, 128, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 0, 8, 128, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1, 8, 129, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1, 8, (1 << 24) + 128, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1, (1 << 30) + 1, 128, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 1 << 30, 1 << 30, 128, None, 0, None) == ERR_SHAPE        # M*N > 2^40
+    assert f(P, P, P, P, P, P, 1 << 20, 8, 1 << 21, None, 0, None) == ERR_SHAPE         # M*K > 2^40
+    assert f(P, P, P, P, P, P, 1, 1 << 30, 1 << 14, None, 0, None) == ERR_SHAPE         # N*K/4 > 2^40
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None, 0, None) == ERR_ALIGN   # codes needs 16 B
+    assert f(P, P, P, P, P + 1, P, 1, 8, 128, None, 0, None) == ERR_ALIGN   # wscale needs 2 B
+    assert f(P, P, P, P, P, P + 2, 1, 8, 128, None, 0, None) == ERR_ALIGN   # y needs 4 B
+    assert f(P, P, P, P, P, P, 1, 8, 128, P + 4, 64, None) == ERR_ALIGN     # workspace 16 B
 
 
 def test_gemm_bf16_validation():
     f = pq2.lib.pq2_gemm_bf16
-    assert f(None, P, P, P, P, P, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, P, P, P, None, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
-    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
-    assert f(P, P, P, P, P, P + 1, 1, 8, 128, None) == ERR_ALIGN   # y needs 2 B
+    assert f(None, P, P, P, P, P, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 8, 129, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None, 0, None) == ERR_ALIGN   # codes needs 16 B
+    assert f(P, P, P, P, P, P + 1, 1, 8, 128, None, 0, None) == ERR_ALIGN   # y needs 2 B
 
 
 def test_quantize_16bit_validation():
@@ -125,29 +126,38 @@ def test_group_dots_validation():
 
 def test_gemm_path_validation():
     f = pq2.lib.pq2_gemm_path
-    assert f(None, P, P, P, P, P, 1, 8, 128, 0, None) == ERR_NULL
-    assert f(P, P, P, P, P, None, 1, 8, 128, 0, None) == ERR_NULL
-    assert f(P, P, P, P, P, P, 1, 8, 200, 0, None) == ERR_SHAPE
-    assert f(P, P, P, P + 8, P, P, 1, 8, 128, 1, None) == ERR_ALIGN
-    assert f(P, P, P, P, P, P, 5, 8, 128, pq2.PATH_GEMV, None) == ERR_ARG
-    assert f(P, P, P, P, P, P, 17, 8, 1024, pq2.PATH_SMALL, None) == ERR_ARG
-    assert f(P, P, P, P, P, P, 65, 8, 2048, pq2.PATH_PANEL, None) == ERR_ARG   # M <= 64
-    assert f(P, P, P, P, P, P, 8, 8, 1920, pq2.PATH_PANEL, None) == ERR_ARG    # K >= 2048
-    assert f(P, P, P, P, P, P, 8, 8, 18560, pq2.PATH_PANEL, None) == ERR_ARG   # K <= 18432
-    assert f(P, P, P, P, P, P, 1, 8, 128, 5, None) == ERR_ARG
+    assert f(None, P, P, P, P, P, 1, 8, 128, 0, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, 0, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 8, 200, 0, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, 1, None, 0, None) == ERR_ALIGN
+    assert f(P, P, P, P, P, P, 5, 8, 128, pq2.PATH_GEMV, None, 0, None) == ERR_ARG
+    assert f(P, P, P, P, P, P, 17, 8, 1024, pq2.PATH_SMALL, None, 0, None) == ERR_ARG
+    assert f(P, P, P, P, P, P, 65, 8, 2048, pq2.PATH_PANEL, None, 0, None) == ERR_ARG   # M <= 64
+    assert f(P, P, P, P, P, P, 8, 8, 1920, pq2.PATH_PANEL, None, 0, None) == ERR_ARG    # K >= 2048
+    assert f(P, P, P, P, P, P, 8, 8, 18560, pq2.PATH_PANEL, None, 0, None) == ERR_ARG   # K <= 18432
+    assert f(P, P, P, P, P, P, 1, 8, 128, 5, None, 0, None) == ERR_ARG
 
 
 def test_kernel_path_query():
     f = pq2.lib.pq2_gemm_kernel_path
-    assert f(1, 8, 100) == -1 and f(0, 8, 128) == -1
-    assert f(1, 5120, 6144) == pq2.PATH_GEMV
-    assert f(2, 17408, 5120) == pq2.PATH_GEMV
-    assert f(17, 8, 128) == pq2.PATH_PREFILL
-    assert f(16, 8, 32768 + 128) == pq2.PATH_PREFILL
+    big = 1 << 40
+    assert f(1, 8, 100, big) == -1 and f(0, 8, 128, big) == -1
+    assert f(1, 5120, 6144, 0) == pq2.PATH_GEMV
+    assert f(2, 17408, 5120, big) == pq2.PATH_GEMV
+    assert f(17, 8, 128, big) == pq2.PATH_PREFILL
+    assert f(16, 8, 32768 + 128, big) == pq2.PATH_PREFILL
     # 17..64 rows where the tiled GEMM fills two blocks per CU: the tiled GEMM
-    assert f(32, 17408, 5120) == pq2.PATH_PREFILL
+    assert f(32, 17408, 5120, big) == pq2.PATH_PREFILL
     # without a GPU the panel kernel never fits: the 16-token kernel is chosen
-    assert f(8, 5120, 17408) == pq2.PATH_SMALL
+    assert f(8, 5120, 17408, big) == pq2.PATH_SMALL
+    assert f(8, 5120, 17408, 0) == pq2.PATH_SMALL
+
+
+def test_workspace_query():
+    f = pq2.lib.pq2_gemm_workspace_bytes
+    assert f(1, 8, 100) == 0 and f(0, 8, 128) == 0     # invalid shapes
+    assert f(1, 5120, 6144) == 0                        # the GEMV never splits K
+    assert f(4096, 17408, 5120) == 0                    # nor does the tiled GEMM
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -155,3 +165,46 @@ def test_python_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 128)
     with pytest.raises(ValueError):
         pq2.quantize_act(x)
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "pq2_probe.h")
+PROBE_LIB = os.path.join(ROOT, "gemm_pq2_w2a8_amd", "libpq2_probe.so")
+
+
+def probe_lib():
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libpq2_probe.so not built")
+    lib = ctypes.CDLL(PROBE_LIB)
+    Pv, SZ = ctypes.c_void_p, ctypes.c_size_t
+    lib.pq2_probe_stream_read.argtypes = [Pv, SZ, Pv, ctypes.c_int, Pv]
+    lib.pq2_probe_mfma_i8.argtypes = [Pv, ctypes.c_int, ctypes.c_int, Pv]
+    lib.pq2_probe_clock.argtypes = [Pv, ctypes.c_uint64, Pv]
+    return lib
+
+
+def test_probe_header_symbols_exported():
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(pq2_[a-z0-9_]+)\s*\(", src)))
+    assert names == ["pq2_probe_clock", "pq2_probe_mfma_i8", "pq2_probe_stream_read"]
+    lib = probe_lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_probe_validation():
+    lib = probe_lib()
+    f = lib.pq2_probe_stream_read
+    assert f(None, 1024, P, 256, None) == -1
+    assert f(P, 1000, P, 256, None) == -1          # bytes a multiple of 16
+    assert f(P + 8, 1024, P, 256, None) == -1      # src 16-byte aligned
+    assert f(P, 1024, P, 0, None) == -1
+    assert f(P, 1024, P, (1 << 20) + 1, None) == -1
+    g = lib.pq2_probe_mfma_i8
+    assert g(None, 10, 256, None) == -1
+    assert g(P, 0, 256, None) == -1
+    assert g(P, 10, 0, None) == -1
+    h = lib.pq2_probe_clock
+    assert h(None, 100, None) == -1
+    assert h(P + 4, 100, None) == -1
+    assert h(P, 0, None) == -1
+    assert h(P, (1 << 28) + 1, None) == -1

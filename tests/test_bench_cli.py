@@ -47,3 +47,10 @@ def test_proxy_spin_length_is_linear_between_2_and_16():
     import bench
     a, b = bench.proxy_spin_us(2), bench.proxy_spin_us(16)
     assert bench.proxy_spin_us(9) == pytest.approx((a + b) / 2)
+
+
+def test_bad_counts_are_rejected():
+    for flags in (["--steps", "0"], ["--trials", "0"], ["--warmup", "-1"]):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2, flags

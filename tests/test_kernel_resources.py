@@ -20,7 +20,7 @@ _spec = importlib.util.spec_from_file_location(
 hip_build = importlib.util.module_from_spec(_spec)
 _spec.loader.exec_module(hip_build)
 
-SOURCES = [s for s in hip_build.SOURCES if s.endswith(".hip")]
+SOURCES = [s for s in hip_build.SOURCES + hip_build.PROBE_SOURCES if s.endswith(".hip")]
 
 
 @pytest.mark.skipif(shutil.which(hip_build.HIPCC) is None and not os.path.exists(hip_build.HIPCC),
