@@ -254,6 +254,11 @@ class Probes:
         self.sink = torch.empty(1 << 20, dtype=torch.int32, device=dev)
         self.clk = torch.zeros(2, dtype=torch.int64, device=dev)
         self.side = torch.cuda.Stream(dev)
+        # first launch on the side stream outside any timed region (a stream's
+        # first launch costs far more than later ones)
+        self._ok(self.lib.pq2_probe_clock(self.clk.data_ptr(), 1000, self.side.cuda_stream),
+                 "clock")
+        torch.cuda.synchronize()
         props = torch.cuda.get_device_properties(dev)
         self.cus = props.multi_processor_count
         # wall clock counter rate (hipDeviceAttributeWallClockRate): 100 MHz on CDNA
