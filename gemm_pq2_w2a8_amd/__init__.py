@@ -45,6 +45,8 @@ lib.pq2_gemm.restype = ctypes.c_int
 lib.pq2_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
 lib.pq2_gemm_bf16.restype = ctypes.c_int
 lib.pq2_gemm_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
+lib.pq2_gemm_noalloc.restype = ctypes.c_int
+lib.pq2_gemm_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]
 lib.pq2_gemm_kernel_path.restype = ctypes.c_int
 lib.pq2_gemm_kernel_path.argtypes = [_I64, _I64, _I64, _SZ]
 lib.pq2_gemm_path.restype = ctypes.c_int
@@ -59,8 +61,10 @@ LINEAR_MAX_M = 4    # PQ2_LINEAR_MAX_M
 
 # Every extern "C" symbol declared in include/pq2.h.
 ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_quantize_act_16",
-               "pq2_gemm_workspace_bytes", "pq2_gemm", "pq2_gemm_bf16", "pq2_gemm_kernel_path",
-               "pq2_gemm_path", "pq2_linear", "pq2_gemm_group_dots")
+               "pq2_gemm_workspace_bytes", "pq2_gemm", "pq2_gemm_noalloc", "pq2_gemm_bf16",
+               "pq2_gemm_kernel_path", "pq2_gemm_path", "pq2_linear", "pq2_gemm_group_dots")
+
+NOALLOC_SCRATCH_BYTES = 16 << 20    # PQ2_NOALLOC_SCRATCH_BYTES
 
 PATH_NAMES = {PATH_GEMV: "gemv_dot4", PATH_SMALL: "small_mfma", PATH_PREFILL: "prefill_mfma",
               PATH_PANEL: "small_panel"}
@@ -194,6 +198,25 @@ def pq2_gemm(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Ten
     _need(y, "y", torch.float32, (M, N))
     _check(lib.pq2_gemm(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
                         wscale.data_ptr(), y.data_ptr(), M, N, K, wp, wn, _stream(q, stream)))
+
+
+def pq2_gemm_noalloc(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
+                     wscale: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """pq2_gemm with the library's own per-device split-K scratch: no workspace,
+    no allocation (calls that overlap on one device race on the scratch)."""
+    M, K = _mk(q)
+    N = int(codes.shape[0])
+    G = K // GROUP
+    _need(q, "q", torch.int8, (M, K))
+    _need(s, "s", torch.float32, (M, G))
+    _need(t, "t", torch.int32, (M, G))
+    _need(codes, "codes", torch.uint8, (N, K // 4))
+    if wscale.dtype == torch.float16:
+        wscale = wscale.view(torch.int16)
+    _need(wscale, "wscale", torch.int16, (N, G))
+    _need(y, "y", torch.float32, (M, N))
+    _check(lib.pq2_gemm_noalloc(q.data_ptr(), s.data_ptr(), t.data_ptr(), codes.data_ptr(),
+                                wscale.data_ptr(), y.data_ptr(), M, N, K, _stream(q, stream)))
 
 
 def pq2_gemm_path(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,

@@ -127,6 +127,7 @@ const char *pq2_status_str(int status) {
         case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
         case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
         case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this shape and workspace, M too large for pq2_linear, or unknown activation format";
+        case PQ2_ERR_SCRATCH: return "PQ2_ERR_SCRATCH: the shape needs more split-K scratch than pq2_gemm_noalloc holds (PQ2_NOALLOC_SCRATCH_BYTES)";
         default: return "PQ2 unknown status";
     }
 }
@@ -179,6 +180,27 @@ pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t, cons
     out.y16 = y;
     return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s,
                     static_cast<float *>(workspace), static_cast<hipStream_t>(hip_stream));
+}
+
+pq2_status pq2_gemm_noalloc(const int8_t *q, const float *s, const int32_t *t,
+                            const uint8_t *codes, const uint16_t *wscale, float *y, int64_t M,
+                            int64_t N, int64_t K, void *hip_stream) {
+    static_assert(PQ2_NOALLOC_SCRATCH_BYTES == pq2::kScratchBytes, "scratch size in the header");
+    pq2_status st = check_gemm(q, s, t, codes, wscale, y, 4, nullptr, M, N, K);
+    if (st != PQ2_OK) return st;
+    const size_t need = workspace_need(M, N, K);
+    if (need > pq2::kScratchBytes) return PQ2_ERR_SCRATCH;
+    float *work = nullptr;
+    if (need > 0) {
+        hipError_t e = hipSuccess;
+        work = pq2::scratch_address(&e);
+        if (!work) return PQ2_ERR_HIP;
+    }
+    // the same plan pq2_gemm takes with a workspace of exactly `need` bytes
+    const int max_s = need > 0 ? splits_for_bytes(need, M, N) : 1;
+    const pq2::GemmOut out{y, nullptr, s, wscale};
+    return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s, work,
+                    static_cast<hipStream_t>(hip_stream));
 }
 
 int pq2_gemm_kernel_path(int64_t M, int64_t N, int64_t K, size_t workspace_bytes) {

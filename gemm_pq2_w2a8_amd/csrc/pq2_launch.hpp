@@ -63,6 +63,12 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
                               int max_splits, float *work, hipStream_t stream);
 
+// The allocation-free entry's split-K buffer: kScratchBytes of device memory
+// per device (a file-scope array), its address on the current device looked
+// up once per device (nullptr and *err set if the lookup fails).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+float *scratch_address(hipError_t *err);
+
 // y = sum over the chunks of part[c][M*N], added in chunk order.
 hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t MN, int splits,
                             hipStream_t stream);

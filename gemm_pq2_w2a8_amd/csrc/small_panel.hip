@@ -1165,6 +1165,37 @@ PanelPlan choose_panel(int64_t M, int64_t N, int64_t K, int max_splits, PanelKin
 
 }  // namespace
 
+// Split-K partial sums of the allocation-free entry: a file-scope device
+// array (one copy per device, alive until the process ends). Host code never
+// passes the array's name to a kernel -- in host code it is a stand-in, not
+// a device address -- but the address hipGetSymbolAddress returns for the
+// current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+float *scratch_address(hipError_t *err) {
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && (dev < 0 || dev >= 64)) e = hipErrorInvalidDevice;
+    if (e != hipSuccess) {
+        *err = e;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    *err = hipSuccess;
+    return static_cast<float *>(addr[dev]);
+}
+
 int small_panel_splits(int64_t M, int64_t N, int64_t K, int max_splits) {
     if (!small_panel_fits(M, K, max_splits)) return 0;
     PanelKind kind;

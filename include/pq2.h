@@ -49,6 +49,8 @@
  *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), M above
  *                PQ2_LINEAR_MAX_M (pq2_linear), or an unknown activation
  *                format (pq2_quantize_act_16);
+ *  PQ2_ERR_SCRATCH (pq2_gemm_noalloc) the shape's split-K partial sums need
+ *                more than PQ2_NOALLOC_SCRATCH_BYTES;
  *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
  * Nothing is enqueued when a status other than PQ2_OK is returned, except for
  * PQ2_ERR_HIP. A fault during execution surfaces at the caller's next
@@ -76,7 +78,8 @@ typedef enum {
     PQ2_ERR_SHAPE = 2,
     PQ2_ERR_ALIGN = 3,
     PQ2_ERR_HIP = 4,
-    PQ2_ERR_ARG = 5
+    PQ2_ERR_ARG = 5,
+    PQ2_ERR_SCRATCH = 6
 } pq2_status;
 
 /* Kernel path selectors for pq2_gemm_group_dots. */
@@ -175,6 +178,27 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
                     const uint8_t *codes, const uint16_t *wscale, float *y,
                     int64_t M, int64_t N, int64_t K,
                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * pq2_gemm for callers that cannot allocate device memory or hold a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments as pq2_gemm without the workspace,
+ * same plan as pq2_gemm given pq2_gemm_workspace_bytes(M, N, K) bytes, so y
+ * is bit-identical to that call. The split-K partial sums go to a buffer of
+ * PQ2_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one per
+ * device (part of the loaded library, alive until the process ends); its
+ * address is looked up on the first call on each device. Shapes whose
+ * pq2_gemm_workspace_bytes exceeds PQ2_NOALLOC_SCRATCH_BYTES return
+ * PQ2_ERR_SCRATCH (nothing enqueued). Nothing is allocated or freed. Every
+ * call on a device shares that device's buffer: calls that may overlap on one
+ * device (different streams, or host threads) race on it and must be
+ * serialised by the caller; calls on one stream are ordered and safe. The
+ * buffer needs no clearing (every call writes all partial sums it reads).
+ */
+#define PQ2_NOALLOC_SCRATCH_BYTES (16u << 20)
+pq2_status pq2_gemm_noalloc(const int8_t *q, const float *s, const int32_t *t,
+                            const uint8_t *codes, const uint16_t *wscale, float *y,
+                            int64_t M, int64_t N, int64_t K, void *hip_stream);
 
 /*
  * pq2_gemm with a bfloat16 output, for callers whose activations are bfloat16

@@ -35,7 +35,7 @@ def test_abi_version_matches_header():
 
 
 def test_status_strings():
-    for st in range(6):
+    for st in range(7):
         s = pq2.lib.pq2_status_str(st)
         assert s and s.startswith(b"PQ2_")
     assert pq2.lib.pq2_status_str(99)
@@ -208,3 +208,13 @@ def test_probe_validation():
     assert h(P + 4, 100, None) == -1
     assert h(P, 0, None) == -1
     assert h(P, (1 << 28) + 1, None) == -1
+
+
+def test_noalloc_validation():
+    f = pq2.lib.pq2_gemm_noalloc
+    assert f(None, P, P, P, P, P, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, P, None, 1, 8, 128, None) == ERR_NULL
+    assert f(P, P, P, P, P, P, 1, 8, 129, None) == ERR_SHAPE
+    assert f(P, P, P, P, P, P, 0, 8, 128, None) == ERR_SHAPE
+    assert f(P, P, P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN   # codes needs 16 B
+    assert f(P, P, P, P, P, P + 2, 1, 8, 128, None) == ERR_ALIGN   # y needs 4 B
