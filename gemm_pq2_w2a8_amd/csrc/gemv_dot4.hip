@@ -73,37 +73,41 @@ __device__ __forceinline__ int token_of(int u, int n) {
     return m;
 }
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / kWave;
 constexpr int kLoadsPerBatch = 6;                 // uint4 code loads per lane per batch
 constexpr int64_t kMaxStage = 40960;              // activations staged per window (all tokens)
-constexpr int kQStagePer = kMaxStage / 16 / kGemvThreads;   // q chunks per thread
-constexpr int kSTStagePer = (kMaxStage / 128 + kGemvThreads - 1) / kGemvThreads;  // s, t per thread
 constexpr int64_t kPersistBlocks = 512;           // two blocks per CU
 constexpr int kXRound = 8;                        // groups per 32-lane slot and pass (fused)
 
-template <int LOG_CL, int RP>
+// NW waves per block (4 by default; 5 to 10 for the one-block-per-CU plans
+// of the decode shapes, see launch_mt), IB0 chunk iterations per batch (0:
+// kLoadsPerBatch / RP; those plans take a row's whole iteration count).
+template <int LOG_CL, int RP, int NW, int IB0 = 0>
 struct GemvShape {
     static constexpr int CL = 1 << LOG_CL;
     static constexpr int RL = kWave / CL;
     static constexpr int ROWS_PER_WAVE = RL * RP;
-    static constexpr int ROWS_PER_BLOCK = kGemvWaves * ROWS_PER_WAVE;
-    static constexpr int IB = kLoadsPerBatch / RP;    // chunk iterations per batch
+    static constexpr int ROWS_PER_BLOCK = NW * ROWS_PER_WAVE;
+    static constexpr int IB = IB0 > 0 ? IB0 : kLoadsPerBatch / RP;   // chunk iterations per batch
+    static constexpr int kThreads = NW * kWave;
+    static constexpr int kQStagePer = (kMaxStage / 16 + kThreads - 1) / kThreads;   // q chunks per thread
+    static constexpr int kSTStagePer = (kMaxStage / 128 + kThreads - 1) / kThreads; // s, t per thread
 };
 
 // LDS bytes per group and token of a window: q (128), s (4), t (4).
 constexpr int64_t kLdsPerGroup = kGroup + 8;
 
-template <int LOG_CL, int RP, int MT, bool DOTS, bool FUSED, bool Y16>
-__global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
+template <int LOG_CL, int RP, int MT, bool DOTS, bool FUSED, bool Y16, int NW, int IB0>
+__global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
     const float *__restrict__ x, const int8_t *__restrict__ q, const float *__restrict__ s,
     const int32_t *__restrict__ t, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ ws, float *__restrict__ y, uint16_t *__restrict__ y16,
     int32_t *__restrict__ d, int64_t M,
     int64_t N, int64_t K, int64_t window) {
     static_assert(!(FUSED && DOTS), "the fused variant writes y");
-    using S = GemvShape<LOG_CL, RP>;
+    using S = GemvShape<LOG_CL, RP, NW, IB0>;
     constexpr int CL = S::CL, RL = S::RL, IB = S::IB;
+    constexpr int kGemvThreads = S::kThreads;
+    constexpr int kQStagePer = S::kQStagePer, kSTStagePer = S::kSTStagePer;
     extern __shared__ uint4 smem[];
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -222,8 +226,12 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
             uint32_t *qw = reinterpret_cast<uint32_t *>(smem);
             const int ngr = MT * wg;
             auto quantize_pass = [&](int base) __attribute__((always_inline)) {
+                // rounds with a group for some slot (uniform, as in load_x): a
+                // block of many waves needs few of the kXRound
+                const int rounds = (ngr - base + kSlots - 1) / kSlots;
 #pragma unroll
                 for (int i = 0; i < kXRound; ++i) {
+                    if (i >= rounds) break;
                     const int graw = base + slot + kSlots * i;
                     const float4 xi[1] = {xv[i]};
                     uint32_t word[1];
@@ -429,48 +437,99 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_dot4_kernel(
     }
 }
 
-template <int LOG_CL, int RP, int MT>
+// window: the largest multiple of 64 * CL activations per token within
+// kMaxStage / MT (iterations then divide every window)
+template <int LOG_CL, int MT>
+constexpr int64_t gemv_window() {
+    return (kMaxStage / MT) / (64 << LOG_CL) * (64 << LOG_CL);
+}
+
+template <int LOG_CL, int RP, int MT, int NW, int IB0 = 0>
 hipError_t launch_cfg(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
                       const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    using S = GemvShape<LOG_CL, RP>;
+    using S = GemvShape<LOG_CL, RP, NW, IB0>;
     const int64_t n_rg = (N + S::ROWS_PER_BLOCK - 1) / S::ROWS_PER_BLOCK;
-    // window: the largest multiple of 64 * CL activations per token within
-    // kMaxStage / MT (iterations then divide every window)
-    constexpr int64_t kUnit = 64 * S::CL;
-    constexpr int64_t kWindow = (kMaxStage / MT) / kUnit * kUnit;
-    static_assert(kWindow >= kUnit, "window");
+    constexpr int64_t kWindow = gemv_window<LOG_CL, MT>();
+    static_assert(kWindow >= (64 << LOG_CL), "window");
     const int64_t window = K < kWindow ? K : kWindow;
     const int64_t blocks = K <= window ? (n_rg < kPersistBlocks ? n_rg : kPersistBlocks) : n_rg;
     const size_t lds = (size_t)(MT * (window / kGroup) * kLdsPerGroup);
+    const dim3 threads(S::kThreads);
     if (x) {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, true, false>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), lds, stream, x, nullptr, nullptr, nullptr, codes,
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, true, false, NW, IB0>), dim3((unsigned)blocks),
+                           threads, lds, stream, x, nullptr, nullptr, nullptr, codes,
                            out.ws, out.y, nullptr, nullptr, M, N, K, window);
     } else if (out.d) {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true, false, false>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), lds, stream, nullptr, q, nullptr, t, codes,
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, true, false, false, NW, IB0>), dim3((unsigned)blocks),
+                           threads, lds, stream, nullptr, q, nullptr, t, codes,
                            nullptr, nullptr, nullptr, out.d, M, N, K, window);
     } else if (out.y16) {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false, true>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), lds, stream, nullptr, q, out.s, t, codes, out.ws,
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false, true, NW, IB0>), dim3((unsigned)blocks),
+                           threads, lds, stream, nullptr, q, out.s, t, codes, out.ws,
                            nullptr, out.y16, nullptr, M, N, K, window);
     } else {
-        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false, false>), dim3((unsigned)blocks),
-                           dim3(kGemvThreads), lds, stream, nullptr, q, out.s, t, codes, out.ws,
+        hipLaunchKernelGGL((gemv_dot4_kernel<LOG_CL, RP, MT, false, false, false, NW, IB0>), dim3((unsigned)blocks),
+                           threads, lds, stream, nullptr, q, out.s, t, codes, out.ws,
                            out.y, nullptr, nullptr, M, N, K, window);
     }
     return hipGetLastError();
 }
 
-// Two rows per lane when a row slot is wide (CL >= 32): each wave then still
-// covers four rows, and every q word read from LDS serves both rows.
+// Launch plan. Where a row takes 3 (CL = 32) or 5 (CL = 16) chunk
+// iterations and the rows split into 5 to 10 waves per compute unit: one
+// block per CU with one row per lane, that many waves, and a row's whole
+// iteration count in one batch (no clamped re-reads). Every CU then streams
+// the same number of rows (with 16-row blocks of four waves, 5120 rows make
+// 320 blocks and 64 CUs carry two) and each wave's compute after its last
+// code word lands is short. MI355X, us per call, 64 rotating weight sets,
+// M = 1: 5120 x 6144 4.82 against 5.08 with four-wave blocks of two rows per
+// lane; 6144 x 5120 4.85 against 4.91. Otherwise four-wave blocks, two rows
+// per lane when a row slot is wide (CL >= 32: every q word read from LDS
+// then serves both rows), persistent over at most 512 blocks (17408 x 5120
+// would need 17 waves per CU: 8.02 us this way).
+template <int LOG_CL, int NW, int MT, int ITER>
+hipError_t launch_nw(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
+                     const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    return launch_cfg<LOG_CL, 1, MT, NW, ITER>(x, q, t, codes, out, M, N, K, stream);
+}
+
+template <int LOG_CL, int MT, int ITER>
+hipError_t launch_balanced(int64_t nw, const float *x, const int8_t *q, const int32_t *t,
+                           const uint8_t *codes, const GemmOut &out, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream) {
+    switch (nw) {
+        case 5: return launch_nw<LOG_CL, 5, MT, ITER>(x, q, t, codes, out, M, N, K, stream);
+        case 6: return launch_nw<LOG_CL, 6, MT, ITER>(x, q, t, codes, out, M, N, K, stream);
+        case 7:
+        case 8: return launch_nw<LOG_CL, 8, MT, ITER>(x, q, t, codes, out, M, N, K, stream);
+        default: return launch_nw<LOG_CL, 10, MT, ITER>(x, q, t, codes, out, M, N, K, stream);
+    }
+}
+
+template <int LOG_CL, int MT>
+hipError_t launch_mt(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
+                     const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    if constexpr ((LOG_CL == 4 || LOG_CL == 5) && MT <= 2) {
+        constexpr int64_t RL = kWave >> LOG_CL;
+        constexpr int64_t kIter = LOG_CL == 5 ? 3 : 5;
+        const int cus = device_cus();
+        if (K == kIter * (64 << LOG_CL) && cus > 0) {
+            const int64_t units = (N + RL - 1) / RL;
+            const int64_t nw = (units + cus - 1) / cus;
+            if (nw >= 5 && nw <= 10)
+                return launch_balanced<LOG_CL, MT, kIter>(nw, x, q, t, codes, out, M, N, K, stream);
+        }
+    }
+    constexpr int RP = (LOG_CL >= 5) ? 2 : 1;
+    return launch_cfg<LOG_CL, RP, MT, 4>(x, q, t, codes, out, M, N, K, stream);
+}
+
 template <int LOG_CL>
 hipError_t launch_cl(const float *x, const int8_t *q, const int32_t *t, const uint8_t *codes,
                      const GemmOut &out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    constexpr int RP = (LOG_CL >= 5) ? 2 : 1;
-    if (M == 1) return launch_cfg<LOG_CL, RP, 1>(x, q, t, codes, out, M, N, K, stream);
-    if (M == 2) return launch_cfg<LOG_CL, RP, 2>(x, q, t, codes, out, M, N, K, stream);
-    return launch_cfg<LOG_CL, RP, 4>(x, q, t, codes, out, M, N, K, stream);
+    if (M == 1) return launch_mt<LOG_CL, 1>(x, q, t, codes, out, M, N, K, stream);
+    if (M == 2) return launch_mt<LOG_CL, 2>(x, q, t, codes, out, M, N, K, stream);
+    return launch_mt<LOG_CL, 4>(x, q, t, codes, out, M, N, K, stream);
 }
 
 // x != nullptr: the fused variant (quantises x itself); else q, t from

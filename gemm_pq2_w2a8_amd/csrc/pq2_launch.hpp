@@ -17,6 +17,9 @@ struct GemmOut {
     uint16_t *y16 = nullptr;  // bfloat16 [M][N] instead of y, when set
 };
 
+// Compute units of the current device (read once per device; 0 if unknown).
+int device_cus();
+
 // format 0: float32 x; 1: bfloat16; 2: IEEE binary16 (each widened exactly).
 hipError_t launch_quantize(const void *x, int format, int8_t *q, float *s, int32_t *t,
                            int64_t M, int64_t K, hipStream_t stream);

@@ -1127,6 +1127,8 @@ hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t 
     return hipGetLastError();
 }
 
+int device_cus() { return dev_limits().cus; }
+
 bool small_panel_ring_fits(int64_t M, int64_t K, int max_splits) {
     if (M < 1 || M > 16 || K > kPanelMaxK || K / kGroup < 16) return false;
     return plan_ring(M, 16, K, dev_limits(), max_splits).S > 0;
