@@ -15,22 +15,24 @@ constexpr uint32_t kNever = 0x9E3779B9u; // folded value that triggers the one s
 
 // Grid-stride streaming read. Lane i of a wave reads the 16 bytes after
 // lane i - 1, so each load instruction covers 1 KB of contiguous memory.
+// Each round issues all of a thread's kUnroll loads (those past the end
+// masked off) before it uses any of them, so a thread never waits for one
+// load before issuing the next.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4 *__restrict__ src,
                                                                int64_t n16,
                                                                uint32_t *__restrict__ sink) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+         i += kUnroll * stride) {
         uint4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+        for (int u = 0; u < kUnroll; ++u) {
+            v[u] = make_uint4(0, 0, 0, 0);
+            if (i + u * stride < n16) v[u] = src[i + u * stride];
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    for (; i < n16; i += stride) {
-        const uint4 v = src[i];
-        acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     if (acc == kNever) sink[blockIdx.x] = acc;
 }

@@ -27,8 +27,8 @@ extern "C" {
 /*
  * Streaming read: `blocks` blocks of 256 threads read the `bytes` bytes at
  * src once, with 16-byte loads (consecutive lanes on consecutive 16-byte
- * pieces, a grid-stride loop with eight loads in flight per thread), and
- * fold them into one word per thread. Nothing is written unless a block's
+ * pieces; a grid-stride loop whose rounds issue up to eight loads per
+ * thread before using any), and fold them into one word per thread. Nothing is written unless a block's
  * folded value equals a fixed constant, so the write traffic is at most one
  * word per block into sink (uint32 [blocks]).
  *   src: 16-byte aligned; bytes: a positive multiple of 16;
