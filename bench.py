@@ -49,6 +49,13 @@ def quant_bytes(M, K):
 LINEAR_MAX_M = 4   # PQ2_LINEAR_MAX_M
 
 
+def linear_bytes(M, N, K):
+    """Algorithmic HBM bytes of the one-launch pq2_linear: codes + fp16 group
+    scales + float32 x + y (q, s and t never leave the kernel)."""
+    G = K // GROUP
+    return N * K // 4 + 2 * N * G + 4 * M * K + 4 * M * N
+
+
 def step_bytes(M, N, K):
     """Algorithmic HBM bytes of quantise + GEMM (q, s, t written and read back)."""
     return gemm_bytes(M, N, K) + quant_bytes(M, K)
@@ -502,24 +509,38 @@ def layer_step(m, torch, pq2, stream):
     # quantises its own input
     shares_input = tuple(i > 0 and synth.LAYER_SHAPES[i] == synth.LAYER_SHAPES[i - 1]
                          for i in range(len(synth.LAYER_SHAPES)))
+    # one launch (pq2_linear, quantisation inside the GEMV) where that measured
+    # faster than pq2_quantize_act + pq2_gemm on MI355X: one token row with
+    # K <= 6144 (6144 x 5120: 6.93 against 7.24 us; 5120 x 6144: 6.48 against
+    # 7.28); the two-launch step elsewhere (gate and up share a quantisation;
+    # at K = 17408 and from two rows on, quantising in every block costs more
+    # than the separate launch)
+    fused = tuple(m == 1 and k <= 6144 and not shares_input[i] and
+                  not (i + 1 < len(synth.LAYER_SHAPES) and shares_input[i + 1])
+                  for i, (n, k) in enumerate(synth.LAYER_SHAPES))
     calls = []
     for projs in layers:
         for i, (codes, ws, n, k) in enumerate(projs):
             q, s, t = bufs[k]
-            calls.append((not shares_input[i], xs[k].data_ptr(), q.data_ptr(), s.data_ptr(),
-                          t.data_ptr(), codes.data_ptr(), ws.data_ptr(), ys[n].data_ptr(), n, k))
-    quant, gemm = lib.pq2_quantize_act, lib.pq2_gemm
+            calls.append((fused[i], not shares_input[i], xs[k].data_ptr(), q.data_ptr(),
+                          s.data_ptr(), t.data_ptr(), codes.data_ptr(), ws.data_ptr(),
+                          ys[n].data_ptr(), n, k))
+    quant, gemm, linear = lib.pq2_quantize_act, lib.pq2_gemm, lib.pq2_linear
 
     def step(after=None):
-        for (qz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
-            if qz:
-                quant(xp, qp, sp, tp, m, k, stream)
-            gemm(qp, sp, tp, cp, wp, yp, m, n, k, wkp, wsz, stream)
+        for (fz, qz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
+            if fz:
+                linear(xp, cp, wp, yp, m, n, k, stream)
+            else:
+                if qz:
+                    quant(xp, qp, sp, tp, m, k, stream)
+                gemm(qp, sp, tp, cp, wp, yp, m, n, k, wkp, wsz, stream)
             if after is not None:
                 after()
 
     step.buffers = (layers, xs, bufs, ys, work)   # the launches hold raw pointers into these
     step.workspace_bytes = wsz
+    step.fused = fused
     return step, shares_input
 
 
@@ -538,16 +559,22 @@ def run_layers(args, m, torch, pq2, steps, trials):
     ms = median(runs) / steps
     total = 0
     for i, (n, k) in enumerate(synth.LAYER_SHAPES):
-        total += gemm_bytes(m, n, k) + (0 if shares_input[i] else quant_bytes(m, k))
+        if step.fused[i]:
+            total += linear_bytes(m, n, k)
+        else:
+            total += gemm_bytes(m, n, k) + (0 if shares_input[i] else quant_bytes(m, k))
     total *= synth.N_LAYERS
     gbs = total / (ms * 1e-3) / 1e9
+    n_quant = sum(not shares_input[i] and not step.fused[i] for i in range(len(shares_input)))
     return {"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps,
             "warmup": 2, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
             "config": {"workload": f"layer64_m{m}", "M": m, "layers": synth.N_LAYERS,
                        "gemms_per_step": 5 * synth.N_LAYERS,
-                       "quantisations_per_step": (5 - sum(shares_input)) * synth.N_LAYERS,
-                       "projection": "pq2_quantize_act + pq2_gemm (gate and up share one quantisation)",
+                       "quantiser_launches_per_step": n_quant * synth.N_LAYERS,
+                       "projection": "pq2_quantize_act + pq2_gemm (gate and up share one "
+                                     "quantisation), or pq2_linear where that is faster",
+                       "fused_projections_per_layer": int(sum(step.fused)),
                        "algorithmic_bytes_per_step": total, "trials": trials,
                        "trial_ms": [round(v / steps, 4) for v in runs],
                        "workspace_bytes": step.workspace_bytes},

@@ -170,8 +170,9 @@ def test_layer64_step(pq2, M):
     """The 64-layer decode step as the benchmark issues it: per layer the
     projections 5120 -> 6144, 6144 -> 5120, 5120 -> 17408 twice (gate and up,
     which share one quantisation) and 17408 -> 5120, back to back on one
-    stream with one workspace; 32 sampled outputs of every projection (the last
-    row and column included) against the oracle."""
+    stream with one workspace, one token row's K <= 6144 projections through
+    the one-launch pq2_linear; 32 sampled outputs of every projection (the
+    last row and column included) against the oracle."""
     print(f"config layer64 M={M}", flush=True)
     gen = torch.Generator(device="cuda").manual_seed(M)
     shapes = synth.LAYER_SHAPES
@@ -189,16 +190,22 @@ def test_layer64_step(pq2, M):
             y = torch.empty((M, n), dtype=torch.float32, device="cuda")
             projs.append((layer, i, n, k, codes, ws, y))
     shares = [i > 0 and shapes[i] == shapes[i - 1] for i in range(len(shapes))]
+    fused = [M == 1 and k <= 6144 and not shares[i] and
+             not (i + 1 < len(shapes) and shares[i + 1]) for i, (_, k) in enumerate(shapes)]
     torch.cuda.synchronize()
     for (layer, i, n, k, codes, ws, y) in projs:         # the step, no host syncs
+        if fused[i]:
+            pq2.pq2_linear(xd[k], codes, ws, y)
+            continue
         q, s, t = qst[k]
         if not shares[i]:
             pq2.pq2_quantize_act(xd[k], q, s, t)
         pq2.pq2_gemm(q, s, t, codes, ws, y, workspace=work)
     torch.cuda.synchronize()
     qso = {k: oracle.quantize(v) for k, v in xs.items()}
-    for k, (q, s, t) in qst.items():
-        check_qst(q, s, t, *qso[k])
+    for i, (_, k) in enumerate(shapes):
+        if not fused[i]:
+            check_qst(*qst[k], *qso[k])
     rng = np.random.default_rng(64 + M)
     worst = 0.0
     for (layer, i, n, k, codes, ws, y) in projs:
