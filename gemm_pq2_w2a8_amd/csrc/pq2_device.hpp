@@ -243,6 +243,14 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void *ld
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, 0, 0, 0);
 }
 
+// The same copy from voff + soff, soff wave-uniform (an SGPR operand). A lane
+// whose voff is kCopyOob stays out of range whatever soff is; in-range lanes
+// must keep voff + soff inside the resource.
+__device__ __forceinline__ void copy16_to_lds_at(__amdgpu_buffer_rsrc_t r, void *lds, int voff,
+                                                 int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, soff, 0, 0);
+}
+
 // Block barrier after this wave's LDS accesses have completed. Without the
 // release fence of __syncthreads, which would also wait for every buffer ->
 // LDS copy in flight; the copies a step needs are waited for explicitly.

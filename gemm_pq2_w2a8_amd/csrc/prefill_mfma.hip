@@ -683,6 +683,297 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
     }
 }
 
+// ---------------------------------------------------------------- wide variant
+//
+// Block tile 256 weight rows x 128 tokens: four waves side by side along N,
+// each owning 64 rows x 128 tokens (4 x 8 MFMA tiles), so the code words a
+// wave decodes per group serve eight token tiles, and the block's buffer ->
+// LDS copies move 24 KB per group for 32768 outputs (8 KB codes, 16 KB
+// activations). The scale products s[m] * ws[n] come from the matrix core:
+// per group, token tile and row tile one v_mfma_f32_4x4x1_16b forms the
+// outer products of weight and token scales in sixteen 4 x 4 blocks, lane
+// 4k + i supplying row i and column i of block k: with the weight scale of
+// row 4 (lane / 16) + (lane % 4) and the token scale of token lane % 16 as
+// operands, block k's result lands in the lanes and registers that hold the
+// int8 results of the same outputs. That leaves the VALU one conversion and
+// one FMA per output and group (measured here, MFMA and VALU time add up
+// rather than overlap, so VALU work moved to the matrix core is time saved
+// as long as it costs fewer cycles there). The product is the correctly
+// rounded float32 product the other tiles form with a mixed-precision FMA,
+// and the accumulation order over groups is the same: results are
+// identical.
+// Staging as in the ring variant, with two stages and the group offset of
+// every copy in the SGPR operand: stage g + 1 (and every eight groups the
+// next scale chunk) is copied while group g is computed.
+template <bool DOTS>
+struct PfWide {
+    static constexpr int T = 256, BN = 256, BM = 128, WN = 4, WM = 8;
+    static constexpr int kCodeInst = 2 * BN / T;          // code units per thread
+    static constexpr int kQInst = 8 * BM / T;             // activation units per thread
+    static constexpr int kStageInst = kCodeInst + kQInst;
+    static constexpr int kQBase = 2 * BN * 16;            // activation bytes of a stage
+    static constexpr int kStageBytes = kQBase + 8 * BM * 16;
+    // scale chunk of 8 groups: ws unit per row (8 halves), then s and t in
+    // two units per token (8 values each)
+    static constexpr int kSBase = BN * 16;
+    static constexpr int kTBase = kSBase + BM * 32;
+    static constexpr int kScaleBytes = kTBase + BM * 32;
+    static constexpr int kScaleInst = DOTS ? 1 : 3;
+    static constexpr int kLdsBytes = 2 * kStageBytes + 2 * kScaleBytes;
+    static_assert(T == BN && 2 * BM == T, "one scale unit per thread and table");
+};
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <bool DOTS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__ s,
+                         const int32_t *__restrict__ t, const uint8_t *__restrict__ codes,
+                         const uint16_t *__restrict__ ws, float *__restrict__ y,
+                         uint16_t *__restrict__ y16, int32_t *__restrict__ d, int64_t M,
+                         int64_t N, int64_t K) {
+    using L = PfWide<DOTS>;
+    constexpr int T = L::T, WN = L::WN, WM = L::WM;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *const stage0 = smem;
+    uint8_t *const stage1 = smem + L::kStageBytes;
+    uint8_t *const scl0 = smem + 2 * L::kStageBytes;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int r = lane & 15, lg = lane >> 4;
+    const int half = lg & 1;
+    const int sh0 = 2 * (lg >> 1);
+    const int G = (int)(K / kGroup);
+    const int KB = (int)(K / 4);
+
+    const int64_t tiles_n = (N + L::BN - 1) / L::BN;
+    const int64_t tiles_m = (M + L::BM - 1) / L::BM;
+    const int64_t tile = xcd_tile(blockIdx.x, tiles_n * tiles_m);
+    const int64_t n0 = (tile % tiles_n) * L::BN;
+    const int64_t m0 = (tile / tiles_n) * L::BM;
+    const int rows = N - n0 < L::BN ? (int)(N - n0) : L::BN;
+    const int toks = M - m0 < L::BM ? (int)(M - m0) : L::BM;
+
+    const __amdgpu_buffer_rsrc_t rs_codes = make_rsrc(codes + n0 * KB, (int64_t)rows * KB);
+    const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(q + m0 * K, (int64_t)toks * K);
+    const __amdgpu_buffer_rsrc_t rs_t = make_rsrc(t + m0 * G, (int64_t)toks * G * 4);
+    const __amdgpu_buffer_rsrc_t rs_ws = make_rsrc(DOTS ? nullptr : ws + n0 * G, DOTS ? 0 : (int64_t)rows * G * 2);
+    const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(DOTS ? nullptr : s + m0 * G, DOTS ? 0 : (int64_t)toks * G * 4);
+
+    // Copy sources of group 0 (group g adds 32 g or 128 g through the SGPR
+    // offset). Unit u of copy instruction i is i * T + tid; code unit
+    // 2 row + (half ^ ((row >> 2) & 1)), activation unit 8 token +
+    // (piece ^ (token & 7)), as in the ring variant. Rows and tokens past the
+    // end are never read (their LDS units receive zeros).
+    int coff[L::kCodeInst], qoff[L::kQInst];
+#pragma unroll
+    for (int i = 0; i < L::kCodeInst; ++i) {
+        const int u = i * T + tid;
+        const int row = u >> 1;
+        const int h = (u & 1) ^ ((row >> 2) & 1);
+        coff[i] = row < rows ? row * KB + 16 * h : kCopyOob;
+    }
+#pragma unroll
+    for (int i = 0; i < L::kQInst; ++i) {
+        const int u = i * T + tid;
+        const int tok = u >> 3;
+        const int piece = (u & 7) ^ (tok & 7);
+        qoff[i] = tok < toks ? tok * (int)K + 16 * piece : kCopyOob;
+    }
+    // scale chunk c: ws unit tid = row tid, groups 8c .. 8c + 7 (byte offset
+    // 2 (row G + 8c)); s / t unit tid = token tid / 2, groups 8c + 4 (tid & 1)
+    // .. + 3 (byte offset 4 (token G + 8c + 4 (tid & 1)))
+    const int wsoff = tid < rows ? 2 * tid * G : kCopyOob;
+    const int tokoff = (tid >> 1) < toks ? 4 * ((tid >> 1) * G + 4 * (tid & 1)) : kCopyOob;
+
+    auto issue_stage = [&](int g, uint8_t *st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < L::kCodeInst; ++i)
+            copy16_to_lds_at(rs_codes, st + 16 * (i * T + kWave * wave), coff[i], 32 * g);
+#pragma unroll
+        for (int i = 0; i < L::kQInst; ++i)
+            copy16_to_lds_at(rs_q, st + L::kQBase + 16 * (i * T + kWave * wave), qoff[i],
+                             kGroup * g);
+    };
+    auto issue_scales = [&](int c) __attribute__((always_inline)) {
+        uint8_t *sc = scl0 + (c & 1) * L::kScaleBytes + 16 * kWave * wave;
+        if (!DOTS) {
+            copy16_to_lds_at(rs_ws, sc, wsoff, 16 * c);
+            copy16_to_lds_at(rs_s, sc + L::kSBase, tokoff, 32 * c);
+        }
+        copy16_to_lds_at(rs_t, sc + L::kTBase, tokoff, 32 * c);
+    };
+
+    const int row_base = 64 * wave;
+    // per-lane LDS byte offsets: code words of row tile a at cbase + 512 a;
+    // activation pieces lg and lg + 4 of token tile b at qb0 / qb1 + 2048 b;
+    // s / t of token tile b, group j at tokb + 512 b + 4 j; the outer-product
+    // weight scale of row tile a at wsb + 256 a + 2 j
+    const int cbase = 32 * (row_base + r) + 16 * (half ^ ((r >> 2) & 1));
+    const int qb0 = L::kQBase + 128 * r + 16 * (lg ^ (r & 7));
+    const int qb1 = L::kQBase + 128 * r + 16 * ((lg + 4) ^ (r & 7));
+    const int tokb = 32 * r;
+    const int wsb = 16 * (row_base + 4 * lg + (lane & 3));
+
+    float acc[WN][WM][4];
+#pragma unroll
+    for (int a = 0; a < WN; ++a)
+#pragma unroll
+        for (int b = 0; b < WM; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
+
+    auto compute = [&](const uint8_t *st, int g) __attribute__((always_inline)) {
+        const uint8_t *sc = scl0 + ((g >> 3) & 1) * L::kScaleBytes;
+        const int j = g & 7;
+        v4i w[WN];
+#pragma unroll
+        for (int a = 0; a < WN; ++a) w[a] = *reinterpret_cast<const v4i *>(st + cbase + 512 * a);
+        // weight-scale operand of the outer products: lane 4k + i of row tile a
+        // supplies ws of row 16 a + 4 (lane / 16) + i
+        float wsa[WN];
+        float sv[WM];
+        if (!DOTS) {
+#pragma unroll
+            for (int a = 0; a < WN; ++a)
+                wsa[a] = half_bits_to_float(
+                    *reinterpret_cast<const uint16_t *>(sc + wsb + 256 * a + 2 * j));
+#pragma unroll
+            for (int b = 0; b < WM; ++b)
+                sv[b] = *reinterpret_cast<const float *>(sc + L::kSBase + tokb + 512 * b + 4 * j);
+        }
+        v4i a0[WN], a1[WN];
+#pragma unroll
+        for (int a = 0; a < WN; ++a) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t sh = (uint32_t)w[a][k] >> sh0;
+                a0[a][k] = (int)(sh & kPlaneMask);
+                a1[a][k] = (int)((sh >> 4) & kPlaneMask);
+            }
+        }
+        // token-tile pipeline: activations of tile b + 2 are read and the
+        // MFMAs of tile b + 1 issued before tile b's epilogue
+        v4i bq0[2], bq1[2];
+        int ttq[2];
+        auto load_tile = [&](int b, int slot) __attribute__((always_inline)) {
+            bq0[slot] = *reinterpret_cast<const v4i *>(st + qb0 + 2048 * b);
+            bq1[slot] = *reinterpret_cast<const v4i *>(st + qb1 + 2048 * b);
+            ttq[slot] = *reinterpret_cast<const int32_t *>(sc + L::kTBase + tokb + 512 * b + 4 * j);
+        };
+        v4i c[2][WN];
+        auto mma = [&](int slot) __attribute__((always_inline)) {
+            const int tt = ttq[slot];
+            const v4i seed = {-tt, -tt, -tt, -tt};
+#pragma unroll
+            for (int a = 0; a < WN; ++a) c[slot][a] = mfma16x16x64(a0[a], bq0[slot], seed);
+#pragma unroll
+            for (int a = 0; a < WN; ++a) c[slot][a] = mfma16x16x64(a1[a], bq1[slot], c[slot][a]);
+        };
+        load_tile(0, 0);
+        load_tile(1, 1);
+        mma(0);
+#pragma unroll
+        for (int b = 0; b < WM; ++b) {
+            const int cur = b & 1;
+            if (b + 2 < WM) load_tile(b + 2, cur);
+            if (b + 1 < WM) mma(cur ^ 1);
+            if (DOTS) {
+                const int64_t m = m0 + 16 * b + r;
+                int64_t at = (m * N + n0 + row_base + 4 * lg) * G + g;
+                // recomputed per tile: hoisted, the 128 store addresses of a group
+                // would not fit in registers
+                asm volatile("" : "+v"(at));
+#pragma unroll
+                for (int a = 0; a < WN; ++a)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t n = n0 + row_base + 16 * a + 4 * lg + i;
+                        if (m < M && n < N) d[at + (int64_t)(16 * a + i) * G] = c[cur][a][i];
+                    }
+            } else {
+#pragma unroll
+                for (int a = 0; a < WN; ++a) {
+                    const v4f sp = __builtin_amdgcn_mfma_f32_4x4x1f32(wsa[a], sv[b], v4f{}, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[a][b][i] = fmaf((float)c[cur][a][i], sp[i], acc[a][b][i]);
+                    // keeps the tile's epilogue here: left free, the compiler sinks it
+                    // past the next group's barrier and holds every MFMA result of the
+                    // group in scratch memory meanwhile
+                    asm volatile("" : "+v"(acc[a][b][0]), "+v"(acc[a][b][1]), "+v"(acc[a][b][2]),
+                                 "+v"(acc[a][b][3]));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // one group: stage g in LDS once this wave's copies older than the last
+    // scale chunk have landed and every wave has passed the barrier
+    auto step = [&](int g, const uint8_t *cur, uint8_t *nxt) __attribute__((always_inline)) {
+        if (g >= 1 && ((g - 1) & 7) == 0 && g + 7 < G)
+            wait_vmem<L::kScaleInst>();          // chunk (g - 1) / 8 + 1 may still be in flight
+        else
+            wait_vmem<0>();
+        ring_barrier();
+        if (g + 1 < G) issue_stage(g + 1, nxt);
+        if ((g & 7) == 0 && g + 8 < G) issue_scales((g >> 3) + 1);
+        compute(cur, g);
+    };
+
+    issue_scales(0);
+    issue_stage(0, stage0);
+    for (int g = 0; g < G; g += 2) {             // G is a multiple of 8
+        step(g, stage0, stage1);
+        step(g + 1, stage1, stage0);
+    }
+    wait_vmem<0>();
+
+    if (!DOTS) {
+        // four outputs of a lane as one 16-byte store where y allows it
+        const bool vec_y = !y16 && (N & 3) == 0 && ((uintptr_t)y & 15) == 0;
+#pragma unroll
+        for (int b = 0; b < WM; ++b) {
+            const int64_t m = m0 + 16 * b + r;
+            if (m >= M) continue;
+#pragma unroll
+            for (int a = 0; a < WN; ++a) {
+                const int64_t nb = n0 + row_base + 16 * a + 4 * lg;
+                if (vec_y && nb + 3 < N) {
+                    *reinterpret_cast<float4 *>(y + m * N + nb) =
+                        make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (nb + i < N) store_y(y, y16, m * N + nb + i, acc[a][b][i]);
+                }
+            }
+        }
+    }
+}
+
+template <bool DOTS>
+hipError_t launch_wide_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                            const GemmOut &out, int64_t M, int64_t N, int64_t K,
+                            hipStream_t stream) {
+    using L = PfWide<DOTS>;
+    const int64_t blocks = ((N + L::BN - 1) / L::BN) * ((M + L::BM - 1) / L::BM);
+    hipLaunchKernelGGL((prefill_wide_kernel<DOTS>), dim3((unsigned)blocks), dim3(L::T),
+                       (size_t)L::kLdsBytes, stream, q, DOTS ? nullptr : out.s, t, codes,
+                       DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y,
+                       DOTS ? nullptr : out.y16, DOTS ? out.d : nullptr, M, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                       const GemmOut &out, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream) {
+    return out.d ? launch_wide_dots<true>(q, t, codes, out, M, N, K, stream)
+                 : launch_wide_dots<false>(q, t, codes, out, M, N, K, stream);
+}
+
 template <int WN, int WM, int WAVES_N, int WAVES_M, int R>
 hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
                            const GemmOut &out, int64_t M, int64_t N, int64_t K,
@@ -726,6 +1017,8 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 }  // namespace
 
 // Tile configurations (rows x tokens, waves, prefetch depth):
+//  10: 256 x 128, 4 x 1 waves of 64 x 128, ring of 2 stages, scale products
+//      on the matrix core (the wide variant)
 //   0: 128 x 128, 2 x 2 waves of 64 x 64, depth 1
 //   6: 128 x 128, 2 x 2 waves of 64 x 64, ring of 2 stages (buffer -> LDS copies)
 //   7:  64 x 64,  2 x 2 waves of 32 x 32, depth 2
@@ -763,12 +1056,17 @@ hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *code
     // a multiple of 8 and offsets stay below their sentinel: 3-20 % faster;
     // the 64 x 64 ring (88 VGPRs, 31 KB of LDS) runs five blocks per CU. Ring
     // forms of the 32 x 32, 64 x 128 tiles and a 3-stage 64 x 64 ring were
-    // slower.
+    // slower. The wide variant, where it gives at least two tiles per CU,
+    // is faster again: M = 4096, N = 17408: 524 us against 672 for the
+    // 128 x 128 ring; N = 5120: 184 against 216; at M = 512, N = 17408 (272
+    // tiles) it loses to the 64 x 64 ring (117 against 107).
     const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
-    const int cfg = tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
+    const int cfg = ring && tiles(256, 128) >= 2 * kCUs ? 10
+                  : tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
                   : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
                                                 : 9;
     switch (cfg) {
+        case 10: return launch_wide(q, t, codes, out, M, N, K, stream);
         case 6: return launch_ring_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 7: return launch_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 8: return launch_ring_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);

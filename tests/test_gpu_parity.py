@@ -224,13 +224,16 @@ def test_group_dots_prefill(pq2, M, N, K):
                                   oracle.group_dots(qn, codes))
 
 
-@pytest.mark.parametrize("M,N,K", [(4000, 4200, 1024), (4096, 4100, 1152), (2000, 2100, 2048),
-                                   (2048, 2100, 1152)])
+@pytest.mark.parametrize("M,N,K", [(4000, 4200, 1024), (4100, 8300, 2048), (4001, 4203, 1024),
+                                   (4096, 4100, 1152), (2000, 2100, 2048), (2048, 2100, 1152)])
 def test_prefill_large_tiles_sampled(pq2, M, N, K):
-    """Shapes that give four 128 x 128 tiles per CU (the first two) or two 64 x 64
-    tiles per CU (the last two): G a multiple of 8 takes the variants whose stages
-    arrive by buffer -> LDS copies (ragged M and N, scale chunks of 8 groups),
-    G = 9 the register-staged ones. Exact sampled group dots, sampled y within
+    """Shapes with at least two 256 x 128 tiles per CU and G a multiple of 8
+    (the first three: the wide tile, ragged in M and N, the last token tile 4
+    tokens wide in the second, N odd in the third so y is stored element by
+    element), four 128 x 128 tiles per CU (the fourth) or two 64 x 64 tiles
+    per CU (the last two): G a multiple of 8 takes the variants whose stages
+    arrive by buffer -> LDS copies (scale chunks of 8 groups), G = 9 the
+    register-staged ones. Exact sampled group dots, sampled y within
     tolerance, exact y with unit scales."""
     print(f"prefill large tiles M={M} N={N} K={K}", flush=True)
     assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PREFILL
