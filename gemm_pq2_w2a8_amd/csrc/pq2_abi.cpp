@@ -36,16 +36,19 @@ int max_splits(const void *work, size_t work_bytes, int64_t M, int64_t N) {
     return work ? splits_for_bytes(work_bytes, M, N) : 1;
 }
 
+// work / work_bytes: the caller's workspace (nullptr / 0 when none); max_s:
+// the K chunks of M x N partial sums it holds for the panel kernel.
 pq2_status run_path(int path, const int8_t *q, const int32_t *t, const uint8_t *codes,
                     const pq2::GemmOut &out, int64_t M, int64_t N, int64_t K, int max_s,
-                    float *work, hipStream_t stream) {
+                    float *work, size_t work_bytes, hipStream_t stream) {
     switch (path) {
         case PQ2_PATH_GEMV:
             return from_hip(pq2::launch_gemv(q, t, codes, out, M, N, K, stream));
         case PQ2_PATH_SMALL:
             return from_hip(pq2::launch_small(q, t, codes, out, M, N, K, stream));
         case PQ2_PATH_PREFILL:
-            return from_hip(pq2::launch_prefill(q, t, codes, out, M, N, K, stream));
+            return from_hip(pq2::launch_prefill(q, t, codes, out, M, N, K, work,
+                                                work ? work_bytes : 0, stream));
         case PQ2_PATH_PANEL:
             return from_hip(pq2::launch_small_panel(q, t, codes, out, M, N, K, max_s, work,
                                                     stream));
@@ -94,7 +97,9 @@ pq2_status resolve_path(int &path, int64_t M, int64_t N, int64_t K, int max_s) {
 // Bytes of partial sums pq2_gemm's plan for this shape writes when the
 // workspace is large enough (0: its plan does not split K).
 size_t workspace_need(int64_t M, int64_t N, int64_t K) {
-    if (auto_path(M, N, K, pq2::kPanelMaxSplits) != PQ2_PATH_PANEL) return 0;
+    const int path = auto_path(M, N, K, pq2::kPanelMaxSplits);
+    if (path == PQ2_PATH_PREFILL) return pq2::prefill_workspace_bytes(M, N, K);
+    if (path != PQ2_PATH_PANEL) return 0;
     const int S = pq2::small_panel_splits(M, N, K, pq2::kPanelMaxSplits);
     return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
@@ -167,7 +172,8 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t, const uin
     const int max_s = max_splits(workspace, workspace_bytes, M, N);
     const pq2::GemmOut out{y, nullptr, s, wscale};
     return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s,
-                    static_cast<float *>(workspace), static_cast<hipStream_t>(hip_stream));
+                    static_cast<float *>(workspace), workspace_bytes,
+                    static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t, const uint8_t *codes,
@@ -179,7 +185,8 @@ pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t, cons
     pq2::GemmOut out{nullptr, nullptr, s, wscale};
     out.y16 = y;
     return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s,
-                    static_cast<float *>(workspace), static_cast<hipStream_t>(hip_stream));
+                    static_cast<float *>(workspace), workspace_bytes,
+                    static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_gemm_noalloc(const int8_t *q, const float *s, const int32_t *t,
@@ -188,7 +195,11 @@ pq2_status pq2_gemm_noalloc(const int8_t *q, const float *s, const int32_t *t,
     static_assert(PQ2_NOALLOC_SCRATCH_BYTES == pq2::kScratchBytes, "scratch size in the header");
     pq2_status st = check_gemm(q, s, t, codes, wscale, y, 4, nullptr, M, N, K);
     if (st != PQ2_OK) return st;
-    const size_t need = workspace_need(M, N, K);
+    // The prefill plan splits only as far as its partial sums fit the scratch
+    // array (down to no split); a panel plan that needs more is refused.
+    const bool prefill = auto_path(M, N, K, pq2::kPanelMaxSplits) == PQ2_PATH_PREFILL;
+    size_t need = workspace_need(M, N, K);
+    if (prefill && need > pq2::kScratchBytes) need = pq2::kScratchBytes;
     if (need > pq2::kScratchBytes) return PQ2_ERR_SCRATCH;
     float *work = nullptr;
     if (need > 0) {
@@ -199,7 +210,7 @@ pq2_status pq2_gemm_noalloc(const int8_t *q, const float *s, const int32_t *t,
     // the same plan pq2_gemm takes with a workspace of exactly `need` bytes
     const int max_s = need > 0 ? splits_for_bytes(need, M, N) : 1;
     const pq2::GemmOut out{y, nullptr, s, wscale};
-    return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s, work,
+    return run_path(auto_path(M, N, K, max_s), q, t, codes, out, M, N, K, max_s, work, need,
                     static_cast<hipStream_t>(hip_stream));
 }
 
@@ -218,7 +229,7 @@ pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t, cons
     if (st != PQ2_OK) return st;
     const pq2::GemmOut out{y, nullptr, s, wscale};
     return run_path(path, q, t, codes, out, M, N, K, max_s, static_cast<float *>(workspace),
-                    static_cast<hipStream_t>(hip_stream));
+                    workspace_bytes, static_cast<hipStream_t>(hip_stream));
 }
 
 pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
@@ -247,7 +258,7 @@ pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t 
     st = resolve_path(path, M, N, K, pq2::kPanelMaxSplits);
     if (st != PQ2_OK) return st;
     const pq2::GemmOut out{nullptr, d, nullptr, nullptr};
-    return run_path(path, q, t, codes, out, M, N, K, pq2::kPanelMaxSplits, nullptr,
+    return run_path(path, q, t, codes, out, M, N, K, pq2::kPanelMaxSplits, nullptr, 0,
                     static_cast<hipStream_t>(hip_stream));
 }
 

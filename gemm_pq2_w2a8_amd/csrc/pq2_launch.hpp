@@ -79,8 +79,15 @@ hipError_t launch_split_sum(const float *part, float *y, uint16_t *y16, int64_t 
 // Blocks the tiled prefill kernel launches for M x N (its tile rule).
 int64_t prefill_blocks(int64_t M, int64_t N);
 
+// Bytes of partial sums the prefill plan for M x N x K uses when it splits
+// the K range of its last tiles (0: its plan does not split).
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// work: device buffer of work_bytes (or nullptr); the plan splits its last
+// tiles into as many K chunks as their partial sums fit there (with no room,
+// or for group dots, nothing is split).
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                          const GemmOut &out, int64_t M, int64_t N, int64_t K,
-                          hipStream_t stream);
+                          const GemmOut &out, int64_t M, int64_t N, int64_t K, float *work,
+                          size_t work_bytes, hipStream_t stream);
 
 }  // namespace pq2

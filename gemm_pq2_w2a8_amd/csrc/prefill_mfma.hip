@@ -725,13 +725,42 @@ struct PfWide {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// K split of the last tiles of the wide variant (see prefill_wide_kernel);
+// full = every tile and chunks = 1 when nothing is split.
+struct WideSplit {
+    int64_t full;        // tiles computed whole
+    int chunks;          // K chunks per remaining tile
+    int chunk_groups;    // groups per chunk (even)
+    float *part;         // (tiles - full) * chunks partial [BM][BN] tiles
+};
+
+// y of the split tiles: the chunks' partial sums added in chunk order. One
+// block per (tile, token row), one thread per weight row.
+__global__ __launch_bounds__(256) void wide_tail_sum_kernel(const float *__restrict__ part,
+                                                            float *__restrict__ y,
+                                                            uint16_t *__restrict__ y16, int64_t M,
+                                                            int64_t N, WideSplit sp) {
+    constexpr int BM = 128, BN = 256;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t v = blockIdx.x / BM;                 // split tile index
+    const int ml = blockIdx.x % BM;
+    const int64_t tile = sp.full + v;
+    const int64_t m = (tile / tiles_n) * BM + ml;
+    const int64_t n = (tile % tiles_n) * BN + threadIdx.x;
+    if (m >= M || n >= N) return;
+    const float *p = part + v * sp.chunks * (BM * BN) + ml * BN + threadIdx.x;
+    float acc = p[0];
+    for (int c = 1; c < sp.chunks; ++c) acc += p[(int64_t)c * (BM * BN)];
+    store_y(y, y16, m * N + n, acc);
+}
+
 template <bool DOTS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__ s,
                          const int32_t *__restrict__ t, const uint8_t *__restrict__ codes,
                          const uint16_t *__restrict__ ws, float *__restrict__ y,
                          uint16_t *__restrict__ y16, int32_t *__restrict__ d, int64_t M,
-                         int64_t N, int64_t K) {
+                         int64_t N, int64_t K, WideSplit sp) {
     using L = PfWide<DOTS>;
     constexpr int T = L::T, WN = L::WN, WM = L::WM;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -748,8 +777,22 @@ void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__
     const int KB = (int)(K / 4);
 
     const int64_t tiles_n = (N + L::BN - 1) / L::BN;
-    const int64_t tiles_m = (M + L::BM - 1) / L::BM;
-    const int64_t tile = xcd_tile(blockIdx.x, tiles_n * tiles_m);
+    // Dispatch slots below sp.full run whole tiles 0 .. sp.full - 1 (in XCD
+    // order); slot sp.full + u runs K chunk u % sp.chunks (groups
+    // chunk * sp.chunk_groups onward) of tile sp.full + u / sp.chunks and
+    // leaves its partial sums in sp.part[u] ([BM][BN] float32).
+    int64_t tile;
+    int g0 = 0, g1 = G;
+    float *partial = nullptr;
+    if ((int64_t)blockIdx.x < sp.full) {
+        tile = xcd_tile(blockIdx.x, sp.full);
+    } else {
+        const int64_t u = (int64_t)blockIdx.x - sp.full;
+        tile = sp.full + u / sp.chunks;
+        g0 = (int)(u % sp.chunks) * sp.chunk_groups;
+        g1 = g0 + sp.chunk_groups < G ? g0 + sp.chunk_groups : G;
+        partial = sp.part + u * (L::BM * L::BN);
+    }
     const int64_t n0 = (tile % tiles_n) * L::BN;
     const int64_t m0 = (tile / tiles_n) * L::BM;
     const int rows = N - n0 < L::BN ? (int)(N - n0) : L::BN;
@@ -906,31 +949,57 @@ void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__
                                  "+v"(acc[a][b][3]));
                 }
             }
+            // issue order: the LDS reads, then one MFMA per three VALU
+            // instructions, so the epilogue's VALU work goes out between
+            // the next tile's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+#pragma unroll
+            for (int k = 0; k < 12; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
+    // whether the step of group g issues the next scale chunk (chunk g / 8 + 1)
+    auto scales_at = [&](int g) __attribute__((always_inline)) {
+        return (g & 7) == 0 && g + 8 < g1;
+    };
     // one group: stage g in LDS once this wave's copies older than the last
     // scale chunk have landed and every wave has passed the barrier
     auto step = [&](int g, const uint8_t *cur, uint8_t *nxt) __attribute__((always_inline)) {
-        if (g >= 1 && ((g - 1) & 7) == 0 && g + 7 < G)
-            wait_vmem<L::kScaleInst>();          // chunk (g - 1) / 8 + 1 may still be in flight
+        if (g > g0 && scales_at(g - 1))
+            wait_vmem<L::kScaleInst>();          // that chunk may still be in flight
         else
             wait_vmem<0>();
         ring_barrier();
-        if (g + 1 < G) issue_stage(g + 1, nxt);
-        if ((g & 7) == 0 && g + 8 < G) issue_scales((g >> 3) + 1);
+        if (g + 1 < g1) issue_stage(g + 1, nxt);
+        if (scales_at(g)) issue_scales((g >> 3) + 1);
         compute(cur, g);
     };
 
-    issue_scales(0);
-    issue_stage(0, stage0);
-    for (int g = 0; g < G; g += 2) {             // G is a multiple of 8
+    // scale chunk of group g0, and the next one when g0 starts mid-chunk
+    // (the loop issues chunks only at multiples of 8)
+    issue_scales(g0 >> 3);
+    if ((g0 & 7) != 0 && ((g0 >> 3) + 1) * 8 < g1) issue_scales((g0 >> 3) + 1);
+    issue_stage(g0, stage0);
+    for (int g = g0; g < g1; g += 2) {           // g0 and g1 - g0 are even
         step(g, stage0, stage1);
         step(g + 1, stage1, stage0);
     }
     wait_vmem<0>();
 
+    if (!DOTS && partial) {
+#pragma unroll
+        for (int b = 0; b < WM; ++b)
+#pragma unroll
+            for (int a = 0; a < WN; ++a)
+                *reinterpret_cast<float4 *>(partial + (16 * b + r) * L::BN + row_base + 16 * a + 4 * lg) =
+                    make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        return;
+    }
     if (!DOTS) {
         // four outputs of a lane as one 16-byte store where y allows it
         const bool vec_y = !y16 && (N & 3) == 0 && ((uintptr_t)y & 15) == 0;
@@ -954,24 +1023,73 @@ void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__
     }
 }
 
+constexpr int64_t kWideBM = 128, kWideBN = 256;
+
+int64_t wide_tiles(int64_t M, int64_t N) {
+    return ((N + kWideBN - 1) / kWideBN) * ((M + kWideBM - 1) / kWideBM);
+}
+
+// K split of the wide variant's last tiles within work_bytes of partial sums.
+// Two blocks fit per CU, so P = 2 * CUs blocks run at once and T tiles leave
+// T % P of them for a last round that keeps part of the GPU idle; splitting
+// the K range of those tiles into S chunks (S <= P / (T % P), at most 4, at
+// least 8 groups and whole pairs of groups per chunk) fills that round with S
+// times as many blocks of 1 / S of the work each. Measured: M = 4096, K =
+// 5120: N = 17408 535 us against 564 unsplit, N = 5120 167 against 182; with
+// chunks of 2 groups (M = 1100, N = 17408, K = 1024) splitting lost (60
+// against 51 us), hence the 8-group floor.
+WideSplit wide_split(int64_t M, int64_t N, int64_t K, float *work, size_t work_bytes) {
+    const int64_t T = wide_tiles(M, N);
+    const int G = (int)(K / kGroup);
+    WideSplit sp{T, 1, G, nullptr};
+    const int cus = device_cus() > 0 ? device_cus() : 256;
+    const int64_t P = 2 * (int64_t)cus;
+    const int64_t tail = T % P;
+    if (T < P || tail == 0) return sp;
+    const uint64_t per = (uint64_t)tail * kWideBM * kWideBN * sizeof(float);
+    int64_t S = P / tail < 4 ? P / tail : 4;
+    if (S > G / 8) S = G / 8;
+    if ((uint64_t)S > work_bytes / per) S = (int64_t)(work_bytes / per);
+    if (S < 2) return sp;
+    int cg = (G + (int)S - 1) / (int)S;
+    cg += cg & 1;
+    S = (G + cg - 1) / cg;
+    if (S < 2) return sp;
+    sp.full = T - tail;
+    sp.chunks = (int)S;
+    sp.chunk_groups = cg;
+    sp.part = work;
+    return sp;
+}
+
 template <bool DOTS>
 hipError_t launch_wide_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,
                             const GemmOut &out, int64_t M, int64_t N, int64_t K,
-                            hipStream_t stream) {
+                            const WideSplit &sp, hipStream_t stream) {
     using L = PfWide<DOTS>;
-    const int64_t blocks = ((N + L::BN - 1) / L::BN) * ((M + L::BM - 1) / L::BM);
+    static_assert(L::BM == kWideBM && L::BN == kWideBN, "tile sizes");
+    const int64_t T = wide_tiles(M, N);
+    const int64_t blocks = sp.full + (T - sp.full) * sp.chunks;
     hipLaunchKernelGGL((prefill_wide_kernel<DOTS>), dim3((unsigned)blocks), dim3(L::T),
                        (size_t)L::kLdsBytes, stream, q, DOTS ? nullptr : out.s, t, codes,
                        DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y,
-                       DOTS ? nullptr : out.y16, DOTS ? out.d : nullptr, M, N, K);
+                       DOTS ? nullptr : out.y16, DOTS ? out.d : nullptr, M, N, K, sp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || DOTS || sp.chunks == 1) return e;
+    hipLaunchKernelGGL(wide_tail_sum_kernel, dim3((unsigned)((T - sp.full) * kWideBM)),
+                       dim3((unsigned)kWideBN), 0, stream, sp.part, out.y, out.y16, M, N, sp);
     return hipGetLastError();
 }
 
 hipError_t launch_wide(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                       const GemmOut &out, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream) {
-    return out.d ? launch_wide_dots<true>(q, t, codes, out, M, N, K, stream)
-                 : launch_wide_dots<false>(q, t, codes, out, M, N, K, stream);
+                       const GemmOut &out, int64_t M, int64_t N, int64_t K, float *work,
+                       size_t work_bytes, hipStream_t stream) {
+    if (out.d) {
+        const WideSplit whole{wide_tiles(M, N), 1, (int)(K / kGroup), nullptr};
+        return launch_wide_dots<true>(q, t, codes, out, M, N, K, whole, stream);
+    }
+    const WideSplit sp = wide_split(M, N, K, work, work ? work_bytes : 0);
+    return launch_wide_dots<false>(q, t, codes, out, M, N, K, sp, stream);
 }
 
 template <int WN, int WM, int WAVES_N, int WAVES_M, int R>
@@ -1042,31 +1160,45 @@ int64_t prefill_blocks(int64_t M, int64_t N) {
     return prefill_tiles(M, N, 32, 32);
 }
 
-hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                          const GemmOut &out, int64_t M, int64_t N, int64_t K,
-                          hipStream_t stream) {
+namespace {
+
+// Tile choice (MI355X sweeps over M = 128 / 512 / 4096 on the 5120 and 17408
+// shapes): 128 x 128 where that gives at least four tiles per CU, else
+// 64 x 64 where that gives two, else 32 x 32 -- at these sizes more,
+// smaller tiles keep more waves per CU busy (M = 128, N = 17408: 43.7 us
+// against 54.2 with 64 x 128; M = 128, N = 5120: 20.4 against 27.0).
+// Ring forms (stages and scale chunks by buffer -> LDS copies) where G is
+// a multiple of 8 and offsets stay below their sentinel: 3-20 % faster;
+// the 64 x 64 ring (88 VGPRs, 31 KB of LDS) runs five blocks per CU. Ring
+// forms of the 32 x 32, 64 x 128 tiles and a 3-stage 64 x 64 ring were
+// slower. The wide variant, where it gives at least two tiles per CU,
+// is faster again: M = 4096, N = 17408: 524 us against 672 for the
+// 128 x 128 ring; N = 5120: 184 against 216; at M = 512, N = 17408 (272
+// tiles) it loses to the 64 x 64 ring (117 against 107).
+int prefill_cfg(int64_t M, int64_t N, int64_t K) {
     auto tiles = [&](int64_t bn, int64_t bm) { return prefill_tiles(M, N, bn, bm); };
     constexpr int64_t kCUs = kPrefillCUs;
-    // Tile choice (MI355X sweeps over M = 128 / 512 / 4096 on the 5120 and 17408
-    // shapes): 128 x 128 where that gives at least four tiles per CU, else
-    // 64 x 64 where that gives two, else 32 x 32 -- at these sizes more,
-    // smaller tiles keep more waves per CU busy (M = 128, N = 17408: 43.7 us
-    // against 54.2 with 64 x 128; M = 128, N = 5120: 20.4 against 27.0).
-    // Ring forms (stages and scale chunks by buffer -> LDS copies) where G is
-    // a multiple of 8 and offsets stay below their sentinel: 3-20 % faster;
-    // the 64 x 64 ring (88 VGPRs, 31 KB of LDS) runs five blocks per CU. Ring
-    // forms of the 32 x 32, 64 x 128 tiles and a 3-stage 64 x 64 ring were
-    // slower. The wide variant, where it gives at least two tiles per CU,
-    // is faster again: M = 4096, N = 17408: 524 us against 672 for the
-    // 128 x 128 ring; N = 5120: 184 against 216; at M = 512, N = 17408 (272
-    // tiles) it loses to the 64 x 64 ring (117 against 107).
     const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
-    const int cfg = ring && tiles(256, 128) >= 2 * kCUs ? 10
-                  : tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
-                  : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
-                                                : 9;
-    switch (cfg) {
-        case 10: return launch_wide(q, t, codes, out, M, N, K, stream);
+    return ring && tiles(256, 128) >= 2 * kCUs ? 10
+         : tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
+         : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
+                                       : 9;
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (prefill_cfg(M, N, K) != 10) return 0;
+    const WideSplit sp = wide_split(M, N, K, nullptr, SIZE_MAX);
+    if (sp.chunks == 1) return 0;
+    return (size_t)(wide_tiles(M, N) - sp.full) * sp.chunks * kWideBM * kWideBN * sizeof(float);
+}
+
+hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
+                          const GemmOut &out, int64_t M, int64_t N, int64_t K, float *work,
+                          size_t work_bytes, hipStream_t stream) {
+    switch (prefill_cfg(M, N, K)) {
+        case 10: return launch_wide(q, t, codes, out, M, N, K, work, work_bytes, stream);
         case 6: return launch_ring_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 7: return launch_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 8: return launch_ring_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);

@@ -157,7 +157,14 @@ def test_workspace_query():
     f = pq2.lib.pq2_gemm_workspace_bytes
     assert f(1, 8, 100) == 0 and f(0, 8, 128) == 0     # invalid shapes
     assert f(1, 5120, 6144) == 0                        # the GEMV never splits K
-    assert f(4096, 17408, 5120) == 0                    # nor does the tiled GEMM
+    # The wide prefill tile splits the K range of the tiles left over after
+    # whole rounds of two blocks per CU (256 CUs assumed where no GPU is
+    # visible): 4096 x 17408 is 2176 tiles of 128 x 256, 128 left over, split
+    # into 4 chunks of 128 x 256 float32 partial sums each.
+    assert f(4096, 17408, 5120) == 128 * 4 * 128 * 256 * 4
+    assert f(4096, 4096, 5120) == 0                     # 512 tiles: whole rounds only
+    assert f(512, 17408, 5120) == 0                     # a smaller tile, no split
+    assert f(4096, 17408, 5248) == 0                    # 41 groups, not a multiple of 8: not the wide tile
 
 
 def test_python_binding_rejects_cpu_tensors():

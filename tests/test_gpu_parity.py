@@ -841,6 +841,65 @@ def test_workspace_size_and_fallbacks(pq2, M, N, K):
     np.testing.assert_array_equal(host(d), oracle.group_dots(qo, w.codes))
 
 
+SPLIT_SHAPES = [(1100, 17408, 2048), (2100, 8200, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
+def test_prefill_tail_split(pq2, M, N, K):
+    """The wide prefill tile with the K range of its last tiles split across
+    blocks (partial sums in the workspace, added in chunk order): the size
+    query is a whole number of 128 x 256 float32 tiles; the tiles computed
+    whole are bit-identical with and without a workspace; every sampled output
+    (the split tiles' token rows and their ragged edges included) within
+    tolerance of the oracle; with unit scales y is the exact sum of the group
+    dots; the allocation-free entry, whose scratch array is too small for
+    these partial sums, gives the unsplit result bit for bit."""
+    wsz = pq2.gemm_workspace_bytes(M, N, K)
+    tile = 128 * 256 * 4
+    tiles_n, tiles_m = -(-N // 256), -(-M // 128)
+    T = tiles_n * tiles_m
+    P = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    tail = T % P
+    print(f"tail split M={M} N={N} K={K} tiles={T} tail={tail} workspace={wsz}", flush=True)
+    assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PREFILL
+    assert wsz > 0 and wsz % tile == 0 and wsz // tile == tail * (wsz // tile // tail)
+    x = synth.activations(M, K, M + K, outlier_frac=0.0)
+    w = synth.weights(N, K, synth.matrix_seed(N), synth.PREFILL_CODES)
+    qo, so, to = oracle.quantize(x)
+    qd, sd, td = dev(oracle.plane_order(qo)), dev(so), dev(to)
+    cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    work = torch.empty(wsz, dtype=torch.uint8, device="cuda")
+    ys = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    yw = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(qd, sd, td, cd, wd, ys, workspace=work)
+    pq2.pq2_gemm(qd, sd, td, cd, wd, yw, workspace=None)
+    full_rows = ((T - tail) // tiles_n) * 128          # token panels computed whole
+    hs, hw = host(ys), host(yw)
+    np.testing.assert_array_equal(hs[:full_rows], hw[:full_rows])
+    rng = np.random.default_rng(M + N)
+    P_ = 768
+    lo = (T - tail) // tiles_n * 128                     # first row of a split tile
+    mm = np.concatenate([rng.integers(lo, M, P_ // 2), rng.integers(0, M, P_ // 2 - 4),
+                         [lo, M - 1, M - 1, lo]])
+    nn = np.concatenate([rng.integers(0, N, P_ - 4), [0, N - 1, 0, N - 1]])
+    yo, tabs = oracle.gemm_f64_sampled(qo, so, w.codes, w.wscale, mm, nn)
+    assert oracle.rel_err(hs[mm, nn], yo, tabs) < TOL
+    assert oracle.rel_err(hw[mm, nn], yo, tabs) < TOL
+    ones_w = torch.full((N, K // G), 0x3C00, dtype=torch.int16, device="cuda")
+    pq2.pq2_gemm(qd, torch.ones_like(sd), td, cd, ones_w, ys, workspace=work)
+    dots = oracle.group_dots_sampled(qo, w.codes, mm, nn)
+    np.testing.assert_array_equal(host(ys)[mm, nn], dots.sum(-1).astype(np.float32))
+    # scratch smaller than the partial sums: the plan of a workspace of the
+    # scratch size (fewer chunks, or none)
+    assert wsz > pq2.NOALLOC_SCRATCH_BYTES
+    yn = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm_noalloc(qd, sd, td, cd, wd, yn)
+    small = torch.empty(pq2.NOALLOC_SCRATCH_BYTES, dtype=torch.uint8, device="cuda")
+    pq2.pq2_gemm(qd, sd, td, cd, wd, ys, workspace=small)
+    np.testing.assert_array_equal(host(yn), host(ys))
+    assert oracle.rel_err(host(yn)[mm, nn], yo, tabs) < TOL
+
+
 def test_workspace_two_streams(pq2):
     """Split-K calls on two streams at once, each with its own workspace,
     different inputs: y identical to the same calls run one at a time."""
