@@ -49,8 +49,8 @@
  *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), M above
  *                PQ2_LINEAR_MAX_M (pq2_linear), or an unknown activation
  *                format (pq2_quantize_act_16);
- *  PQ2_ERR_SCRATCH (pq2_gemm_noalloc) the shape's split-K partial sums need
- *                more than PQ2_NOALLOC_SCRATCH_BYTES;
+ *  PQ2_ERR_SCRATCH (pq2_gemm_noalloc) the small-batch plan's split-K partial
+ *                sums need more than PQ2_NOALLOC_SCRATCH_BYTES;
  *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
  * Nothing is enqueued when a status other than PQ2_OK is returned, except for
  * PQ2_ERR_HIP. A fault during execution surfaces at the caller's next
@@ -133,8 +133,10 @@ pq2_status pq2_quantize_act_16(const uint16_t *x, int x_format, int8_t *q, float
  * its fastest plan for this shape: the persistent small-batch kernel splits
  * K into S chunks for some shapes (K = 17408 at 3..16 token rows: S = 3;
  * 17..64 rows: most K) and writes S * M * N float32 partial sums, which a
- * second small launch adds in chunk order. 0 when that plan does not split
- * K, or when the shape is invalid. Pure host query; enqueues nothing. (The
+ * second small launch adds in chunk order; the tiled prefill GEMM splits the
+ * K range of its leftover 256 x 128 tiles (M = 4096, K = 5120, N = 17408 or
+ * 5120: 128 tiles x 4 chunks, 64 MiB). 0 when the plan does not split K, or
+ * when the shape is invalid. Pure host query; enqueues nothing. (The
  * page "Making a ternary reasoning model fast in vLLM", section "Measure at
  * the clock speeds used in serving", counts the split-K reduction launches;
  * its section "Speed up a small unquantised projection" sums splits in a
@@ -164,12 +166,16 @@ size_t pq2_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * order that differs from a sequential sum only by float32 rounding (a fixed
  * order: repeated calls give identical y).
  * Workspace: a caller-owned device buffer of workspace_bytes bytes, 16-byte
- * aligned, or NULL. Plans that split K into S chunks are taken only when
+ * aligned, or NULL, that holds float32 partial sums of plans splitting K.
+ * The persistent small-batch kernel splits K into S chunks only when
  * S * M * N * 4 <= workspace_bytes (the largest chunk count that fits, at
- * most 16); pq2_gemm_workspace_bytes gives the size of the fastest plan.
- * With NULL, or a buffer too small for any split, pq2_gemm takes a plan that
- * does not split K (same result up to float32 summation order; slower on
- * some shapes, e.g. K = 17408 at 3..16 rows). The workspace's contents
+ * most 16). The tiled prefill GEMM, on its 256 x 128 tile, splits the K range
+ * of the tiles left over after whole rounds of two blocks per CU into up to
+ * 4 chunks, each chunk's partial tile (128 x 256 float32) in the workspace,
+ * and takes as many chunks as fit. pq2_gemm_workspace_bytes gives the size
+ * of the fastest plan. With NULL, or a buffer too small for any split,
+ * pq2_gemm takes a plan that does not split K (same result up to float32
+ * summation order; slower on some shapes, e.g. K = 17408 at 3..16 rows). The workspace's contents
  * before and after a call are unspecified; calls that may run concurrently
  * (different streams) need different workspaces, calls on one stream may
  * share one.
@@ -183,13 +189,15 @@ pq2_status pq2_gemm(const int8_t *q, const float *s, const int32_t *t,
  * pq2_gemm for callers that cannot allocate device memory or hold a
  * workspace: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc. Same arguments as pq2_gemm without the workspace,
- * same plan as pq2_gemm given pq2_gemm_workspace_bytes(M, N, K) bytes, so y
- * is bit-identical to that call. The split-K partial sums go to a buffer of
+ * same plan as pq2_gemm given min(pq2_gemm_workspace_bytes(M, N, K),
+ * PQ2_NOALLOC_SCRATCH_BYTES) bytes of workspace, so y is bit-identical to
+ * that call. The split-K partial sums go to a buffer of
  * PQ2_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one per
  * device (part of the loaded library, alive until the process ends); its
- * address is looked up on the first call on each device. Shapes whose
- * pq2_gemm_workspace_bytes exceeds PQ2_NOALLOC_SCRATCH_BYTES return
- * PQ2_ERR_SCRATCH (nothing enqueued). Nothing is allocated or freed. Every
+ * address is looked up on the first call on each device. Prefill shapes
+ * split only as far as their partial tiles fit that buffer (or not at all);
+ * small-batch shapes whose pq2_gemm_workspace_bytes exceeds
+ * PQ2_NOALLOC_SCRATCH_BYTES return PQ2_ERR_SCRATCH (nothing enqueued). Nothing is allocated or freed. Every
  * call on a device shares that device's buffer: calls that may overlap on one
  * device (different streams, or host threads) race on it and must be
  * serialised by the caller; calls on one stream are ordered and safe. The
