@@ -483,9 +483,8 @@ def report_gemm(args, wl, r, torch):
 
 def layer_step(m, torch, pq2, stream):
     """The 64-layer synthetic decode step as a list of launches on `stream`:
-    returns (step, shares_input); step(after=None) enqueues every projection
-    (quantise where the input is new, then pq2_gemm) and calls after() behind
-    each projection's GEMM."""
+    step(after=None) enqueues every GEMM of the step (pq2_linear, or
+    pq2_quantize_act then pq2_gemm) and calls after() behind each."""
     import pq2_synth as synth
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
@@ -504,36 +503,27 @@ def layer_step(m, torch, pq2, stream):
     work = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
     wkp = work.data_ptr() if wsz else None
     lib = pq2.lib
-    # the gate and up projections (the two 5120 -> 17408 ones) read the same
-    # activations, so one quantisation serves both; every other projection
-    # quantises its own input
-    shares_input = tuple(i > 0 and synth.LAYER_SHAPES[i] == synth.LAYER_SHAPES[i - 1]
-                         for i in range(len(synth.LAYER_SHAPES)))
     # one launch (pq2_linear, quantisation inside the GEMV) where that measured
     # faster than pq2_quantize_act + pq2_gemm on MI355X: one token row with
-    # K <= 6144 (6144 x 5120: 6.93 against 7.24 us; 5120 x 6144: 6.48 against
-    # 7.28); the two-launch step elsewhere (gate and up share a quantisation;
-    # at K = 17408 and from two rows on, quantising in every block costs more
-    # than the separate launch)
-    fused = tuple(m == 1 and k <= 6144 and not shares_input[i] and
-                  not (i + 1 < len(synth.LAYER_SHAPES) and shares_input[i + 1])
-                  for i, (n, k) in enumerate(synth.LAYER_SHAPES))
+    # K <= 6144 and N * K <= 2^25 (6144 x 5120: 6.93 against 7.24 us; 5120 x
+    # 6144: 6.48 against 7.28; the stacked 34816 x 5120 gate and up: 14.53
+    # against 14.23); the two-launch step elsewhere (at K = 17408 and from two
+    # rows on, quantising in every block costs more than the separate launch)
+    fused = tuple(m == 1 and k <= 6144 and n * k <= (1 << 25) for (n, k) in synth.LAYER_SHAPES)
     calls = []
     for projs in layers:
         for i, (codes, ws, n, k) in enumerate(projs):
             q, s, t = bufs[k]
-            calls.append((fused[i], not shares_input[i], xs[k].data_ptr(), q.data_ptr(),
-                          s.data_ptr(), t.data_ptr(), codes.data_ptr(), ws.data_ptr(),
-                          ys[n].data_ptr(), n, k))
+            calls.append((fused[i], xs[k].data_ptr(), q.data_ptr(), s.data_ptr(), t.data_ptr(),
+                          codes.data_ptr(), ws.data_ptr(), ys[n].data_ptr(), n, k))
     quant, gemm, linear = lib.pq2_quantize_act, lib.pq2_gemm, lib.pq2_linear
 
     def step(after=None):
-        for (fz, qz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
+        for (fz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
             if fz:
                 linear(xp, cp, wp, yp, m, n, k, stream)
             else:
-                if qz:
-                    quant(xp, qp, sp, tp, m, k, stream)
+                quant(xp, qp, sp, tp, m, k, stream)
                 gemm(qp, sp, tp, cp, wp, yp, m, n, k, wkp, wsz, stream)
             if after is not None:
                 after()
@@ -541,15 +531,16 @@ def layer_step(m, torch, pq2, stream):
     step.buffers = (layers, xs, bufs, ys, work)   # the launches hold raw pointers into these
     step.workspace_bytes = wsz
     step.fused = fused
-    return step, shares_input
+    return step
 
 
 def run_layers(args, m, torch, pq2, steps, trials):
-    """64-layer synthetic decode step: 5 PQ2_0 projections per layer, back to
-    back on one stream (every weight matrix is read once per step, 5.6 GB)."""
+    """64-layer synthetic decode step: per layer 4 PQ2_0 GEMMs (5 projections,
+    gate and up stacked into one matrix), back to back on one stream (every
+    weight matrix is read once per step, 5.6 GB)."""
     import pq2_synth as synth
     stream = torch.cuda.current_stream(torch.device("cuda:0")).cuda_stream
-    step, shares_input = layer_step(m, torch, pq2, stream)
+    step = layer_step(m, torch, pq2, stream)
     for _ in range(2):
         step()
     torch.cuda.synchronize()
@@ -559,21 +550,20 @@ def run_layers(args, m, torch, pq2, steps, trials):
     ms = median(runs) / steps
     total = 0
     for i, (n, k) in enumerate(synth.LAYER_SHAPES):
-        if step.fused[i]:
-            total += linear_bytes(m, n, k)
-        else:
-            total += gemm_bytes(m, n, k) + (0 if shares_input[i] else quant_bytes(m, k))
+        total += linear_bytes(m, n, k) if step.fused[i] else gemm_bytes(m, n, k) + quant_bytes(m, k)
     total *= synth.N_LAYERS
     gbs = total / (ms * 1e-3) / 1e9
-    n_quant = sum(not shares_input[i] and not step.fused[i] for i in range(len(shares_input)))
+    n_quant = sum(not f for f in step.fused)
     return {"metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": steps,
             "warmup": 2, "ms_per_step": ms, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
             "config": {"workload": f"layer64_m{m}", "M": m, "layers": synth.N_LAYERS,
-                       "gemms_per_step": 5 * synth.N_LAYERS,
+                       "projections_per_layer": 5,
+                       "gemms_per_step": len(synth.LAYER_SHAPES) * synth.N_LAYERS,
                        "quantiser_launches_per_step": n_quant * synth.N_LAYERS,
-                       "projection": "pq2_quantize_act + pq2_gemm (gate and up share one "
-                                     "quantisation), or pq2_linear where that is faster",
+                       "projection": "pq2_quantize_act + pq2_gemm, or pq2_linear where that "
+                                     "is faster; gate and up stacked into one 34816 x 5120 "
+                                     "matrix (they read the same activations)",
                        "fused_projections_per_layer": int(sum(step.fused)),
                        "algorithmic_bytes_per_step": total, "trials": trials,
                        "trial_ms": [round(v / steps, 4) for v in runs],
@@ -583,22 +573,22 @@ def run_layers(args, m, torch, pq2, steps, trials):
                          "note": "whole step incl. quantise launches and launch gaps"}}
 
 
-# The pages' power proxy: a low-power spin after every projection stands in for
-# the decode step's other work (norms, attention, recurrent updates, sampling),
-# so that a replay of the projections runs at the clock and power state of
+# The pages' power proxy: a low-power spin after every matrix multiply stands in
+# for the decode step's other work (norms, attention, recurrent updates,
+# sampling), so that a replay of the projections runs at the clock and power state of
 # serving rather than of back-to-back memory-bound kernels. The pages sized
 # the spin from a serving trace (page "Making a ternary reasoning model fast
 # in vLLM", section "A power proxy for the rest of the model"): 25k cycles at
 # 2 tokens rising to 55k at 16, which they relate to the non-GEMM time of the
 # trace at roughly 1.5 spin cycles per ns. Here the spin is that much time
-# per projection.
+# after each GEMM launch (the stacked gate and up projections are one).
 def proxy_spin_us(m):
     cycles = 25000.0 + (min(max(m, 2), 16) - 2) * (55000.0 - 25000.0) / 14.0
     return cycles / 1.5 / 1000.0
 
 
 def run_proxy(args, m, torch, pq2):
-    """The 64-layer step with a spin after every projection, captured once in a
+    """The 64-layer step with a spin after every GEMM, captured once in a
     HIP graph and replayed back to back for --proxy-seconds. Kernel durations
     under the proxy come from a kernel trace of this run (the spin's wall time
     follows the clock, so the step time mixes the two); this line reports the
@@ -608,7 +598,8 @@ def run_proxy(args, m, torch, pq2):
     spin_us = proxy_spin_us(m) if args.proxy_spin_us is None else args.proxy_spin_us
     cyc_per_ms = spin_cycles_per_ms(torch)
     spin = int(cyc_per_ms * spin_us / 1000.0)
-    step, _ = layer_step(m, torch, pq2, cap.cuda_stream)
+    import pq2_synth as synth
+    step = layer_step(m, torch, pq2, cap.cuda_stream)
     after = (lambda: torch.cuda._sleep(spin)) if spin > 0 else None
     with torch.cuda.stream(cap):
         step(after)                 # eager run before capture (checks the launches)
@@ -631,11 +622,12 @@ def run_proxy(args, m, torch, pq2):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / replays
-    return {"proxy": {"workload": f"layer64_m{m}", "M": m, "spin_us_per_projection": spin_us,
-                      "spin_cycles": spin, "projections_per_step": 5 * 64,
+    return {"proxy": {"workload": f"layer64_m{m}", "M": m, "spin_us_per_gemm": spin_us,
+                      "spin_cycles": spin,
+                      "gemms_per_step": len(synth.LAYER_SHAPES) * synth.N_LAYERS,
                       "replays": replays, "ms_per_replay": ms,
                       "note": "HIP-graph replay of the 64-layer step with a spin after every "
-                              "projection; GEMM kernel durations from a kernel trace of this run"}}
+                              "GEMM; GEMM kernel durations from a kernel trace of this run"}}
 
 
 def run_ceiling(torch):
@@ -702,7 +694,7 @@ def main():
                          "(one JSON line of its own, not the bench line)")
     ap.add_argument("--proxy-seconds", type=float, default=5.0)
     ap.add_argument("--proxy-spin-us", type=float, default=None,
-                    help="spin per projection (default: the pages' calibration for M; 0: none)")
+                    help="spin per GEMM (default: the pages' calibration for M; 0: none)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise kernel (y = 2x, float32) over MIB MiB, "
                          "the calibration for HBM byte counters")

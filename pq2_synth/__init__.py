@@ -158,6 +158,9 @@ def prefill(m: int, n: int, k: int) -> Workload:
     return Workload(f"prefill_m{m}_n{n}_k{k}", m, n, k, probs=PREFILL_CODES)
 
 
-# One synthetic decoder layer: (N, K) of the five projections, in order.
-LAYER_SHAPES = ((6144, 5120), (5120, 6144), (17408, 5120), (17408, 5120), (5120, 17408))
+# One synthetic decoder layer: (N, K) of its projections, in order: 5120 ->
+# 6144, 6144 -> 5120, the gate and up projections 5120 -> 17408 stacked into
+# one 34816-row matrix (both read the same activations; gate rows first, then
+# up rows), and 17408 -> 5120. Five projections, four GEMMs.
+LAYER_SHAPES = ((6144, 5120), (5120, 6144), (2 * 17408, 5120), (5120, 17408))
 N_LAYERS = 64

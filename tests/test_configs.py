@@ -12,8 +12,8 @@ asks for), against the CPU oracle on the same seeded inputs.
   4096 sampled outputs that include every 32-row and 32-column tile edge
   (hence every 64- and 128-tile edge), and y in full at 128 rows;
 * the 64-layer decode step at M = 1 and 16: the step as the benchmark issues
-  it (one stream, gate and up sharing one quantisation, one workspace), with
-  sampled outputs of every one of its 320 projections against the oracle.
+  it (one stream, gate and up stacked into one matrix, one workspace), with
+  sampled outputs of every one of its 256 GEMMs against the oracle.
 
 The tolerance is max |y - y*| / sum_g |term_g| < 1e-5 with y* the oracle's
 float64 result (group dots exact, float32 summation of G terms); integer work
@@ -168,10 +168,10 @@ def layer_weights(gen, n, k):
 @pytest.mark.parametrize("M", [1, 16])
 def test_layer64_step(pq2, M):
     """The 64-layer decode step as the benchmark issues it: per layer the
-    projections 5120 -> 6144, 6144 -> 5120, 5120 -> 17408 twice (gate and up,
-    which share one quantisation) and 17408 -> 5120, back to back on one
-    stream with one workspace, one token row's K <= 6144 projections through
-    the one-launch pq2_linear; 32 sampled outputs of every projection (the
+    projections 5120 -> 6144, 6144 -> 5120, gate and up (5120 -> 17408 each)
+    stacked into one 34816 x 5120 matrix, and 17408 -> 5120, back to back on
+    one stream with one workspace, one token row's small K <= 6144 matrices
+    through the one-launch pq2_linear; 32 sampled outputs of every GEMM (the
     last row and column included) against the oracle."""
     print(f"config layer64 M={M}", flush=True)
     gen = torch.Generator(device="cuda").manual_seed(M)
@@ -189,17 +189,14 @@ def test_layer64_step(pq2, M):
             codes, ws = layer_weights(gen, n, k)
             y = torch.empty((M, n), dtype=torch.float32, device="cuda")
             projs.append((layer, i, n, k, codes, ws, y))
-    shares = [i > 0 and shapes[i] == shapes[i - 1] for i in range(len(shapes))]
-    fused = [M == 1 and k <= 6144 and not shares[i] and
-             not (i + 1 < len(shapes) and shares[i + 1]) for i, (_, k) in enumerate(shapes)]
+    fused = [M == 1 and k <= 6144 and n * k <= (1 << 25) for (n, k) in shapes]
     torch.cuda.synchronize()
     for (layer, i, n, k, codes, ws, y) in projs:         # the step, no host syncs
         if fused[i]:
             pq2.pq2_linear(xd[k], codes, ws, y)
             continue
         q, s, t = qst[k]
-        if not shares[i]:
-            pq2.pq2_quantize_act(xd[k], q, s, t)
+        pq2.pq2_quantize_act(xd[k], q, s, t)
         pq2.pq2_gemm(q, s, t, codes, ws, y, workspace=work)
     torch.cuda.synchronize()
     qso = {k: oracle.quantize(v) for k, v in xs.items()}
@@ -221,5 +218,5 @@ def test_layer64_step(pq2, M):
         yo, tabs = oracle.gemm_f64_sampled(qo, so, cs, wh, mm, inv.astype(np.int64))
         err = oracle.rel_err(ys, yo, tabs)
         worst = max(worst, err)
-        assert err < TOL, f"layer {layer} projection {i} ({n} x {k}): error {err:.3g}"
-    print(f"layer64 M={M}: worst error {worst:.3g} over {len(projs)} projections", flush=True)
+        assert err < TOL, f"layer {layer} GEMM {i} ({n} x {k}): error {err:.3g}"
+    print(f"layer64 M={M}: worst error {worst:.3g} over {len(projs)} GEMMs", flush=True)
