@@ -253,8 +253,10 @@ class Probes:
         P, SZ = ctypes.c_void_p, ctypes.c_size_t
         lib.pq2_probe_stream_read.argtypes = [P, SZ, P, ctypes.c_int, P]
         lib.pq2_probe_mfma_i8.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        lib.pq2_probe_epilogue_mix.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
         lib.pq2_probe_clock.argtypes = [P, ctypes.c_uint64, P]
-        for f in (lib.pq2_probe_stream_read, lib.pq2_probe_mfma_i8, lib.pq2_probe_clock):
+        for f in (lib.pq2_probe_stream_read, lib.pq2_probe_mfma_i8, lib.pq2_probe_epilogue_mix,
+                  lib.pq2_probe_clock):
             f.restype = ctypes.c_int
         self.lib = lib
         dev = torch.device("cuda:0")
@@ -336,6 +338,27 @@ class Probes:
         return {"TOP/s": ops / (ms * 1e-3) / 1e12, "us": ms * 1e3, "blocks": blocks,
                 "waves_per_cu": 4 * blocks // self.cus,
                 "instruction": "v_mfma_i32_16x16x64_i8, 8 independent chains per wave"}
+
+
+    def epilogue_mix(self, trials=5):
+        """The int8 MFMA rate left once an exact float32 per-group epilogue
+        runs beside it (per 16 x 16 tile and group: 2 int8 MFMAs, one float32
+        4x4x1 outer-product MFMA, 4 conversions and 4 FMAs per lane)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream().cuda_stream
+        blocks, iters = self.cus * 8, 1000
+        tm = Timer(torch, 4)
+
+        def body():
+            self._ok(self.lib.pq2_probe_epilogue_mix(self.sink.data_ptr(), iters, blocks, stream),
+                     "epilogue mix")
+        h = tm.host_ms(body)
+        ms = median([tm.run(body, h) for _ in range(trials)]) / 4
+        ops = blocks * 4 * iters * 8 * 2 * 2 * 16 * 16 * 64
+        return {"TOP/s": ops / (ms * 1e-3) / 1e12, "us": ms * 1e3, "blocks": blocks,
+                "waves_per_cu": 4 * blocks // self.cus,
+                "mix": "per 16x16 tile and group: 2 v_mfma_i32_16x16x64_i8, 1 "
+                       "v_mfma_f32_4x4x1_16b_f32, 4 v_cvt_f32_i32, 4 v_fmac_f32"}
 
 
 def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
@@ -641,7 +664,9 @@ def run_ceiling(torch):
         reads.append(probes.stream_read(nbytes, 1 << 30, calls=max(4, 800 // mib)))
     print("# int8 MFMA loop", file=sys.stderr, flush=True)
     mf = probes.mfma_i8()
-    return {"ceiling": {"stream_read": reads, "mfma_i8": mf,
+    print("# int8 MFMA with the float32 epilogue mix", file=sys.stderr, flush=True)
+    em = probes.epilogue_mix()
+    return {"ceiling": {"stream_read": reads, "mfma_i8": mf, "epilogue_mix": em,
                         "hbm_peak_GB/s": HBM_PEAK_GBS, "i8_peak_TOP/s": I8_PEAK_TOPS}}
 
 
@@ -677,6 +702,7 @@ def extras(args, wl, r, torch, pq2, probes):
         sr["pq2_gemm_time_over_read_time"] = r["kernel_ms"] * 1e3 / sr["us"]
         out["stream_read_same_bytes"] = sr
     out["mfma_i8_loop"] = probes.mfma_i8()
+    out["mfma_i8_with_epilogue_mix"] = probes.epilogue_mix()
     return out
 
 

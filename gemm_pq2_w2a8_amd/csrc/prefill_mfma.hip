@@ -705,9 +705,9 @@ __global__ __launch_bounds__(64 * WAVES_N * WAVES_M) void prefill_ring_kernel(
 // Staging as in the ring variant, with two stages and the group offset of
 // every copy in the SGPR operand: stage g + 1 (and every eight groups the
 // next scale chunk) is copied while group g is computed.
-template <bool DOTS>
+template <bool DOTS, int WM_>
 struct PfWide {
-    static constexpr int T = 256, BN = 256, BM = 128, WN = 4, WM = 8;
+    static constexpr int T = 256, BN = 256, WN = 4, WM = WM_, BM = 16 * WM;
     static constexpr int kCodeInst = 2 * BN / T;          // code units per thread
     static constexpr int kQInst = 8 * BM / T;             // activation units per thread
     static constexpr int kStageInst = kCodeInst + kQInst;
@@ -719,8 +719,11 @@ struct PfWide {
     static constexpr int kTBase = kSBase + BM * 32;
     static constexpr int kScaleBytes = kTBase + BM * 32;
     static constexpr int kScaleInst = DOTS ? 1 : 3;
-    static constexpr int kLdsBytes = 2 * kStageBytes + 2 * kScaleBytes;
-    static_assert(T == BN && 2 * BM == T, "one scale unit per thread and table");
+    // s and t have 2 BM units: with fewer than T, the waves past them copy
+    // into a 1 KB sink (their lanes read no memory)
+    static constexpr int kSinkBase = 2 * kStageBytes + 2 * kScaleBytes;
+    static constexpr int kLdsBytes = kSinkBase + (2 * BM < T ? 1024 : 0);
+    static_assert(T == BN && 2 * BM <= T && (2 * BM) % kWave == 0, "scale units per thread");
 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -736,11 +739,12 @@ struct WideSplit {
 
 // y of the split tiles: the chunks' partial sums added in chunk order. One
 // block per (tile, token row), one thread per weight row.
+template <int BM>
 __global__ __launch_bounds__(256) void wide_tail_sum_kernel(const float *__restrict__ part,
                                                             float *__restrict__ y,
                                                             uint16_t *__restrict__ y16, int64_t M,
                                                             int64_t N, WideSplit sp) {
-    constexpr int BM = 128, BN = 256;
+    constexpr int BN = 256;
     const int64_t tiles_n = (N + BN - 1) / BN;
     const int64_t v = blockIdx.x / BM;                 // split tile index
     const int ml = blockIdx.x % BM;
@@ -754,14 +758,14 @@ __global__ __launch_bounds__(256) void wide_tail_sum_kernel(const float *__restr
     store_y(y, y16, m * N + n, acc);
 }
 
-template <bool DOTS>
+template <bool DOTS, int WM_>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__ s,
                          const int32_t *__restrict__ t, const uint8_t *__restrict__ codes,
                          const uint16_t *__restrict__ ws, float *__restrict__ y,
                          uint16_t *__restrict__ y16, int32_t *__restrict__ d, int64_t M,
                          int64_t N, int64_t K, WideSplit sp) {
-    using L = PfWide<DOTS>;
+    using L = PfWide<DOTS, WM_>;
     constexpr int T = L::T, WN = L::WN, WM = L::WM;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *const stage0 = smem;
@@ -839,13 +843,15 @@ void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__
             copy16_to_lds_at(rs_q, st + L::kQBase + 16 * (i * T + kWave * wave), qoff[i],
                              kGroup * g);
     };
+    const bool tok_wave = kWave * wave < 2 * L::BM;   // this wave's s / t units exist
     auto issue_scales = [&](int c) __attribute__((always_inline)) {
         uint8_t *sc = scl0 + (c & 1) * L::kScaleBytes + 16 * kWave * wave;
+        uint8_t *sink = smem + L::kSinkBase;
         if (!DOTS) {
             copy16_to_lds_at(rs_ws, sc, wsoff, 16 * c);
-            copy16_to_lds_at(rs_s, sc + L::kSBase, tokoff, 32 * c);
+            copy16_to_lds_at(rs_s, tok_wave ? sc + L::kSBase : sink, tokoff, 32 * c);
         }
-        copy16_to_lds_at(rs_t, sc + L::kTBase, tokoff, 32 * c);
+        copy16_to_lds_at(rs_t, tok_wave ? sc + L::kTBase : sink, tokoff, 32 * c);
     };
 
     const int row_base = 64 * wave;
@@ -1023,32 +1029,35 @@ void prefill_wide_kernel(const int8_t *__restrict__ q, const float *__restrict__
     }
 }
 
-constexpr int64_t kWideBM = 128, kWideBN = 256;
+constexpr int64_t kWideBN = 256;
 
-int64_t wide_tiles(int64_t M, int64_t N) {
-    return ((N + kWideBN - 1) / kWideBN) * ((M + kWideBM - 1) / kWideBM);
+int64_t wide_tiles(int64_t M, int64_t N, int64_t bm) {
+    return ((N + kWideBN - 1) / kWideBN) * ((M + bm - 1) / bm);
 }
 
 // K split of the wide variant's last tiles within work_bytes of partial sums.
 // Two blocks fit per CU, so P = 2 * CUs blocks run at once and T tiles leave
 // T % P of them for a last round that keeps part of the GPU idle; splitting
 // the K range of those tiles into S chunks (S <= P / (T % P), at most 4, at
-// least 8 groups and whole pairs of groups per chunk) fills that round with S
-// times as many blocks of 1 / S of the work each. Measured: M = 4096, K =
-// 5120: N = 17408 535 us against 564 unsplit, N = 5120 167 against 182; with
-// chunks of 2 groups (M = 1100, N = 17408, K = 1024) splitting lost (60
-// against 51 us), hence the 8-group floor.
-WideSplit wide_split(int64_t M, int64_t N, int64_t K, float *work, size_t work_bytes) {
-    const int64_t T = wide_tiles(M, N);
+// least 10 groups and whole pairs of groups per chunk) fills that round with
+// S times as many blocks of 1 / S of the work each. Measured (K = 5120): the
+// 256 x 128 tile at M = 4096, N = 17408 523 us against 560 unsplit, M =
+// 1024 138 against 182; the 256 x 64 tile at M = 512, N = 17408 84 against
+// 111, M = 2048, N = 5120 95 against 105. Shorter chunks lost: 8 groups (M =
+// 600, N = 17300, K = 2048) 58 against 51 us, 2 groups (K = 1024) 60
+// against 51.
+WideSplit wide_split(int64_t M, int64_t N, int64_t K, int64_t bm, float *work,
+                     size_t work_bytes) {
+    const int64_t T = wide_tiles(M, N, bm);
     const int G = (int)(K / kGroup);
     WideSplit sp{T, 1, G, nullptr};
     const int cus = device_cus() > 0 ? device_cus() : 256;
     const int64_t P = 2 * (int64_t)cus;
     const int64_t tail = T % P;
     if (T < P || tail == 0) return sp;
-    const uint64_t per = (uint64_t)tail * kWideBM * kWideBN * sizeof(float);
+    const uint64_t per = (uint64_t)tail * bm * kWideBN * sizeof(float);
     int64_t S = P / tail < 4 ? P / tail : 4;
-    if (S > G / 8) S = G / 8;
+    if (S > G / 10) S = G / 10;
     if ((uint64_t)S > work_bytes / per) S = (int64_t)(work_bytes / per);
     if (S < 2) return sp;
     int cg = (G + (int)S - 1) / (int)S;
@@ -1062,34 +1071,36 @@ WideSplit wide_split(int64_t M, int64_t N, int64_t K, float *work, size_t work_b
     return sp;
 }
 
-template <bool DOTS>
+template <bool DOTS, int WM>
 hipError_t launch_wide_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,
                             const GemmOut &out, int64_t M, int64_t N, int64_t K,
                             const WideSplit &sp, hipStream_t stream) {
-    using L = PfWide<DOTS>;
-    static_assert(L::BM == kWideBM && L::BN == kWideBN, "tile sizes");
-    const int64_t T = wide_tiles(M, N);
+    using L = PfWide<DOTS, WM>;
+    static_assert(L::BN == kWideBN, "tile sizes");
+    const int64_t T = wide_tiles(M, N, L::BM);
     const int64_t blocks = sp.full + (T - sp.full) * sp.chunks;
-    hipLaunchKernelGGL((prefill_wide_kernel<DOTS>), dim3((unsigned)blocks), dim3(L::T),
+    hipLaunchKernelGGL((prefill_wide_kernel<DOTS, WM>), dim3((unsigned)blocks), dim3(L::T),
                        (size_t)L::kLdsBytes, stream, q, DOTS ? nullptr : out.s, t, codes,
                        DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y,
                        DOTS ? nullptr : out.y16, DOTS ? out.d : nullptr, M, N, K, sp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || DOTS || sp.chunks == 1) return e;
-    hipLaunchKernelGGL(wide_tail_sum_kernel, dim3((unsigned)((T - sp.full) * kWideBM)),
+    hipLaunchKernelGGL(wide_tail_sum_kernel<L::BM>, dim3((unsigned)((T - sp.full) * L::BM)),
                        dim3((unsigned)kWideBN), 0, stream, sp.part, out.y, out.y16, M, N, sp);
     return hipGetLastError();
 }
 
+// WM token tiles of 16 per wave: block tile 256 x 16 WM
+template <int WM>
 hipError_t launch_wide(const int8_t *q, const int32_t *t, const uint8_t *codes,
                        const GemmOut &out, int64_t M, int64_t N, int64_t K, float *work,
                        size_t work_bytes, hipStream_t stream) {
     if (out.d) {
-        const WideSplit whole{wide_tiles(M, N), 1, (int)(K / kGroup), nullptr};
-        return launch_wide_dots<true>(q, t, codes, out, M, N, K, whole, stream);
+        const WideSplit whole{wide_tiles(M, N, 16 * WM), 1, (int)(K / kGroup), nullptr};
+        return launch_wide_dots<true, WM>(q, t, codes, out, M, N, K, whole, stream);
     }
-    const WideSplit sp = wide_split(M, N, K, work, work ? work_bytes : 0);
-    return launch_wide_dots<false>(q, t, codes, out, M, N, K, sp, stream);
+    const WideSplit sp = wide_split(M, N, K, 16 * WM, work, work ? work_bytes : 0);
+    return launch_wide_dots<false, WM>(q, t, codes, out, M, N, K, sp, stream);
 }
 
 template <int WN, int WM, int WAVES_N, int WAVES_M, int R>
@@ -1137,6 +1148,7 @@ hipError_t launch_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
 // Tile configurations (rows x tokens, waves, prefetch depth):
 //  10: 256 x 128, 4 x 1 waves of 64 x 128, ring of 2 stages, scale products
 //      on the matrix core (the wide variant)
+//  12: 256 x 64, 4 x 1 waves of 64 x 64, the wide variant
 //   0: 128 x 128, 2 x 2 waves of 64 x 64, depth 1
 //   6: 128 x 128, 2 x 2 waves of 64 x 64, ring of 2 stages (buffer -> LDS copies)
 //   7:  64 x 64,  2 x 2 waves of 32 x 32, depth 2
@@ -1171,15 +1183,23 @@ namespace {
 // a multiple of 8 and offsets stay below their sentinel: 3-20 % faster;
 // the 64 x 64 ring (88 VGPRs, 31 KB of LDS) runs five blocks per CU. Ring
 // forms of the 32 x 32, 64 x 128 tiles and a 3-stage 64 x 64 ring were
-// slower. The wide variant, where it gives at least two tiles per CU,
-// is faster again: M = 4096, N = 17408: 524 us against 672 for the
-// 128 x 128 ring; N = 5120: 184 against 216; at M = 512, N = 17408 (272
-// tiles) it loses to the 64 x 64 ring (117 against 107).
+// slower. The wide variant (256 weight rows x 128 or 64 tokens), where its
+// tiles fill at least 7/8 of a round of two blocks per CU, is faster again
+// (K = 5120, with the K split of its last round): M = 4096, N = 17408 523 us
+// against 672 for the 128 x 128 ring; M = 3072, N = 5120 118 against 160
+// (480 tiles of 128 tokens: one round; the 64-token tile 130); M = 2048,
+// N = 5120 95 (64 tokens) against 114 for the 64 x 64 ring; M = 512,
+// N = 17408 84 (64 tokens) against 113. With fewer tiles the 64 x 64 ring
+// stays faster (M = 512 / 1024, N = 5120: 42 / 66 us against 47 / 69).
 int prefill_cfg(int64_t M, int64_t N, int64_t K) {
     auto tiles = [&](int64_t bn, int64_t bm) { return prefill_tiles(M, N, bn, bm); };
     constexpr int64_t kCUs = kPrefillCUs;
     const bool ring = (K / kGroup) % 8 == 0 && K <= 65536;
-    return ring && tiles(256, 128) >= 2 * kCUs ? 10
+    // the wide tiles where they fill at least 7/8 of a round of two blocks
+    // per CU: 256 x 128 first, else 256 x 64
+    const int64_t wide_min = 7 * (2 * kCUs) / 8;
+    return ring && tiles(256, 128) >= wide_min ? 10
+         : ring && tiles(256, 64) >= wide_min  ? 12
          : tiles(128, 128) >= 4 * kCUs ? (ring ? 6 : 0)
          : tiles(64, 64) >= 2 * kCUs   ? (ring ? 8 : 7)
                                        : 9;
@@ -1188,17 +1208,20 @@ int prefill_cfg(int64_t M, int64_t N, int64_t K) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (prefill_cfg(M, N, K) != 10) return 0;
-    const WideSplit sp = wide_split(M, N, K, nullptr, SIZE_MAX);
+    const int cfg = prefill_cfg(M, N, K);
+    if (cfg != 10 && cfg != 12) return 0;
+    const int64_t bm = cfg == 10 ? 128 : 64;
+    const WideSplit sp = wide_split(M, N, K, bm, nullptr, SIZE_MAX);
     if (sp.chunks == 1) return 0;
-    return (size_t)(wide_tiles(M, N) - sp.full) * sp.chunks * kWideBM * kWideBN * sizeof(float);
+    return (size_t)(wide_tiles(M, N, bm) - sp.full) * sp.chunks * bm * kWideBN * sizeof(float);
 }
 
 hipError_t launch_prefill(const int8_t *q, const int32_t *t, const uint8_t *codes,
                           const GemmOut &out, int64_t M, int64_t N, int64_t K, float *work,
                           size_t work_bytes, hipStream_t stream) {
     switch (prefill_cfg(M, N, K)) {
-        case 10: return launch_wide(q, t, codes, out, M, N, K, work, work_bytes, stream);
+        case 10: return launch_wide<8>(q, t, codes, out, M, N, K, work, work_bytes, stream);
+        case 12: return launch_wide<4>(q, t, codes, out, M, N, K, work, work_bytes, stream);
         case 6: return launch_ring_cfg<4, 4, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 7: return launch_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);
         case 8: return launch_ring_cfg<2, 2, 2, 2, 2>(q, t, codes, out, M, N, K, stream);

@@ -1,6 +1,7 @@
 // probe.hip -- the measurement probes of include/pq2_probe.h (gfx950): a
-// streaming read, an int8 matrix-core loop and a shader-clock reading. They
-// share nothing with the PQ2_0 kernels.
+// streaming read, an int8 matrix-core loop, the instruction mix of an exact
+// float32 per-group epilogue, and a shader-clock reading. They share nothing
+// with the PQ2_0 kernels.
 #include "../../include/pq2_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -8,6 +9,7 @@
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;               // 16-byte loads in flight per thread
@@ -57,6 +59,50 @@ __global__ __launch_bounds__(kThreads) void mfma_i8_kernel(int32_t *__restrict__
     if ((uint32_t)s == kNever) sink[blockIdx.x] = s;
 }
 
+// Per 16 x 16 output tile and 128-deep group: two v_mfma_i32_16x16x64_i8 (a
+// dependent pair, as a group's dot is), one v_mfma_f32_4x4x1_16b_f32 (sixteen
+// 4 x 4 outer products of two per-lane floats, i.e. a scale product per
+// output laid out like the int8 results), and per output element of a lane
+// one int32 -> float32 conversion and one FMA that reads the conversion and
+// the scale product. Eight tiles per wave with chains of their own; every
+// value carries from one round to the next, so nothing is hoisted or folded.
+__global__ __launch_bounds__(kThreads) void epilogue_mix_kernel(int32_t *__restrict__ sink,
+                                                                int iters) {
+    const int l = (int)threadIdx.x;
+    const v4i a0 = {l, l * 3 + 1, l ^ 0x55, 7 - l};
+    const v4i a1 = {l ^ 0x0f, l + 2, 5 * l, 3 - l};
+    const v4i b0 = {l * 5, l + 9, l ^ 0x33, 11 - l};
+    const v4i b1 = {l ^ 0x71, 2 * l + 1, l - 4, 13 ^ l};
+    const float wf = 1e-3f * (float)((l & 7) + 1);
+    const float sf = 1e-3f * (float)((l >> 3) + 1);
+    v4i c[8];
+    v4f sp[8];
+    float acc[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        c[j] = v4i{j, 0, 0, 0};
+        sp[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = 0.0f;
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, c[j], 0, 0, 0);
+            c[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, c[j], 0, 0, 0);
+            sp[j] = __builtin_amdgcn_mfma_f32_4x4x1f32(wf, sf, sp[j], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[j][i] = fmaf((float)c[j][i], sp[j][i], acc[j][i]);
+        }
+    }
+    float f = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f += acc[j][i];
+    if (__builtin_bit_cast(uint32_t, f) == kNever) sink[blockIdx.x] = 1;
+}
+
 // One wave: shader clock cycles against wall clock ticks over a spin.
 __global__ __launch_bounds__(64) void clock_kernel(uint64_t *__restrict__ out,
                                                    uint64_t spin_ticks) {
@@ -95,6 +141,15 @@ int pq2_probe_mfma_i8(int32_t *sink, int iters, int blocks, void *hip_stream) {
         !aligned(sink, 4))
         return -1;
     hipLaunchKernelGGL(mfma_i8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(hip_stream), sink, iters);
+    return status(hipGetLastError());
+}
+
+int pq2_probe_epilogue_mix(int32_t *sink, int iters, int blocks, void *hip_stream) {
+    if (!sink || iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > (1 << 20) ||
+        !aligned(sink, 4))
+        return -1;
+    hipLaunchKernelGGL(epilogue_mix_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(hip_stream), sink, iters);
     return status(hipGetLastError());
 }

@@ -48,6 +48,22 @@ int pq2_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int blo
 int pq2_probe_mfma_i8(int32_t *sink, int iters, int blocks, void *hip_stream);
 
 /*
+ * The instruction mix of an exact float32 per-group epilogue on int8 MFMA
+ * results (the PQ2_0 float epilogue of the page "Making a ternary reasoning
+ * model fast in vLLM", section "One token at a time: plain Triton is
+ * enough": y += s * ws * dot per group): per 16 x 16 output tile and
+ * 128-deep group, two v_mfma_i32_16x16x64_i8 (dependent), one
+ * v_mfma_f32_4x4x1_16b_f32 (the scale products as outer products) and, per
+ * output element of a lane, one int32 -> float32 conversion and one FMA;
+ * eight tiles per wave, no memory traffic in the loop. `blocks` blocks of 4
+ * waves run `iters` rounds; the int8 ops counted are those of the two int8
+ * MFMAs: blocks * 4 * iters * 8 * 2 * 32768. At most one word per block is
+ * written to sink (int32 [blocks]).
+ *   iters: 1 .. 2^24; blocks: 1 .. 2^20.
+ */
+int pq2_probe_epilogue_mix(int32_t *sink, int iters, int blocks, void *hip_stream);
+
+/*
  * Shader clock: one wave spins until the constant-rate wall clock counter
  * (wall_clock64, rate hipDeviceAttributeWallClockRate kHz) has advanced by
  * spin_ticks, and writes out[0] = shader clock cycles (clock64) and

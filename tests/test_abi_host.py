@@ -163,7 +163,9 @@ def test_workspace_query():
     # into 4 chunks of 128 x 256 float32 partial sums each.
     assert f(4096, 17408, 5120) == 128 * 4 * 128 * 256 * 4
     assert f(4096, 4096, 5120) == 0                     # 512 tiles: whole rounds only
-    assert f(512, 17408, 5120) == 0                     # a smaller tile, no split
+    # 512 x 17408: the 256 x 64 tile, 544 tiles, 32 left over in 4 chunks
+    assert f(512, 17408, 5120) == 32 * 4 * 64 * 256 * 4
+    assert f(512, 5120, 5120) == 0                      # the 64 x 64 tile: no split
     assert f(4096, 17408, 5248) == 0                    # 41 groups, not a multiple of 8: not the wide tile
 
 
@@ -185,6 +187,7 @@ def probe_lib():
     Pv, SZ = ctypes.c_void_p, ctypes.c_size_t
     lib.pq2_probe_stream_read.argtypes = [Pv, SZ, Pv, ctypes.c_int, Pv]
     lib.pq2_probe_mfma_i8.argtypes = [Pv, ctypes.c_int, ctypes.c_int, Pv]
+    lib.pq2_probe_epilogue_mix.argtypes = [Pv, ctypes.c_int, ctypes.c_int, Pv]
     lib.pq2_probe_clock.argtypes = [Pv, ctypes.c_uint64, Pv]
     return lib
 
@@ -192,7 +195,8 @@ def probe_lib():
 def test_probe_header_symbols_exported():
     src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(pq2_[a-z0-9_]+)\s*\(", src)))
-    assert names == ["pq2_probe_clock", "pq2_probe_mfma_i8", "pq2_probe_stream_read"]
+    assert names == ["pq2_probe_clock", "pq2_probe_epilogue_mix", "pq2_probe_mfma_i8",
+                     "pq2_probe_stream_read"]
     lib = probe_lib()
     for name in names:
         assert hasattr(lib, name), name
@@ -210,6 +214,12 @@ def test_probe_validation():
     assert g(None, 10, 256, None) == -1
     assert g(P, 0, 256, None) == -1
     assert g(P, 10, 0, None) == -1
+    e = lib.pq2_probe_epilogue_mix
+    assert e(None, 10, 256, None) == -1
+    assert e(P, 0, 256, None) == -1
+    assert e(P, (1 << 24) + 1, 256, None) == -1
+    assert e(P, 10, 0, None) == -1
+    assert e(P + 2, 10, 256, None) == -1           # sink 4-byte aligned
     h = lib.pq2_probe_clock
     assert h(None, 100, None) == -1
     assert h(P + 4, 100, None) == -1

@@ -841,28 +841,35 @@ def test_workspace_size_and_fallbacks(pq2, M, N, K):
     np.testing.assert_array_equal(host(d), oracle.group_dots(qo, w.codes))
 
 
-SPLIT_SHAPES = [(1100, 17408, 2048), (2100, 8200, 4096)]
+SPLIT_SHAPES = [(1100, 17408, 3072), (2100, 8200, 4096), (600, 17300, 5120)]
 
 
 @pytest.mark.parametrize("M,N,K", SPLIT_SHAPES)
 def test_prefill_tail_split(pq2, M, N, K):
-    """The wide prefill tile with the K range of its last tiles split across
-    blocks (partial sums in the workspace, added in chunk order): the size
-    query is a whole number of 128 x 256 float32 tiles; the tiles computed
-    whole are bit-identical with and without a workspace; every sampled output
-    (the split tiles' token rows and their ragged edges included) within
-    tolerance of the oracle; with unit scales y is the exact sum of the group
-    dots; the allocation-free entry, whose scratch array is too small for
-    these partial sums, gives the unsplit result bit for bit."""
+    """The wide prefill tiles (256 weight rows x 128 tokens for the first two
+    shapes, x 64 tokens for the third) with the K range of their last round's
+    tiles split across blocks (partial sums in the workspace, added in chunk
+    order): the size query is a whole number of partial tiles per split tile;
+    the tiles computed whole are bit-identical with and without a workspace;
+    every sampled output (the split tiles' token rows and their ragged edges
+    included) within tolerance of the oracle; with unit scales y is the exact
+    sum of the group dots; the allocation-free entry, whose scratch array is
+    smaller than these partial sums, gives the result of a workspace of the
+    scratch size."""
     wsz = pq2.gemm_workspace_bytes(M, N, K)
-    tile = 128 * 256 * 4
-    tiles_n, tiles_m = -(-N // 256), -(-M // 128)
+    tiles_n = -(-N // 256)
+    # the library's tile rule: 128 tokens where those tiles fill 7/8 of a
+    # round of two blocks per CU (256 CUs assumed by the rule), else 64
+    BM = 128 if tiles_n * -(-M // 128) >= 448 else 64
+    tile = BM * 256 * 4
+    tiles_m = -(-M // BM)
     T = tiles_n * tiles_m
     P = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     tail = T % P
-    print(f"tail split M={M} N={N} K={K} tiles={T} tail={tail} workspace={wsz}", flush=True)
+    print(f"tail split M={M} N={N} K={K} tile={BM} tiles={T} tail={tail} workspace={wsz}",
+          flush=True)
     assert pq2.gemm_kernel_path(M, N, K) == pq2.PATH_PREFILL
-    assert wsz > 0 and wsz % tile == 0 and wsz // tile == tail * (wsz // tile // tail)
+    assert wsz > 0 and wsz % tile == 0 and (wsz // tile) % tail == 0
     x = synth.activations(M, K, M + K, outlier_frac=0.0)
     w = synth.weights(N, K, synth.matrix_seed(N), synth.PREFILL_CODES)
     qo, so, to = oracle.quantize(x)
@@ -873,12 +880,12 @@ def test_prefill_tail_split(pq2, M, N, K):
     yw = torch.empty((M, N), dtype=torch.float32, device="cuda")
     pq2.pq2_gemm(qd, sd, td, cd, wd, ys, workspace=work)
     pq2.pq2_gemm(qd, sd, td, cd, wd, yw, workspace=None)
-    full_rows = ((T - tail) // tiles_n) * 128          # token panels computed whole
+    full_rows = ((T - tail) // tiles_n) * BM           # token panels computed whole
     hs, hw = host(ys), host(yw)
     np.testing.assert_array_equal(hs[:full_rows], hw[:full_rows])
     rng = np.random.default_rng(M + N)
     P_ = 768
-    lo = (T - tail) // tiles_n * 128                     # first row of a split tile
+    lo = (T - tail) // tiles_n * BM                      # first row of a split tile
     mm = np.concatenate([rng.integers(lo, M, P_ // 2), rng.integers(0, M, P_ // 2 - 4),
                          [lo, M - 1, M - 1, lo]])
     nn = np.concatenate([rng.integers(0, N, P_ - 4), [0, N - 1, 0, N - 1]])
