@@ -56,6 +56,17 @@ def linear_bytes(M, N, K):
     return N * K // 4 + 2 * N * G + 4 * M * K + 4 * M * N
 
 
+def one_launch(M, N, K):
+    """Where the one-launch pq2_linear (quantisation inside the GEMV) measured
+    faster than pq2_quantize_act + pq2_gemm on MI355X: one token row with
+    K <= 6144 and N * K <= 2^25 (decode 5120 x 6144: 6.57 against 7.29 us;
+    6144 x 5120: 6.93 against 7.24; the stacked 34816 x 5120 gate and up:
+    14.53 against 14.23; at K = 17408 and from two rows on, quantising in
+    every block costs more than the separate launch). The 64-layer step takes
+    it there; the bench line reports it beside its two-launch step."""
+    return M == 1 and K <= 6144 and N * K <= (1 << 25)
+
+
 def step_bytes(M, N, K):
     """Algorithmic HBM bytes of quantise + GEMM (q, s, t written and read back)."""
     return gemm_bytes(M, N, K) + quant_bytes(M, K)
@@ -447,6 +458,7 @@ def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
         out["sclk_mhz"] = median(sclk)
     if fused:
         out["fused_ms_step"] = per(fused_ms)
+        out["trial_fused_us"] = [v / steps * 1e3 for v in fused_ms]
     return out
 
 
@@ -466,6 +478,7 @@ def report_gemm(args, wl, r, torch):
         value = sbytes / (r["ms_step"] * 1e-3) / 1e9
         unit = "GB/s"
         achieved = gemm_bytes(M, N, K) / (r["kernel_ms"] * 1e-3) / 1e9
+    if not prefill:
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     roof["traffic"] = traffic_record(f"{path}_{wl.name}")
@@ -498,6 +511,9 @@ def report_gemm(args, wl, r, torch):
     }
     if fused:
         cfg["fused_step_us"] = r["fused_ms_step"] * 1e3
+        cfg["trial_fused_step_us"] = [round(v, 3) for v in r["trial_fused_us"]]
+        if one_launch(M, N, K):
+            cfg["one_launch_GB/s"] = linear_bytes(M, N, K) / (r["fused_ms_step"] * 1e-3) / 1e9
     if not args.no_cpu:
         line["cpu_baseline"] = (cpu_baseline_prefill(wl, args.cpu_seconds) if prefill
                                 else cpu_baseline(wl, args.cpu_seconds))
@@ -532,7 +548,7 @@ def layer_step(m, torch, pq2, stream):
     # 6144: 6.48 against 7.28; the stacked 34816 x 5120 gate and up: 14.53
     # against 14.23); the two-launch step elsewhere (at K = 17408 and from two
     # rows on, quantising in every block costs more than the separate launch)
-    fused = tuple(m == 1 and k <= 6144 and n * k <= (1 << 25) for (n, k) in synth.LAYER_SHAPES)
+    fused = tuple(one_launch(m, n, k) for (n, k) in synth.LAYER_SHAPES)
     calls = []
     for projs in layers:
         for i, (codes, ws, n, k) in enumerate(projs):

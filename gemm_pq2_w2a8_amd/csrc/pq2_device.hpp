@@ -26,15 +26,6 @@ __device__ __forceinline__ int dpp_xor1(int v) {
     return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
 }
 
-// Sum over aligned segments of `width` lanes (width a power of two <= 64);
-// every lane of a segment receives the segment's sum. Fixed butterfly order.
-template <int WIDTH>
-__device__ __forceinline__ float segment_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < WIDTH; off <<= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 // IEEE binary16 bit pattern -> float32 (exact; v_cvt_f32_f16).
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
@@ -87,6 +78,27 @@ __device__ __forceinline__ int swizzle_xor16(int v) {
 template <int I>
 __device__ __forceinline__ int dpp_quad_bcast(int v) {
     return __builtin_amdgcn_update_dpp(0, v, I * 0x55, 0xF, 0xF, false);
+}
+
+// Sum over aligned segments of `width` lanes (width a power of two <= 64);
+// every lane of a segment receives the segment's sum, bit for bit the same
+// on every lane (each step adds two lanes' values, and the partner adds the
+// same two). Steps: quad permutes (lane ^ 1, lane ^ 2), row half-mirror and
+// row mirror in the VALU, then one ds_swizzle across 16-lane rows and, for a
+// whole wave, one lane shuffle across the halves.
+template <int WIDTH>
+__device__ __forceinline__ float segment_sum(float v) {
+    static_assert(WIDTH >= 1 && WIDTH <= 64 && (WIDTH & (WIDTH - 1)) == 0, "segment width");
+    auto add = [](float a, int b) __attribute__((always_inline)) {
+        return a + __builtin_bit_cast(float, b);
+    };
+    if (WIDTH >= 2) v = add(v, dpp_xor1(__builtin_bit_cast(int, v)));
+    if (WIDTH >= 4) v = add(v, dpp_xor2(__builtin_bit_cast(int, v)));
+    if (WIDTH >= 8) v = add(v, dpp_half_mirror(__builtin_bit_cast(int, v)));
+    if (WIDTH >= 16) v = add(v, dpp_mirror(__builtin_bit_cast(int, v)));
+    if (WIDTH >= 32) v = add(v, swizzle_xor16(__builtin_bit_cast(int, v)));
+    if (WIDTH >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
 }
 
 __device__ __forceinline__ float seg32_max(float a) {
