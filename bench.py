@@ -4,8 +4,9 @@ A step is one pass of the hot path over one batch: pq2_quantize_act on the
 activations, then pq2_gemm against the next weight matrix of a rotating set
 (the set is larger than the 256 MB Infinity Cache, so weights stream from
 HBM). Inputs are resident in HBM before the timed region starts. For
-M <= 4 the single-launch pq2_linear (quantisation inside the GEMV) is timed
-too and reported in the config (fused_step_us).
+M <= 16 the step without the quantiser launch, pq2_linear (quantisation
+inside the GEMM kernel), is timed too where it has a kernel for the shape and
+reported in the config (fused_step_us).
 
 Default workload: decode GEMV, M = 1, N = 5120, K = 6144, 64 rotating
 matrices. ``--workload`` selects another configuration; ``--sweep`` prints
@@ -46,12 +47,12 @@ def quant_bytes(M, K):
     return 4 * M * K + M * K + 8 * M * G
 
 
-LINEAR_MAX_M = 4   # PQ2_LINEAR_MAX_M
+LINEAR_MAX_M = 16   # PQ2_LINEAR_MAX_M
 
 
 def linear_bytes(M, N, K):
-    """Algorithmic HBM bytes of the one-launch pq2_linear: codes + fp16 group
-    scales + float32 x + y (q, s and t never leave the kernel)."""
+    """Algorithmic HBM bytes of pq2_linear: codes + fp16 group scales +
+    float32 x + y (q, s and t never leave the kernel)."""
     G = K // GROUP
     return N * K // 4 + 2 * N * G + 4 * M * K + 4 * M * N
 
@@ -384,17 +385,19 @@ def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
     t = torch.empty((M, G), dtype=torch.int32, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
     wsz = pq2.gemm_workspace_bytes(M, N, K)
-    work = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
+    lwsz = pq2.linear_workspace_bytes(M, N, K) if M <= LINEAR_MAX_M else 0
+    work = torch.empty(max(wsz, lwsz, 16), dtype=torch.uint8, device=dev)
     R = len(codes)
     # raw pointers: the timed loop calls the C ABI directly (no per-call checks)
     lib = pq2.lib
     stream = torch.cuda.current_stream(dev).cuda_stream
     xp, qp, sp, tp, yp = x.data_ptr(), q.data_ptr(), s.data_ptr(), t.data_ptr(), y.data_ptr()
     wkp = work.data_ptr() if wsz else None
+    lwkp = work.data_ptr() if lwsz else None
     cps = [c.data_ptr() for c in codes]
     wps = [w.data_ptr() for w in scales]
     quant, gemm, linear = lib.pq2_quantize_act, lib.pq2_gemm, lib.pq2_linear
-    fused = M <= LINEAR_MAX_M
+    fused = M <= LINEAR_MAX_M and pq2.linear_kernel_path(M, N, K, lwsz) >= 0
     ctr = [0]          # one running matrix index over every pass
 
     def nxt():
@@ -417,7 +420,7 @@ def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
 
     def step_fused():
         i = nxt()
-        st = linear(xp, cps[i], wps[i], yp, M, N, K, stream)
+        st = linear(xp, cps[i], wps[i], yp, M, N, K, lwkp, lwsz, stream)
         if st:
             raise pq2.PQ2Error(st)
 
@@ -538,7 +541,8 @@ def layer_step(m, torch, pq2, stream):
                        torch.empty((m, k // GROUP), dtype=torch.int32, device=dev))
     ys = {n: torch.empty((m, n), dtype=torch.float32, device=dev) for (n, _) in synth.LAYER_SHAPES}
     # one split-K workspace serves every projection: they run in order on one stream
-    wsz = max(pq2.gemm_workspace_bytes(m, n, k) for (n, k) in synth.LAYER_SHAPES)
+    wsz = max(max(pq2.gemm_workspace_bytes(m, n, k), pq2.linear_workspace_bytes(m, n, k))
+              for (n, k) in synth.LAYER_SHAPES)
     work = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
     wkp = work.data_ptr() if wsz else None
     lib = pq2.lib
@@ -560,7 +564,7 @@ def layer_step(m, torch, pq2, stream):
     def step(after=None):
         for (fz, xp, qp, sp, tp, cp, wp, yp, n, k) in calls:
             if fz:
-                linear(xp, cp, wp, yp, m, n, k, stream)
+                linear(xp, cp, wp, yp, m, n, k, wkp, wsz, stream)
             else:
                 quant(xp, qp, sp, tp, m, k, stream)
                 gemm(qp, sp, tp, cp, wp, yp, m, n, k, wkp, wsz, stream)

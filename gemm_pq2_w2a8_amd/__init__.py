@@ -55,14 +55,19 @@ lib.pq2_gemm_path.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c
 lib.pq2_gemm_group_dots.restype = ctypes.c_int
 lib.pq2_gemm_group_dots.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P]
 lib.pq2_linear.restype = ctypes.c_int
-lib.pq2_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P]
+lib.pq2_linear.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]
+lib.pq2_linear_workspace_bytes.restype = _SZ
+lib.pq2_linear_workspace_bytes.argtypes = [_I64, _I64, _I64]
+lib.pq2_linear_kernel_path.restype = ctypes.c_int
+lib.pq2_linear_kernel_path.argtypes = [_I64, _I64, _I64, _SZ]
 
-LINEAR_MAX_M = 4    # PQ2_LINEAR_MAX_M
+LINEAR_MAX_M = 16   # PQ2_LINEAR_MAX_M
 
 # Every extern "C" symbol declared in include/pq2.h.
 ABI_SYMBOLS = ("pq2_abi_version", "pq2_status_str", "pq2_quantize_act", "pq2_quantize_act_16",
                "pq2_gemm_workspace_bytes", "pq2_gemm", "pq2_gemm_noalloc", "pq2_gemm_bf16",
-               "pq2_gemm_kernel_path", "pq2_gemm_path", "pq2_linear", "pq2_gemm_group_dots")
+               "pq2_gemm_kernel_path", "pq2_gemm_path", "pq2_linear", "pq2_linear_workspace_bytes",
+               "pq2_linear_kernel_path", "pq2_gemm_group_dots")
 
 NOALLOC_SCRATCH_BYTES = 16 << 20    # PQ2_NOALLOC_SCRATCH_BYTES
 
@@ -73,6 +78,20 @@ PATH_NAMES = {PATH_GEMV: "gemv_dot4", PATH_SMALL: "small_mfma", PATH_PREFILL: "p
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     """Workspace bytes of pq2_gemm's fastest plan for this shape (0: none needed)."""
     return int(lib.pq2_gemm_workspace_bytes(M, N, K))
+
+
+def linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes of pq2_linear's plan for this shape (0: none needed)."""
+    return int(lib.pq2_linear_workspace_bytes(M, N, K))
+
+
+def linear_kernel_path(M: int, N: int, K: int, workspace_bytes: Optional[int] = None) -> int:
+    """PATH_GEMV or PATH_PANEL: the kernel pq2_linear takes for this shape given
+    a workspace of that many bytes (None: what linear_workspace_bytes asks
+    for); -1 where pq2_linear rejects the shape."""
+    if workspace_bytes is None:
+        workspace_bytes = linear_workspace_bytes(M, N, K)
+    return int(lib.pq2_linear_kernel_path(M, N, K, int(workspace_bytes)))
 
 
 def gemm_kernel_path(M: int, N: int, K: int, workspace_bytes: Optional[int] = None) -> int:
@@ -146,16 +165,17 @@ def pq2_quantize_act(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, t: torch
                                 _stream(x, stream)))
 
 
-def _workspace(workspace, M: int, N: int, K: int, device, stream) -> Tuple[int, int, object]:
+def _workspace(workspace, M: int, N: int, K: int, device, stream,
+               query=None) -> Tuple[int, int, object]:
     """(pointer, bytes, keep-alive) of the split-K workspace argument: "auto"
-    allocates the size pq2_gemm_workspace_bytes asks for with torch (none when
-    0), None passes no workspace, a device tensor passes its storage. An
+    allocates the size pq2_gemm_workspace_bytes (or `query`) asks for with
+    torch (none when 0), None passes no workspace, a device tensor passes its storage. An
     "auto" buffer is tied to the launch stream, so torch's allocator does not
     hand it out again before the kernels on that stream are done with it."""
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError('workspace must be "auto", None or a device tensor')
-        n = gemm_workspace_bytes(M, N, K)
+        n = (query or gemm_workspace_bytes)(M, N, K)
         if n == 0:
             return 0, 0, None
         workspace = torch.empty(n, dtype=torch.uint8, device=device)
@@ -241,8 +261,10 @@ def pq2_gemm_path(q: torch.Tensor, s: torch.Tensor, t: torch.Tensor, codes: torc
 
 
 def pq2_linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor, y: torch.Tensor,
-               stream=None) -> None:
-    """y float32 [M][N] from float32 x [M][K] in one launch (M <= LINEAR_MAX_M)."""
+               workspace="auto", stream=None) -> None:
+    """y float32 [M][N] from float32 x [M][K] with the quantisation inside the
+    GEMM kernel (M <= LINEAR_MAX_M). workspace as for pq2_gemm, sized by
+    linear_workspace_bytes."""
     M, K = _mk(x)
     N = int(codes.shape[0])
     G = K // GROUP
@@ -252,8 +274,9 @@ def pq2_linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor, y: to
         wscale = wscale.view(torch.int16)
     _need(wscale, "wscale", torch.int16, (N, G))
     _need(y, "y", torch.float32, (M, N))
+    wp, wn, _keep = _workspace(workspace, M, N, K, x.device, stream, linear_workspace_bytes)
     _check(lib.pq2_linear(x.data_ptr(), codes.data_ptr(), wscale.data_ptr(), y.data_ptr(),
-                          M, N, K, _stream(x, stream)))
+                          M, N, K, wp, wn, _stream(x, stream)))
 
 
 def pq2_gemm_group_dots(q: torch.Tensor, t: torch.Tensor, codes: torch.Tensor,
@@ -285,14 +308,15 @@ def quantize_act(x: torch.Tensor, stream=None):
 
 def linear(x: torch.Tensor, codes: torch.Tensor, wscale: torch.Tensor,
            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Whole path, y float32 [M][N]: one pq2_linear launch for float32 x with
-    M <= LINEAR_MAX_M, else pq2_quantize_act (float32, bfloat16 or float16 x)
-    into torch-allocated q/s/t followed by pq2_gemm."""
+    """Whole path, y float32 [M][N]: pq2_linear for float32 x with one token
+    row (where quantising inside the GEMV beats the separate launch), else
+    pq2_quantize_act (float32, bfloat16 or float16 x) into torch-allocated
+    q/s/t followed by pq2_gemm."""
     M = int(x.shape[0])
     N = int(codes.shape[0])
     y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
-    if M <= LINEAR_MAX_M and x.dtype == torch.float32:
-        pq2_linear(x, codes, wscale, y, stream)
+    if M == 1 and x.dtype == torch.float32:
+        pq2_linear(x, codes, wscale, y, stream=stream)
         return y
     q, s, t = quantize_act(x, stream)
     pq2_gemm(q, s, t, codes, wscale, y, stream=stream)

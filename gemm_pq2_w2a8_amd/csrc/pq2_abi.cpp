@@ -118,6 +118,20 @@ pq2_status check_gemm(const int8_t *q, const float *s, const int32_t *t, const u
     return PQ2_OK;
 }
 
+// Kernel of pq2_linear: the fused dot4 GEMV for one or two token rows (it
+// reads only the real rows) and, without a ring plan, for three or four;
+// the fused ring variant of the panel kernel for 3 to 16 rows where it has
+// a plan with the K chunks the workspace holds (max_s); 0: no fused kernel.
+enum LinearKernel { kLinearNone = 0, kLinearGemv = 1, kLinearRing = 2 };
+
+LinearKernel linear_kernel(int64_t M, int64_t N, int64_t K, int max_s) {
+    if (M <= 2) return kLinearGemv;
+    if (M <= PQ2_LINEAR_MAX_M && pq2::small_panel_fused_splits(M, N, K, max_s) > 0)
+        return kLinearRing;
+    if (M <= pq2::kGemvMaxM) return kLinearGemv;
+    return kLinearNone;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,7 +145,7 @@ const char *pq2_status_str(int status) {
         case PQ2_ERR_SHAPE: return "PQ2_ERR_SHAPE: need M >= 1, N >= 1, K a positive multiple of 128, K <= 2^24";
         case PQ2_ERR_ALIGN: return "PQ2_ERR_ALIGN: a base pointer is misaligned";
         case PQ2_ERR_HIP: return "PQ2_ERR_HIP: the HIP runtime rejected a launch";
-        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this shape and workspace, M too large for pq2_linear, or unknown activation format";
+        case PQ2_ERR_ARG: return "PQ2_ERR_ARG: invalid path selector for this shape and workspace, no fused kernel of pq2_linear for this shape and workspace, or unknown activation format";
         case PQ2_ERR_SCRATCH: return "PQ2_ERR_SCRATCH: the shape needs more split-K scratch than pq2_gemm_noalloc holds (PQ2_NOALLOC_SCRATCH_BYTES)";
         default: return "PQ2 unknown status";
     }
@@ -232,17 +246,44 @@ pq2_status pq2_gemm_path(const int8_t *q, const float *s, const int32_t *t, cons
                     workspace_bytes, static_cast<hipStream_t>(hip_stream));
 }
 
+size_t pq2_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (check_mnk(M, N, K) != PQ2_OK || M > PQ2_LINEAR_MAX_M) return 0;
+    if (linear_kernel(M, N, K, pq2::kPanelMaxSplits) != kLinearRing) return 0;
+    const int S = pq2::small_panel_fused_splits(M, N, K, pq2::kPanelMaxSplits);
+    return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+int pq2_linear_kernel_path(int64_t M, int64_t N, int64_t K, size_t workspace_bytes) {
+    if (check_mnk(M, N, K) != PQ2_OK || M > PQ2_LINEAR_MAX_M) return -1;
+    switch (linear_kernel(M, N, K, splits_for_bytes(workspace_bytes, M, N))) {
+        case kLinearGemv: return PQ2_PATH_GEMV;
+        case kLinearRing: return PQ2_PATH_PANEL;
+        default: return -1;
+    }
+}
+
 pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
-                      int64_t M, int64_t N, int64_t K, void *hip_stream) {
-    static_assert(PQ2_LINEAR_MAX_M <= pq2::kGemvMaxM, "the fused GEMV covers pq2_linear");
+                      int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                      void *hip_stream) {
     if (!x || !codes || !wscale || !y) return PQ2_ERR_NULL;
     pq2_status st = check_mnk(M, N, K);
     if (st != PQ2_OK) return st;
-    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(wscale, 2) || !aligned(y, 4))
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(wscale, 2) || !aligned(y, 4) ||
+        (workspace && !aligned(workspace, 16)))
         return PQ2_ERR_ALIGN;
     if (M > PQ2_LINEAR_MAX_M) return PQ2_ERR_ARG;
-    return from_hip(pq2::launch_gemv_fused(x, codes, wscale, y, M, N, K,
-                                           static_cast<hipStream_t>(hip_stream)));
+    const int max_s = max_splits(workspace, workspace_bytes, M, N);
+    const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    switch (linear_kernel(M, N, K, max_s)) {
+        case kLinearGemv:
+            return from_hip(pq2::launch_gemv_fused(x, codes, wscale, y, M, N, K, stream));
+        case kLinearRing:
+            return from_hip(pq2::launch_small_panel_fused(x, codes, wscale, y, M, N, K, max_s,
+                                                          static_cast<float *>(workspace),
+                                                          stream));
+        default:
+            return PQ2_ERR_ARG;
+    }
 }
 
 pq2_status pq2_gemm_group_dots(const int8_t *q, const int32_t *t, const uint8_t *codes,

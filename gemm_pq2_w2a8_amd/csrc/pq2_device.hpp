@@ -119,6 +119,24 @@ __device__ __forceinline__ int seg32_sum(int v) {
     return v;
 }
 
+// Per-element steps of the int8 quantiser, shared by every kernel that
+// quantises activations so that all of them give identical q (the
+// reasoning is given with quantize_groups32 below): the tiny-scale test, the
+// fast rounding of x / s through rc = v_rcp_f32(s) with the flag that says
+// it equals the IEEE quotient's rounding, and the final clamp.
+__device__ __forceinline__ bool quant_tiny(float scale) { return scale < 0x1p-100f; }
+
+__device__ __forceinline__ float quant_round_fast(float x, float rc, bool tiny, bool &ok) {
+    const float y = x * rc;
+    const float ry = rintf(y);
+    ok = !tiny && fabsf(fabsf(y - ry) - 0.5f) > 0x1p-13f;
+    return ry;
+}
+
+__device__ __forceinline__ int quant_clamp(float qf, float scale) {
+    return scale == 0.0f ? 0 : (int)fminf(fmaxf(qf, -127.0f), 127.0f);
+}
+
 // Per-128-group int8 quantisation of activations in plane order, shared by
 // the quantise kernel and the fused GEMV so both give identical q, s, t.
 // 32 lanes hold one group (lane b: x[4b .. 4b+3]); amax and the sum of q are
@@ -163,26 +181,24 @@ __device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lan
     for (int r = 0; r < NR; ++r) {
         scale[r] = a[r] / 127.0f;                   // IEEE division
         rc[r] = __builtin_amdgcn_rcpf(scale[r]);
-        const bool tiny = scale[r] < 0x1p-100f;     // includes s == 0
+        const bool tiny = quant_tiny(scale[r]);     // includes s == 0
         const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float y = xs[e] * rc[r];
-            const float ry = rintf(y);
-            const bool ok = !tiny && fabsf(fabsf(y - ry) - 0.5f) > 0x1p-13f;
+            bool ok;
+            qf[r][e] = quant_round_fast(xs[e], rc[r], tiny, ok);
             slow |= !ok && scale[r] != 0.0f;
-            qf[r][e] = ry;
         }
     }
     if (__any(slow)) {                              // rare: the IEEE division decides
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const bool tiny = scale[r] < 0x1p-100f;
+            const bool tiny = quant_tiny(scale[r]);
             const float xs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float y = xs[e] * rc[r];
-                const bool ok = !tiny && fabsf(fabsf(y - rintf(y)) - 0.5f) > 0x1p-13f;
+                bool ok;
+                quant_round_fast(xs[e], rc[r], tiny, ok);
                 if (!ok && scale[r] != 0.0f) qf[r][e] = rintf(xs[e] / scale[r]);
             }
         }
@@ -192,8 +208,7 @@ __device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lan
     for (int r = 0; r < NR; ++r) {
         int q[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            q[e] = scale[r] == 0.0f ? 0 : (int)fminf(fmaxf(qf[r][e], -127.0f), 127.0f);
+        for (int e = 0; e < 4; ++e) q[e] = quant_clamp(qf[r][e], scale[r]);
         sum[r] = q[0] + q[1] + q[2] + q[3];
         // byte p of u = q of column 4*lane32 + p, i.e. plane p, position lane32
         u[r] = (int)((uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |

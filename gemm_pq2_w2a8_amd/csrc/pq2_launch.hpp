@@ -66,6 +66,16 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
                               const GemmOut &out, int64_t M, int64_t N, int64_t K,
                               int max_splits, float *work, hipStream_t stream);
 
+// Quantise + ring-variant panel kernel in one launch (plus the split sum when
+// K is cut into chunks): y from float32 x, M <= 16, where the ring variant
+// has a plan (small_panel_ring_fits). small_panel_fused_splits gives its K
+// chunks (0: no plan); work holds that many M x N float32 partial sums when
+// above 1.
+int small_panel_fused_splits(int64_t M, int64_t N, int64_t K, int max_splits);
+hipError_t launch_small_panel_fused(const float *x, const uint8_t *codes, const uint16_t *ws,
+                                    float *y, int64_t M, int64_t N, int64_t K, int max_splits,
+                                    float *work, hipStream_t stream);
+
 // The allocation-free entry's split-K buffer: kScratchBytes of device memory
 // per device (a file-scope array), its address on the current device looked
 // up once per device (nullptr and *err set if the lookup fails).

@@ -601,6 +601,117 @@ __host__ __device__ constexpr int64_t ring_lds_bytes(int cpt, int nw) {
     return (int64_t)kRingSlots * (cpt * nw / 2 * 1024 + 2048) + 1024 + 2 * nw * 1024;
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// v_permlane32_swap(a, b): lanes 32..63 of a trade places with lanes 0..31
+// of b. Returns the new a and b. (The elements of the builtin's result are
+// read into scalars before any bit cast: a bit cast applied to a vector
+// element expression reads element 0.)
+__device__ __forceinline__ void swap_halves(uint32_t &a, uint32_t &b) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    const uint32_t na = sw[0], nb = sw[1];
+    a = na;
+    b = nb;
+}
+
+// Max and sum of this lane's value and that of lane ^ 32: with a == b, the
+// swap leaves the lower half's value in a and the upper half's in b.
+__device__ __forceinline__ float max_halves(float v) {
+    uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+    swap_halves(a, b);
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ int sum_halves(int v) {
+    uint32_t a = (uint32_t)v, b = a;
+    swap_halves(a, b);
+    return (int)a + (int)b;
+}
+
+// In-register quantisation of one 128-activation group of one token into the
+// ring variant's A fragments (the fused entry). Lanes c, c + 16, c + 32 and
+// c + 48 (lane group lg = 0..3) hold token c's group between them: lane lg
+// has loaded the 32 activations [64 h + 32 u, 64 h + 32 u + 32) of it as
+// f[j] = x[64 h + 32 u + 4 j .. + 3] (h = lg & 1, u = lg >> 1). Its
+// fragments need planes p0 = u and p0 + 2 at plane positions 16 h .. 16 h +
+// 15, i.e. activations 64 h + 4 i + p0 (a0 byte i) and 64 h + 4 i + p0 + 2
+// (a1 byte i), i = 0..15; for i >= 8 they sit in lane ^ 32 (same h, other
+// u), which in turn needs this lane's other two planes. One
+// v_permlane32_swap per component pair trades them, after which
+// a0 byte i comes from f[i].x (i < 8) or f[i - 8].y and a1 byte i from f[i].z
+// or f[i - 8].w, in every lane. amax and sum(q) are reductions over the four
+// lanes (lane ^ 16 by ds_swizzle, lane ^ 32 by v_permlane32_swap); the
+// rounding is the quantiser's own (quant_* helpers), so q, s and t are those
+// pq2_quantize_act writes, bit for bit. Returns s and t of token c in every
+// lane of the token.
+__device__ __forceinline__ void quantize_ring_frag(v4f (&f)[8], v4i &a0, v4i &a1, float &scale,
+                                                   int &tsum) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(f[j].x), fabsf(f[j].y)), fmaxf(fabsf(f[j].z), fabsf(f[j].w))));
+    a = fmaxf(a, __builtin_bit_cast(float, swizzle_xor16(__builtin_bit_cast(int, a))));
+    a = max_halves(a);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float fx = f[j].x, fy = f[j].y, fz = f[j].z, fw = f[j].w;
+        uint32_t x0 = __builtin_bit_cast(uint32_t, fx), y0 = __builtin_bit_cast(uint32_t, fy);
+        uint32_t z0 = __builtin_bit_cast(uint32_t, fz), w0 = __builtin_bit_cast(uint32_t, fw);
+        swap_halves(x0, y0);
+        swap_halves(z0, w0);
+        f[j] = v4f{__builtin_bit_cast(float, x0), __builtin_bit_cast(float, y0),
+                   __builtin_bit_cast(float, z0), __builtin_bit_cast(float, w0)};
+    }
+    scale = a / 127.0f;                             // IEEE division
+    const float rc = __builtin_amdgcn_rcpf(scale);
+    const bool tiny = quant_tiny(scale);
+    // element i of fragment p: p = 0 planes p0, p = 1 planes p0 + 2
+    auto elem = [&](int p, int i) __attribute__((always_inline)) {
+        const v4f &v = f[i & 7];
+        return p == 0 ? (i < 8 ? v.x : v.y) : (i < 8 ? v.z : v.w);
+    };
+    float qf[2][16];
+    bool slow = false;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            bool ok;
+            qf[p][i] = quant_round_fast(elem(p, i), rc, tiny, ok);
+            slow |= !ok && scale != 0.0f;
+        }
+    if (__any(slow)) {                              // rare: the IEEE division decides
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                bool ok;
+                quant_round_fast(elem(p, i), rc, tiny, ok);
+                if (!ok && scale != 0.0f) qf[p][i] = rintf(elem(p, i) / scale);
+            }
+    }
+    v4i w[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                word |= ((uint32_t)quant_clamp(qf[p][4 * k + e], scale) & 0xffu) << (8 * e);
+            w[p][k] = (int)word;
+        }
+    a0 = w[0];
+    a1 = w[1];
+    int t = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        t = dot4((uint32_t)w[0][k], 0x01010101u, t);
+        t = dot4((uint32_t)w[1][k], 0x01010101u, t);
+    }
+    t += swizzle_xor16(t);
+    tsum = sum_halves(t);
+}
+
 // Ring variant (M <= 16, chunks of a multiple of 8 groups): same arithmetic,
 // but the A side never moves again once loaded. Wave w owns groups
 // [g_lo, g_lo + ng) of the chunk for every tile, so its A fragments, -t seeds
@@ -618,8 +729,9 @@ __host__ __device__ constexpr int64_t ring_lds_bytes(int cpt, int nw) {
 // own copies of the tile; after it, tile j - 1's slot is free for tile
 // j + kRingSlots - 1, and tile j - 1's partials (double-buffered) are summed
 // and stored.
-template <int NW, int GSG, int CPT, bool DOTS>
+template <int NW, int GSG, int CPT, bool DOTS, bool FUSED>
 __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
+    const float *__restrict__ x,
     const int8_t *__restrict__ q, const float *__restrict__ s, const int32_t *__restrict__ t,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ ws, float *__restrict__ y,
     uint16_t *__restrict__ y16, int32_t *__restrict__ d, float *__restrict__ part_out, int64_t M,
@@ -707,10 +819,44 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
     // zero seeds and scales, A repeats the last row; their outputs are never
     // stored), then the first R - 1 tiles' copies behind them.
     const int arow = c < Mr ? c : Mr - 1;
-    typedef float v4f __attribute__((ext_vector_type(4)));
     v4i a0[GSG], a1[GSG], seed[GSG];
     v4f sv[GSG];
-    {
+    if constexpr (FUSED) {
+        // float32 x instead: the loads of the first two groups, the first
+        // tiles' copies behind them, then each group quantised in registers
+        // (quantize_ring_frag) while the loads of the group after next are
+        // in flight; -t and s of the lane's output tokens 4 lg + i come from
+        // lane 4 lg + i, which quantised that token.
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (int64_t)Mr * K * 4);
+        const int xlane = arow * (int)K * 4 + 256 * (lg & 1) + 128 * (lg >> 1);
+        v4f xf[2][8];
+        auto load_x = [&](v4f (&f)[8], int b) __attribute__((always_inline)) {
+            const int off = xlane + 512 * (g0 + g_lo + (b < ng ? b : ng - 1));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                f[j] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16 * j, 0, 0));
+        };
+        load_x(xf[0], 0);
+        if constexpr (GSG > 1) load_x(xf[1], 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (copier) {
+#pragma unroll
+            for (int p = 0; p < R - 1; ++p) issue(p);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < GSG; ++b) {
+            float sc;
+            int ts;
+            quantize_ring_frag(xf[b & 1], a0[b], a1[b], sc, ts);
+            if (b + 2 < GSG) load_x(xf[b & 1], b + 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                seed[b][i] = -__shfl(ts, 4 * lg + i, kWave);
+                sv[b][i] = __shfl(sc, 4 * lg + i, kWave);
+            }
+        }
+    } else {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)Mr * K);
         const __amdgpu_buffer_rsrc_t rt = make_rsrc(t, (int64_t)Mr * G * 4);
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(s, DOTS ? 0 : (int64_t)Mr * G * 4);
@@ -729,11 +875,11 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
                     sv[b][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, toff, 0, 0));
             }
         }
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep the copies behind these loads
-    if (copier) {
+        __builtin_amdgcn_sched_barrier(0);   // keep the copies behind these loads
+        if (copier) {
 #pragma unroll
-        for (int p = 0; p < R - 1; ++p) issue(p);
+            for (int p = 0; p < R - 1; ++p) issue(p);
+        }
     }
     // Hand the fragments to the loop as plain register values: the compiler
     // waits for their loads here (only the copies behind them may stay in
@@ -820,6 +966,7 @@ __global__ __launch_bounds__(NW * kWave) void small_panel_ring_kernel(
     };
 
     static_assert(NW == 8, "four summing waves, one per partial slot");
+    static_assert(!(FUSED && DOTS), "the fused variant writes y");
     if (copier) {
         for (int j = 0; j < cnt; ++j) {
             wait_vmem<(R - 2) * LPT>();  // this thread's copies of tile j have landed
@@ -967,29 +1114,37 @@ hipError_t launch_sc(int64_t gs, const int8_t *q, const int32_t *t, const uint8_
 #undef PQ2_PANEL_SC
 }
 
-template <int NW, int GSG, bool DOTS>
-hipError_t launch_ring_cfg(const int8_t *q, const int32_t *t, const uint8_t *codes,
-                           const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
-                           int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
+template <int NW, int GSG, bool DOTS, bool FUSED>
+hipError_t launch_ring_cfg(const float *x, const int8_t *q, const int32_t *t,
+                           const uint8_t *codes, const GemmOut &out, float *part, int64_t M,
+                           int64_t N, int64_t K, int gsplit, int bps, int64_t blocks, size_t lds,
+                           hipStream_t stream) {
     constexpr int CPT = GSG;     // 32 * 8 GSG code units over the 256 copy threads, NW = 8
-    hipLaunchKernelGGL((small_panel_ring_kernel<NW, GSG, CPT, DOTS>), dim3((unsigned)blocks),
-                       dim3(NW * kWave), lds, stream, q, DOTS ? nullptr : out.s, t, codes,
+    hipLaunchKernelGGL((small_panel_ring_kernel<NW, GSG, CPT, DOTS, FUSED>), dim3((unsigned)blocks),
+                       dim3(NW * kWave), lds, stream, x, q, DOTS ? nullptr : out.s, t, codes,
                        DOTS ? nullptr : out.ws, DOTS ? nullptr : out.y, DOTS ? nullptr : out.y16,
                        out.d, part, M, N, K,
                        gsplit, bps);
     return hipGetLastError();
 }
 
+// x != nullptr: the fused variant (quantises x itself; q and t unused).
 template <int NW>
-hipError_t launch_ring(int64_t gs, const int8_t *q, const int32_t *t, const uint8_t *codes,
-                       const GemmOut &out, float *part, int64_t M, int64_t N, int64_t K,
-                       int gsplit, int bps, int64_t blocks, size_t lds, hipStream_t stream) {
-#define PQ2_PANEL_RING(V)                                                                    \
-    case V:                                                                                  \
-        return out.d ? launch_ring_cfg<NW, V, true>(q, t, codes, out, part, M, N, K, gsplit, \
-                                                     bps, blocks, lds, stream)               \
-                     : launch_ring_cfg<NW, V, false>(q, t, codes, out, part, M, N, K,        \
-                                                      gsplit, bps, blocks, lds, stream);
+hipError_t launch_ring(int64_t gs, const float *x, const int8_t *q, const int32_t *t,
+                       const uint8_t *codes, const GemmOut &out, float *part, int64_t M,
+                       int64_t N, int64_t K, int gsplit, int bps, int64_t blocks, size_t lds,
+                       hipStream_t stream) {
+#define PQ2_PANEL_RING(V)                                                                       \
+    case V:                                                                                     \
+        if (out.d)                                                                              \
+            return launch_ring_cfg<NW, V, true, false>(nullptr, q, t, codes, out, part, M, N,   \
+                                                       K, gsplit, bps, blocks, lds, stream);    \
+        if (x)                                                                                  \
+            return launch_ring_cfg<NW, V, false, true>(x, nullptr, nullptr, codes, out, part,   \
+                                                       M, N, K, gsplit, bps, blocks, lds,       \
+                                                       stream);                                 \
+        return launch_ring_cfg<NW, V, false, false>(nullptr, q, t, codes, out, part, M, N, K,   \
+                                                    gsplit, bps, blocks, lds, stream);
     switch (gs) {
         PQ2_PANEL_RING(1)
         PQ2_PANEL_RING(2)
@@ -1225,7 +1380,7 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
     const int64_t blocks = (int64_t)plan.bps * plan.S;
     hipError_t e;
     if (rg)
-        e = launch_ring<kPanelWaves>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
+        e = launch_ring<kPanelWaves>(plan.gs, nullptr, q, t, codes, out, part, M, N, K, plan.gsplit,
                                      plan.bps, blocks, plan.lds, stream);
     else if (sc && plan.tt == 1)
         e = launch_sc<kPanelWaves, 1>(plan.gs, q, t, codes, out, part, M, N, K, plan.gsplit,
@@ -1241,6 +1396,32 @@ hipError_t launch_small_panel(const int8_t *q, const int32_t *t, const uint8_t *
                                       plan.bps, blocks, plan.lds, stream);
     if (e != hipSuccess || !part) return e;
     return launch_split_sum(part, out.y, out.y16, M * N, plan.S, stream);
+}
+
+int small_panel_fused_splits(int64_t M, int64_t N, int64_t K, int max_splits) {
+    if (!small_panel_ring_fits(M, K, max_splits)) return 0;
+    return plan_ring(M, N, K, dev_limits(), max_splits).S;
+}
+
+// The ring variant's plan for this shape, with the fused prologue: the same
+// tiles, chunks and split sums as launch_small_panel's ring plan.
+hipError_t launch_small_panel_fused(const float *x, const uint8_t *codes, const uint16_t *ws,
+                                    float *y, int64_t M, int64_t N, int64_t K, int max_splits,
+                                    float *work, hipStream_t stream) {
+    if (!small_panel_ring_fits(M, K, max_splits)) return hipErrorInvalidValue;
+    const PanelPlan plan = plan_ring(M, N, K, dev_limits(), max_splits);
+    if (plan.S == 0) return hipErrorInvalidValue;
+    float *part = nullptr;
+    if (plan.S > 1) {
+        if (!work) return hipErrorInvalidValue;
+        part = work;
+    }
+    const GemmOut out{y, nullptr, nullptr, ws};
+    const int64_t blocks = (int64_t)plan.bps * plan.S;
+    hipError_t e = launch_ring<kPanelWaves>(plan.gs, x, nullptr, nullptr, codes, out, part, M, N,
+                                            K, plan.gsplit, plan.bps, blocks, plan.lds, stream);
+    if (e != hipSuccess || !part) return e;
+    return launch_split_sum(part, y, nullptr, M * N, plan.S, stream);
 }
 
 }  // namespace pq2

@@ -46,9 +46,9 @@
  *                every launch grid below 2^31 blocks);
  *  PQ2_ERR_ALIGN a base pointer breaks the alignment stated above (a
  *                workspace, when given, must be 16-byte aligned);
- *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), M above
- *                PQ2_LINEAR_MAX_M (pq2_linear), or an unknown activation
- *                format (pq2_quantize_act_16);
+ *  PQ2_ERR_ARG   an invalid path selector (pq2_gemm_group_dots), a shape
+ *                and workspace no fused kernel of pq2_linear runs, or an
+ *                unknown activation format (pq2_quantize_act_16);
  *  PQ2_ERR_SCRATCH (pq2_gemm_noalloc) the small-batch plan's split-K partial
  *                sums need more than PQ2_NOALLOC_SCRATCH_BYTES;
  *  PQ2_ERR_HIP   a kernel launch was rejected by the HIP runtime.
@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define PQ2_ABI_VERSION 2
+#define PQ2_ABI_VERSION 3
 #define PQ2_GROUP 128
 #define PQ2_MAX_DIM (1LL << 30)
 #define PQ2_MAX_K (1LL << 24)
@@ -225,25 +225,54 @@ pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t,
                          void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
- * Quantise and multiply in one launch, for decode batches of 1 to 4 token
- * rows (PQ2_LINEAR_MAX_M): y = the PQ2_0 product of x quantised exactly as
- * pq2_quantize_act would (page "Making a ternary reasoning model fast in
- * vLLM", section "Prompt processing: check configuration and launch costs",
- * counts a separate quantiser launch per projection; this entry removes it).
- * Every block of the v_dot4 GEMV quantises the activations it needs into
- * LDS, with the same arithmetic as pq2_quantize_act, so y is bit-identical
- * to pq2_quantize_act followed by pq2_gemm's GEMV path. q, s and t are not
- * written anywhere. For callers that cannot hold q/s/t buffers: every block
- * re-quantises the whole activation row, which on MI355X costs more than the
- * separate quantiser launch it saves (pq2_quantize_act + pq2_gemm is the
- * faster decode step).
+ * Quantise and multiply without the separate quantiser launch, for decode
+ * batches of 1 to 16 token rows (PQ2_LINEAR_MAX_M): y = the PQ2_0 product of
+ * x quantised exactly as pq2_quantize_act would (page "Making a ternary
+ * reasoning model fast in vLLM", section "Prompt processing: check
+ * configuration and launch costs", counts a quantiser launch per projection;
+ * section "Choose the configuration with the proxy" charges its time to the
+ * matmul). The GEMM kernel quantises the activations it needs itself, with
+ * the quantiser's arithmetic, so q, s and t -- never written anywhere -- are
+ * bit for bit those of pq2_quantize_act, and y is bit-identical to
+ * pq2_quantize_act followed by pq2_gemm on the same kernel path:
+ *   M = 1, 2 (and 3, 4 where the panel kernel below has no plan): the v_dot4
+ *     GEMV; every block quantises the whole activation row into LDS.
+ *   M = 3 .. 16 with K a multiple of 1024 in [2048, 18432]: the persistent
+ *     panel kernel (PQ2_PATH_PANEL, its ring variant), each wave quantising
+ *     its own groups of every token in registers. Its K chunks and their
+ *     split sum are those of pq2_gemm: K up to 6144 runs in one launch, a
+ *     longer K in chunks whose partial sums go to the workspace (then a
+ *     second, summing launch).
+ * Every compute unit quantises the activations it consumes, so the work of
+ * the quantiser is repeated once per unit: on MI355X this pays at one token
+ * row (decode 5120 x 6144: 6.57 against 7.29 us for the two launches) and
+ * costs more than the launch it saves from two rows on (see the bench's
+ * fused_step_us).
  *   x  float32 [M][K], 16-byte aligned; codes, wscale, y as for pq2_gemm.
- * M above PQ2_LINEAR_MAX_M returns PQ2_ERR_ARG (use pq2_quantize_act and
- * pq2_gemm with caller-owned q, s, t).
+ *   workspace, workspace_bytes  as for pq2_gemm, sized by
+ *      pq2_linear_workspace_bytes (0 for M <= 2 and for K <= 6144).
+ * PQ2_ERR_ARG when M > PQ2_LINEAR_MAX_M, or when 5 <= M <= 16 and no panel
+ * plan runs this K with this workspace (use pq2_quantize_act and pq2_gemm).
  */
-#define PQ2_LINEAR_MAX_M 4
+#define PQ2_LINEAR_MAX_M 16
 pq2_status pq2_linear(const float *x, const uint8_t *codes, const uint16_t *wscale, float *y,
-                      int64_t M, int64_t N, int64_t K, void *hip_stream);
+                      int64_t M, int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
+
+/*
+ * Bytes of split-K partial sums pq2_linear's plan for this shape writes to
+ * its workspace (0: the plan needs none). Pure host query; 0 for invalid
+ * shapes and M above PQ2_LINEAR_MAX_M.
+ */
+size_t pq2_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The kernel path pq2_linear takes for this shape given a workspace of
+ * workspace_bytes bytes: PQ2_PATH_GEMV or PQ2_PATH_PANEL, whose pq2_gemm_path
+ * result (same workspace) its y equals bit for bit, or -1 where it returns
+ * PQ2_ERR_SHAPE or PQ2_ERR_ARG. Pure host query; enqueues nothing.
+ */
+int pq2_linear_kernel_path(int64_t M, int64_t N, int64_t K, size_t workspace_bytes);
 
 /*
  * The PQ2_PATH_* kernel path pq2_gemm takes for this shape on the current

@@ -101,13 +101,29 @@ def test_quantize_16bit_validation():
 
 def test_linear_validation():
     f = pq2.lib.pq2_linear
-    assert f(None, P, P, P, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, None, P, 1, 8, 128, None) == ERR_NULL
-    assert f(P, P, P, P, 0, 8, 128, None) == ERR_SHAPE
-    assert f(P, P, P, P, 1, 8, 200, None) == ERR_SHAPE
-    assert f(P + 4, P, P, P, 1, 8, 128, None) == ERR_ALIGN     # x needs 16 B
-    assert f(P, P + 8, P, P, 1, 8, 128, None) == ERR_ALIGN     # codes needs 16 B
-    assert f(P, P, P, P, 5, 8, 128, None) == ERR_ARG            # M above PQ2_LINEAR_MAX_M
+    assert f(None, P, P, P, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, None, P, 1, 8, 128, None, 0, None) == ERR_NULL
+    assert f(P, P, P, P, 0, 8, 128, None, 0, None) == ERR_SHAPE
+    assert f(P, P, P, P, 1, 8, 200, None, 0, None) == ERR_SHAPE
+    assert f(P + 4, P, P, P, 1, 8, 128, None, 0, None) == ERR_ALIGN     # x needs 16 B
+    assert f(P, P + 8, P, P, 1, 8, 128, None, 0, None) == ERR_ALIGN     # codes needs 16 B
+    assert f(P, P, P, P, 1, 8, 128, P + 4, 64, None) == ERR_ALIGN       # workspace 16 B
+    assert f(P, P, P, P, 17, 8, 2048, None, 0, None) == ERR_ARG         # M above PQ2_LINEAR_MAX_M
+    assert f(P, P, P, P, 5, 8, 640, None, 0, None) == ERR_ARG           # 5..16 rows: K % 1024 == 0
+
+
+def test_linear_queries():
+    """Pure host queries: no fused kernel above PQ2_LINEAR_MAX_M or for bad
+    shapes; the dot4 GEMV for one or two rows, which needs no workspace."""
+    assert pq2.LINEAR_MAX_M == 16
+    assert pq2.linear_kernel_path(17, 8, 2048, 0) == -1
+    assert pq2.linear_kernel_path(1, 8, 200, 0) == -1
+    assert pq2.linear_workspace_bytes(17, 5120, 17408) == 0
+    assert pq2.linear_workspace_bytes(0, 5120, 17408) == 0
+    for M, N, K in ((1, 5120, 6144), (2, 5120, 17408), (1, 34816, 5120)):
+        assert pq2.linear_kernel_path(M, N, K, 0) == pq2.PATH_GEMV
+        assert pq2.linear_workspace_bytes(M, N, K) == 0
+    assert pq2.linear_kernel_path(5, 8, 640, 1 << 20) == -1   # 5..16 rows need a ring plan
 
 
 def test_group_dots_validation():

@@ -542,29 +542,46 @@ def test_smallest_problem(pq2):
     assert oracle.rel_err(y, yo, tabs) < TOL
 
 
-# ---------------------------------------------------------------- fused quantise + GEMV
+# ---------------------------------------------------------------- fused quantise + GEMM
 
-LINEAR_SHAPES = [(M, N, K) for M in (1, 2, 3, 4)
-                 for (N, K) in ((1, 128), (300, 640), (257, 6144), (65, 8320), (40, 17408))]
+LINEAR_SHAPES = ([(M, N, K) for M in (1, 2, 3, 4)
+                  for (N, K) in ((1, 128), (300, 640), (257, 6144), (65, 8320), (40, 17408))]
+                 + [(M, N, K) for M in (5, 8, 13, 16)
+                    for (N, K) in ((300, 2048), (257, 6144), (33, 3072), (40, 17408),
+                                   (1000, 5120))])
+
+
+def linear_reference(pq2, xd, cd, wd, M, N, K, wsz):
+    """pq2_quantize_act + pq2_gemm_path on the kernel pq2_linear reports for
+    this shape and workspace (same plan, same float arithmetic)."""
+    path = pq2.linear_kernel_path(M, N, K, wsz)
+    assert path in (pq2.PATH_GEMV, pq2.PATH_PANEL)
+    q, s, t = pq2.quantize_act(xd)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    work = torch.empty(max(wsz, 16), dtype=torch.uint8, device="cuda") if wsz else None
+    pq2.pq2_gemm_path(q, s, t, cd, wd, y, path, workspace=work)
+    return y
 
 
 @pytest.mark.parametrize("M,N,K", LINEAR_SHAPES)
 def test_linear_equals_quantize_then_gemm(pq2, M, N, K):
-    """pq2_linear quantises with the quantiser's own arithmetic, so y is bit-identical
-    to pq2_quantize_act + pq2_gemm on the GEMV path, and within tolerance of the oracle."""
+    """pq2_linear quantises with the quantiser's own arithmetic, so y is
+    bit-identical to pq2_quantize_act + pq2_gemm on the kernel path it takes
+    (the dot4 GEMV, or the panel kernel's ring variant with the same K chunks),
+    and within tolerance of the oracle."""
     print(f"linear M={M} N={N} K={K}", flush=True)
     x = synth.activations(M, K, M * 31 + N, outlier_frac=0.01)
     x[0, :128] = 0.0                                   # a zero group (s = 0)
+    x[M - 1, 128:256] *= np.float32(1e-39)             # subnormal x, tiny s
     w = synth.weights(N, K, synth.matrix_seed(M + N))
     xd, cd, wd = dev(x), dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    wsz = pq2.linear_workspace_bytes(M, N, K)
+    expect = pq2.PATH_PANEL if (M >= 3 and K % 1024 == 0 and 2048 <= K <= 18432) else pq2.PATH_GEMV
+    assert pq2.linear_kernel_path(M, N, K, wsz) == expect
     y1 = torch.empty((M, N), dtype=torch.float32, device="cuda")
     pq2.pq2_linear(xd, cd, wd, y1)
-    q, s, t = pq2.quantize_act(xd)
-    y2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    pq2.pq2_gemm(q, s, t, cd, wd, y2)
     yh = host(y1)
-    if M <= 2:       # pq2_gemm takes the GEMV path: identical arithmetic
-        np.testing.assert_array_equal(yh, host(y2))
+    np.testing.assert_array_equal(yh, host(linear_reference(pq2, xd, cd, wd, M, N, K, wsz)))
     yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
     assert oracle.rel_err(yh, yo, tabs) < TOL
     # unit scales, through the float path of the same kernel: exact integers
@@ -572,11 +589,30 @@ def test_linear_equals_quantize_then_gemm(pq2, M, N, K):
     xs = np.repeat(np.float32(127.0) * np.sign(x.reshape(M, -1, G)[:, :, :1]), G, -1)
     xs = np.where(xs == 0, np.float32(127.0), xs).reshape(M, K)   # amax 127 -> s = 1
     xs[:, 1::3] = np.float32(-3.0)
+    xs[:, 2::7] = np.float32(2.5)                      # exact ties: the IEEE division decides
     pq2.pq2_linear(dev(xs), cd, ones_w, y1)
     qo, so, to = oracle.quantize(xs)
     assert (so == 1.0).all()
     D = oracle.group_dots(qo, w.codes)
     np.testing.assert_array_equal(host(y1), D.sum(-1).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K,wsz", [(5, 64, 640, 0), (16, 64, 128, 0), (17, 64, 2048, 0),
+                                      (8, 40, 17408, 0), (8, 40, 17408, 1024)])
+def test_linear_rejects_shapes_without_fused_kernel(pq2, M, N, K, wsz):
+    """5..16 rows need the panel kernel's ring plan (K a multiple of 1024 in
+    [2048, 18432], K chunks within the workspace); above 16 rows there is no
+    fused kernel: PQ2_ERR_ARG, nothing written."""
+    assert pq2.linear_kernel_path(M, N, K, wsz) == -1
+    x = dev(synth.activations(M, K, 5))
+    w = synth.weights(N, K, 5)
+    y = torch.full((M, N), 7.0, device="cuda")
+    work = torch.empty(max(wsz, 16), dtype=torch.uint8, device="cuda") if wsz else None
+    with pytest.raises(pq2.PQ2Error) as e:
+        pq2.pq2_linear(x, dev(w.codes), dev(w.wscale_bits.view(np.int16)), y, workspace=work)
+    assert e.value.status == 5    # PQ2_ERR_ARG
+    torch.cuda.synchronize()
+    assert (host(y) == 7.0).all()
 
 
 # ---------------------------------------------------------------- full workload sizes
@@ -605,34 +641,36 @@ TOKENS_PATH = {"tokens_m32_up": "PATH_PREFILL", "tokens_m64_down": "PATH_PANEL",
                "tokens_m32_oproj": "PATH_PANEL"}
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (4, 300, 17408), (2, 1000, 2048), (3, 70, 128)])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (4, 300, 17408), (2, 1000, 2048), (3, 70, 128),
+                                   (16, 700, 5120), (8, 300, 17408)])
 def test_linear_back_to_back_and_streams(pq2, M, N, K):
     """Calls of pq2_linear issued back to back with no host synchronisation, on
-    one stream and alternating over two, each give y bit-identical to
-    pq2_quantize_act + the GEMV path on their own input; so do a larger call
-    (K doubled, four rows) and a smaller one after it."""
+    one stream and alternating over two (each call with its own workspace),
+    each give y bit-identical to pq2_quantize_act + pq2_gemm on the same
+    kernel path for their own input; so do a larger call (K doubled, four
+    rows) and a smaller one after it."""
     print(f"linear back-to-back M={M} N={N} K={K}", flush=True)
     w = synth.weights(N, K, synth.matrix_seed(K + M))
     cd, wd = dev(w.codes), dev(w.wscale_bits.view(np.int16))
+    wsz = pq2.linear_workspace_bytes(M, N, K)
     streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
-    xs, ys = [], []
+    xs, ys, works = [], [], []
     for i in range(12):
         x = dev(synth.activations(M, K, 100 + i, outlier_frac=0.01))
         y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         xs.append(x)
         ys.append(y)
+        works.append(torch.empty(max(wsz, 16), dtype=torch.uint8, device="cuda") if wsz else None)
     torch.cuda.synchronize()
     for i in range(6):                       # one stream, back to back
-        pq2.pq2_linear(xs[i], cd, wd, ys[i])
+        pq2.pq2_linear(xs[i], cd, wd, ys[i], workspace=works[i])
     for i in range(6, 12):                   # two streams, interleaved
         st = streams[i % 2]
         with torch.cuda.stream(st):
-            pq2.pq2_linear(xs[i], cd, wd, ys[i], stream=st)
+            pq2.pq2_linear(xs[i], cd, wd, ys[i], workspace=works[i], stream=st)
     torch.cuda.synchronize()
     for i in range(12):
-        q, s, t = pq2.quantize_act(xs[i])
-        yr = torch.empty((M, N), dtype=torch.float32, device="cuda")
-        pq2.pq2_gemm_path(q, s, t, cd, wd, yr, pq2.PATH_GEMV)
+        yr = linear_reference(pq2, xs[i], cd, wd, M, N, K, wsz)
         np.testing.assert_array_equal(host(ys[i]), host(yr), err_msg=f"call {i}")
     # a larger call, then a smaller one
     xb = dev(synth.activations(4, 2 * K, 7, outlier_frac=0.01))
@@ -640,18 +678,15 @@ def test_linear_back_to_back_and_streams(pq2, M, N, K):
     cb, wbd = dev(wb.codes), dev(wb.wscale_bits.view(np.int16))
     yb = torch.empty((4, N), dtype=torch.float32, device="cuda")
     pq2.pq2_linear(xb, cb, wbd, yb)
-    pq2.pq2_linear(xs[0], cd, wd, ys[0])
-    q, s, t = pq2.quantize_act(xb)
-    yr = torch.empty((4, N), dtype=torch.float32, device="cuda")
-    pq2.pq2_gemm_path(q, s, t, cb, wbd, yr, pq2.PATH_GEMV)
+    pq2.pq2_linear(xs[0], cd, wd, ys[0], workspace=works[0])
+    yr = linear_reference(pq2, xb, cb, wbd, 4, N, 2 * K, pq2.linear_workspace_bytes(4, N, 2 * K))
     np.testing.assert_array_equal(host(yb), host(yr))
-    q, s, t = pq2.quantize_act(xs[0])
-    yr = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    pq2.pq2_gemm_path(q, s, t, cd, wd, yr, pq2.PATH_GEMV)
+    yr = linear_reference(pq2, xs[0], cd, wd, M, N, K, wsz)
     np.testing.assert_array_equal(host(ys[0]), host(yr))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (2, 17408, 5120), (4, 5120, 17408)])
+@pytest.mark.parametrize("M,N,K", [(1, 5120, 6144), (2, 17408, 5120), (4, 5120, 17408),
+                                   (16, 17408, 5120), (16, 5120, 17408), (8, 6144, 5120)])
 def test_linear_full_size_sampled(pq2, M, N, K):
     """pq2_linear at the decode and small-batch sizes against sampled oracle outputs."""
     print(f"linear full M={M} N={N} K={K}", flush=True)
