@@ -673,20 +673,72 @@ def run_proxy(args, m, torch, pq2):
                               "GEMM; GEMM kernel durations from a kernel trace of this run"}}
 
 
+def layer_read_floor(torch, probes, m, steps=5, trials=5):
+    """The 64-layer step's practical ceiling when every GEMM is its own launch:
+    the step's launches in the step's order on one stream, each replaced by a
+    plain streaming read of that launch's algorithmic bytes (a projection's
+    codes, scales, activations and y; the quantiser's float32 activations),
+    every projection reading its own slice of one buffer as large as the
+    step's weights (so the reads come from HBM), with no arithmetic."""
+    import pq2_synth as synth
+    dev = torch.device("cuda:0")
+    r16 = lambda b: (b + 15) // 16 * 16
+    sizes = []
+    for (n, k) in synth.LAYER_SHAPES:
+        fused = one_launch(m, n, k)
+        sizes.append((r16(linear_bytes(m, n, k) if fused else gemm_bytes(m, n, k)),
+                      0 if fused else r16(4 * m * k)))
+    per_layer = sum(g for g, _ in sizes)
+    buf = torch.empty(per_layer * synth.N_LAYERS, dtype=torch.uint8, device=dev)
+    small = torch.empty(r16(max(q for _, q in sizes) + 16), dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    small.fill_(1)
+    big_blocks = probes.cus * 4
+    launches, off = [], 0
+    for _ in range(synth.N_LAYERS):
+        for g, q in sizes:
+            if q:
+                launches.append((small.data_ptr(), q, max(1, min(big_blocks, q // 32768))))
+            launches.append((buf.data_ptr() + off, g, big_blocks))
+            off += g
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lib, sink = probes.lib, probes.sink.data_ptr()
+
+    def step():
+        for ptr, nb, blocks in launches:
+            probes._ok(lib.pq2_probe_stream_read(ptr, nb, sink, blocks, stream), "stream_read")
+    step()
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps)
+    h = tm.host_ms(step)
+    ms = median([tm.run(step, h) for _ in range(trials)]) / steps
+    total = sum(nb for _, nb, _ in launches)
+    del buf, small
+    return {"ms_per_step": ms, "GB/s": total / (ms * 1e-3) / 1e9, "bytes_per_step": total,
+            "launches_per_step": len(launches)}
+
+
 def run_ceiling(torch):
     """Practical ceilings of one MI355X: a plain streaming read at several
-    sizes (slices cycling through 1 GiB) and the int8 MFMA loop."""
+    sizes (slices cycling through 1 GiB), the 64-layer step's launches as
+    plain reads, the int8 MFMA loop and the exact-epilogue instruction mix."""
     probes = Probes(torch)
     reads = []
     for mib in (8, 24, 64, 256):
         nbytes = mib << 20
         print(f"# stream read {mib} MiB", file=sys.stderr, flush=True)
         reads.append(probes.stream_read(nbytes, 1 << 30, calls=max(4, 800 // mib)))
+    floors = {}
+    for m in (1, 16):
+        print(f"# 64-layer step read floor, M = {m}", file=sys.stderr, flush=True)
+        floors[f"layer64_m{m}"] = layer_read_floor(torch, probes, m)
+        torch.cuda.empty_cache()
     print("# int8 MFMA loop", file=sys.stderr, flush=True)
     mf = probes.mfma_i8()
     print("# int8 MFMA with the float32 epilogue mix", file=sys.stderr, flush=True)
     em = probes.epilogue_mix()
-    return {"ceiling": {"stream_read": reads, "mfma_i8": mf, "epilogue_mix": em,
+    return {"ceiling": {"stream_read": reads, "layer_read_floor": floors, "mfma_i8": mf,
+                        "epilogue_mix": em,
                         "hbm_peak_GB/s": HBM_PEAK_GBS, "i8_peak_TOP/s": I8_PEAK_TOPS}}
 
 
@@ -714,6 +766,12 @@ def extras(args, wl, r, torch, pq2, probes):
                          "frac_hbm_peak": lr["value"] / HBM_PEAK_GBS,
                          "algorithmic_bytes_per_step": lr["config"]["algorithmic_bytes_per_step"],
                          "trial_ms": lr["config"]["trial_ms"]}
+    torch.cuda.empty_cache()
+    print("# extras: layer64 m1 read floor", file=sys.stderr, flush=True)
+    fl = layer_read_floor(torch, probes, 1)
+    out["layer64_m1"]["read_floor_ms"] = fl["ms_per_step"]
+    out["layer64_m1"]["read_floor_launches"] = fl["launches_per_step"]
+    out["layer64_m1"]["step_time_over_read_floor"] = lr["ms_per_step"] / fl["ms_per_step"]
     torch.cuda.empty_cache()
     if r is not None and r["M"] <= 16:
         print("# extras: ceilings", file=sys.stderr, flush=True)
