@@ -151,8 +151,16 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
 
     // x loads of the fused variant (first pass of window kx)
     constexpr int kSlots = kGemvThreads / 32;
+    // groups per slot and pass: kXRound, except in the plans of more than
+    // eight waves with five-chunk batches, where eight rounds of x do not fit
+    // the 168 VGPRs of three waves per SIMD; those plans fix K (G = IB0 * CL / 2
+    // groups) and take exactly the rounds it needs. (Fewer rounds than
+    // kXRound elsewhere measured slower: 6144 x 5120 fused, 6.14 against
+    // 5.72 us.)
+    constexpr int kXNeed = IB0 > 0 ? (MT * IB0 * CL / 2 + kSlots - 1) / kSlots : kXRound;
+    constexpr int kXR = (NW > 8 && IB0 >= 5 && kXNeed < kXRound) ? kXNeed : kXRound;
     const int lane32 = threadIdx.x & 31, slot = threadIdx.x >> 5;
-    float4 xv[kXRound];
+    float4 xv[kXR];
     auto load_x = [&](int64_t kx, int base) __attribute__((always_inline)) {
         const int wkx = (int)((K - kx < window) ? K - kx : window);
         const int wgx = wkx / kGroup, ngx = MT * wgx;
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
         // the last group quantise zeros that are never stored
         const int rounds = (ngx - base + kSlots - 1) / kSlots;
 #pragma unroll
-        for (int i = 0; i < kXRound; ++i) {
+        for (int i = 0; i < kXR; ++i) {
             xv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             // slots past the last group load nothing (see stage_load)
             const int gi = base + slot + kSlots * i;
@@ -225,15 +233,15 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
         int32_t *t_l = reinterpret_cast<int32_t *>(s_l + MT * wg);
         if constexpr (FUSED) {
             // quantise the window's MT x wg groups from x straight into the
-            // LDS layout: 32 lanes per group, kXRound groups per slot and pass
+            // LDS layout: 32 lanes per group, kXR groups per slot and pass
             uint32_t *qw = reinterpret_cast<uint32_t *>(smem);
             const int ngr = MT * wg;
             auto quantize_pass = [&](int base) __attribute__((always_inline)) {
                 // rounds with a group for some slot (uniform, as in load_x): a
-                // block of many waves needs few of the kXRound
+                // block of many waves needs few of the kXR
                 const int rounds = (ngr - base + kSlots - 1) / kSlots;
 #pragma unroll
-                for (int i = 0; i < kXRound; ++i) {
+                for (int i = 0; i < kXR; ++i) {
                     if (i >= rounds) break;
                     const int graw = base + slot + kSlots * i;
                     const float4 xi[1] = {xv[i]};
@@ -254,7 +262,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
             };
             // pass 0 on x loads issued ahead of the first code batch
             quantize_pass(0);
-            for (int base = kSlots * kXRound; base < ngr; base += kSlots * kXRound) {
+            for (int base = kSlots * kXR; base < ngr; base += kSlots * kXR) {
                 load_x(k0, base);
                 quantize_pass(base);
             }
