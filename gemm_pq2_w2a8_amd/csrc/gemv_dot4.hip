@@ -54,9 +54,9 @@
 //    stored.
 //  * The fused variant (pq2_linear) reads float32 x instead of q, s, t: each
 //    block quantises its window in LDS with the quantiser's own arithmetic
-//    (quantize_groups32). The first pass of x loads is issued before the
-//    first code batch (loads complete in issue order for the wait counter),
-//    so the block quantises while its codes are in flight.
+//    (quantize_groups8, 8 lanes per group). The first pass of x loads is
+//    issued before the first code batch (loads complete in issue order for
+//    the wait counter), so the block quantises while its codes are in flight.
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
@@ -76,7 +76,7 @@ __device__ __forceinline__ int token_of(int u, int n) {
 constexpr int kLoadsPerBatch = 6;                 // uint4 code loads per lane per batch
 constexpr int64_t kMaxStage = 40960;              // activations staged per window (all tokens)
 constexpr int64_t kPersistBlocks = 512;           // two blocks per CU
-constexpr int kXRound = 8;                        // groups per 32-lane slot and pass (fused)
+constexpr int kXRound = 2;                        // groups per 8-lane slot and pass (fused)
 
 // NW waves per block (4 by default; 5 to 10 for the one-block-per-CU plans
 // of the decode shapes, see launch_mt), IB0 chunk iterations per batch (0:
@@ -149,33 +149,33 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
         }
     };
 
-    // x loads of the fused variant (first pass of window kx)
-    constexpr int kSlots = kGemvThreads / 32;
-    // groups per slot and pass: kXRound, except in the plans of more than
-    // eight waves with five-chunk batches, where eight rounds of x do not fit
-    // the 168 VGPRs of three waves per SIMD; those plans fix K (G = IB0 * CL / 2
-    // groups) and take exactly the rounds it needs. (Fewer rounds than
-    // kXRound elsewhere measured slower: 6144 x 5120 fused, 6.14 against
-    // 5.72 us.)
+    // x loads of the fused variant (first pass of window kx): 8-lane slots,
+    // one group per slot and round, lane j of a slot loading the group's
+    // activations 16j .. 16j + 15 (quantize_groups8)
+    constexpr int kSlots = kGemvThreads / 8;
+    // rounds per pass: kXRound, or the exact count where the plan fixes K (a
+    // row's whole iteration count in one batch: G = IB0 * CL / 2 groups)
     constexpr int kXNeed = IB0 > 0 ? (MT * IB0 * CL / 2 + kSlots - 1) / kSlots : kXRound;
-    constexpr int kXR = (NW > 8 && IB0 >= 5 && kXNeed < kXRound) ? kXNeed : kXRound;
-    const int lane32 = threadIdx.x & 31, slot = threadIdx.x >> 5;
-    float4 xv[kXR];
+    constexpr int kXR = kXNeed < kXRound ? kXNeed : kXRound;
+    const int lane8 = threadIdx.x & 7, slot = threadIdx.x >> 3;
+    float4 xv[kXR][4];
     auto load_x = [&](int64_t kx, int base) __attribute__((always_inline)) {
         const int wkx = (int)((K - kx < window) ? K - kx : window);
         const int wgx = wkx / kGroup, ngx = MT * wgx;
         // rounds i with a group for some slot (a uniform bound); slots past
-        // the last group quantise zeros that are never stored
+        // the last group load nothing and quantise zeros that are never stored
         const int rounds = (ngx - base + kSlots - 1) / kSlots;
 #pragma unroll
         for (int i = 0; i < kXR; ++i) {
-            xv[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            // slots past the last group load nothing (see stage_load)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[i][e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             const int gi = base + slot + kSlots * i;
             if (i < rounds && gi < ngx) {
                 const int m = token_of<MT>(gi, wgx), gw = gi - m * wgx;
                 const int64_t mc = m < M ? m : M - 1;
-                xv[i] = *reinterpret_cast<const float4 *>(x + mc * K + kx + kGroup * gw + 4 * lane32);
+                const float4 *src = reinterpret_cast<const float4 *>(x + mc * K + kx + kGroup * gw + 16 * lane8);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[i][e] = src[e];
             }
         }
     };
@@ -233,29 +233,29 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
         int32_t *t_l = reinterpret_cast<int32_t *>(s_l + MT * wg);
         if constexpr (FUSED) {
             // quantise the window's MT x wg groups from x straight into the
-            // LDS layout: 32 lanes per group, kXR groups per slot and pass
+            // LDS layout: 8 lanes per group, kXR groups per slot and pass
             uint32_t *qw = reinterpret_cast<uint32_t *>(smem);
             const int ngr = MT * wg;
             auto quantize_pass = [&](int base) __attribute__((always_inline)) {
-                // rounds with a group for some slot (uniform, as in load_x): a
-                // block of many waves needs few of the kXR
+                // rounds with a group for some slot (uniform, as in load_x)
                 const int rounds = (ngr - base + kSlots - 1) / kSlots;
 #pragma unroll
                 for (int i = 0; i < kXR; ++i) {
                     if (i >= rounds) break;
                     const int graw = base + slot + kSlots * i;
-                    const float4 xi[1] = {xv[i]};
-                    uint32_t word[1];
-                    float sc[1];
-                    int sm[1];
-                    quantize_groups32<1>(xi, lane32, word, sc, sm);   // all 32 lanes
+                    uint32_t word[4];
+                    float sc;
+                    int sm;
+                    quantize_groups8(xv[i], word, sc, sm);   // all 8 lanes
                     if (graw < ngr) {
                         const int m = token_of<MT>(graw, wg), gw = graw - m * wg;
-                        const int p = lane32 & 3, j = lane32 >> 2;
-                        qw[((m * 4 + p) * wchunks + 2 * gw + (j >> 2)) * 4 + (j & 3)] = word[0];
-                        if (lane32 == 0) {
-                            s_l[m * wg + gw] = sc[0];
-                            t_l[m * wg + gw] = sm[0];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            qw[((m * 4 + p) * wchunks + 2 * gw + (lane8 >> 2)) * 4 + (lane8 & 3)] =
+                                word[p];
+                        if (lane8 == 0) {
+                            s_l[m * wg + gw] = sc;
+                            t_l[m * wg + gw] = sm;
                         }
                     }
                 }

@@ -235,6 +235,67 @@ __device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lan
     }
 }
 
+// The same quantisation with 8 lanes per group (aligned 8-lane segments):
+// lane j of a segment holds activations 16j .. 16j + 15 of the group as
+// v[i] = x[16j + 4i .. 16j + 4i + 3], i.e. plane positions b = 4j + i with
+// planes 0..3 in .x .y .z .w. Plane p's bytes 32p + 4j .. 32p + 4j + 3 are
+// then this lane's own q at positions 4j .. 4j + 3, so word[p] is the plane
+// word (p, j) with no byte transpose; amax and sum(q) reduce over the 8 lanes
+// (quad permutes and the row half-mirror). Rounding, clamp and the exact
+// fallback are the quant_* helpers, as in quantize_groups32, so q, s and t are
+// identical. A quarter of the lanes per group makes the per-group work (the
+// reductions, the division) four times rarer per activation.
+__device__ __forceinline__ void quantize_groups8(const float4 (&v)[4], uint32_t (&word)[4],
+                                                 float &scale, int &sum) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(int, a))));
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_xor2(__builtin_bit_cast(int, a))));
+    a = fmaxf(a, __builtin_bit_cast(float, dpp_half_mirror(__builtin_bit_cast(int, a))));
+    scale = a / 127.0f;                             // IEEE division
+    const float rc = __builtin_amdgcn_rcpf(scale);
+    const bool tiny = quant_tiny(scale);            // includes s == 0
+    float qf[4][4];                                 // [position i][plane p]
+    bool slow = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float xs[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            bool ok;
+            qf[i][p] = quant_round_fast(xs[p], rc, tiny, ok);
+            slow |= !ok && scale != 0.0f;
+        }
+    }
+    if (__any(slow)) {                              // rare: the IEEE division decides
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float xs[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                bool ok;
+                quant_round_fast(xs[p], rc, tiny, ok);
+                if (!ok && scale != 0.0f) qf[i][p] = rintf(xs[p] / scale);
+            }
+        }
+    }
+    int t = 0;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= ((uint32_t)quant_clamp(qf[i][p], scale) & 0xffu) << (8 * i);
+        word[p] = w;
+        t = dot4(w, 0x01010101u, t);
+    }
+    t += dpp_xor1(t);
+    t += dpp_xor2(t);
+    t += dpp_half_mirror(t);
+    sum = t;
+}
+
 // Buffer resource over [base, base + bytes) (bytes clamped to 32 bits; every
 // offset used is in range by construction, the hardware range check is a
 // second guard: loads beyond the range return zero). Word 3 selects 32-bit
