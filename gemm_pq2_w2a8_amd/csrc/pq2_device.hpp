@@ -101,29 +101,21 @@ __device__ __forceinline__ float segment_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float seg32_max(float a) {
-    a = fmaxf(a, __builtin_bit_cast(float, dpp_xor1(__builtin_bit_cast(int, a))));
-    a = fmaxf(a, __builtin_bit_cast(float, dpp_xor2(__builtin_bit_cast(int, a))));
-    a = fmaxf(a, __builtin_bit_cast(float, dpp_half_mirror(__builtin_bit_cast(int, a))));
-    a = fmaxf(a, __builtin_bit_cast(float, dpp_mirror(__builtin_bit_cast(int, a))));
-    a = fmaxf(a, __builtin_bit_cast(float, swizzle_xor16(__builtin_bit_cast(int, a))));
-    return a;
-}
-
-__device__ __forceinline__ int seg32_sum(int v) {
-    v += dpp_xor1(v);
-    v += dpp_xor2(v);
-    v += dpp_half_mirror(v);
-    v += dpp_mirror(v);
-    v += swizzle_xor16(v);
-    return v;
-}
-
 // Per-element steps of the int8 quantiser, shared by every kernel that
-// quantises activations so that all of them give identical q (the
-// reasoning is given with quantize_groups32 below): the tiny-scale test, the
-// fast rounding of x / s through rc = v_rcp_f32(s) with the flag that says
-// it equals the IEEE quotient's rounding, and the final clamp.
+// quantises activations so that all of them give identical q: the tiny-scale
+// test, the fast rounding of x / s through rc = v_rcp_f32(s) with the flag
+// that says it equals the IEEE quotient's rounding, and the final clamp.
+// s = amax / 127 is the IEEE float32 quotient (the library is built with
+// correctly rounded division and float32 denormals) and q = clamp(rne(fl32(x
+// / s)), -127, 127) the IEEE result as well, through an exact shortcut:
+//   with rc = v_rcp_f32(s) (relative error <= 2^-23) and y = fl32(x * rc),
+//   |y - x/s| <= 127.5 * (2^-23 + 2^-24) < 2^-15.4 and |fl32(x/s) - x/s|
+//   <= 2^-18 (|x / s| <= 127.5), so y and fl32(x/s) are within 2^-15 of each
+//   other; when y is farther than 2^-13 from every half-integer both round
+//   to the same integer and neither is a tie. Otherwise (about 2e-4 of
+//   random inputs), and for scales below 2^-100 (whose reciprocal may
+//   overflow), the IEEE division decides (a wave-uniform branch, taken only
+//   when some lane needs it). s == 0 gives q = 0.
 __device__ __forceinline__ bool quant_tiny(float scale) { return scale < 0x1p-100f; }
 
 __device__ __forceinline__ float quant_round_fast(float x, float rc, bool tiny, bool &ok) {
@@ -137,26 +129,16 @@ __device__ __forceinline__ int quant_clamp(float qf, float scale) {
     return scale == 0.0f ? 0 : (int)fminf(fmaxf(qf, -127.0f), 127.0f);
 }
 
-// Per-128-group int8 quantisation of activations in plane order, shared by
-// the quantise kernel and the fused GEMV so both give identical q, s, t.
-// 32 lanes hold one group (lane b: x[4b .. 4b+3]); amax and the sum of q are
-// reductions over the 32 lanes (exact in any order). s = amax / 127 is the
-// IEEE float32 quotient (the library is built with correctly rounded
-// division and float32 denormals) and q = clamp(rne(fl32(x / s)), -127, 127)
-// the IEEE result as well, through an exact shortcut:
-//   with rc = v_rcp_f32(s) (relative error <= 2^-23) and y = fl32(x * rc),
-//   |y - x/s| <= 127.5 * (2^-23 + 2^-24) < 2^-15.4 and |fl32(x/s) - x/s|
-//   <= 2^-18 (|x / s| <= 127.5), so y and fl32(x/s) are within 2^-15 of each
-//   other; when y is farther than 2^-13 from every half-integer both round
-//   to the same integer and neither is a tie. Otherwise (about 2e-4 of
-//   random inputs), and for scales below 2^-100 (whose reciprocal may
-//   overflow), the IEEE division decides. s == 0 gives q = 0.
-// A 4x4 byte transpose inside each quad (lanes 4j..4j+3: quad broadcasts and
-// byte permutes) leaves lane 4j+p holding the 32-bit plane word (p, j): the
-// group's bytes 32p + 4j .. 32p + 4j + 3.
-// NR groups per 32-lane slot are processed stage by stage, so their latency
-// chains (lane exchanges, divisions) overlap; the exact fallback is a single
-// wave-uniform branch, taken only when some lane needs it.
+// Per-128-group int8 quantisation of activations in plane order, in two lane
+// layouts with the same element arithmetic (the quant_* helpers; amax and
+// sum(q) are exact in any order), so every kernel gives identical q, s, t.
+// 32 lanes per group: lane b holds x[4b .. 4b+3] (plane position b, planes
+// 0..3), amax and the sum of q reduce over the 32 lanes, and a 4x4 byte
+// transpose inside each quad (lanes 4j..4j+3: quad broadcasts and byte
+// permutes) leaves lane 4j+p holding the plane word (p, j): the group's
+// bytes 32p + 4j .. 32p + 4j + 3. NR groups per 32-lane slot are processed
+// stage by stage. Each lane's chain is short (one float4), which suits
+// launches of few groups, where latency rather than issue decides.
 template <int NR>
 __device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lane32,
                                                   uint32_t (&word)[NR], float (&scale)[NR],
@@ -235,16 +217,17 @@ __device__ __forceinline__ void quantize_groups32(const float4 (&v)[NR], int lan
     }
 }
 
-// The same quantisation with 8 lanes per group (aligned 8-lane segments):
-// lane j of a segment holds activations 16j .. 16j + 15 of the group as
+// 8 lanes per group (aligned 8-lane segments): lane j of a segment holds
+// activations 16j .. 16j + 15 of the group as
 // v[i] = x[16j + 4i .. 16j + 4i + 3], i.e. plane positions b = 4j + i with
 // planes 0..3 in .x .y .z .w. Plane p's bytes 32p + 4j .. 32p + 4j + 3 are
 // then this lane's own q at positions 4j .. 4j + 3, so word[p] is the plane
 // word (p, j) with no byte transpose; amax and sum(q) reduce over the 8 lanes
-// (quad permutes and the row half-mirror). Rounding, clamp and the exact
-// fallback are the quant_* helpers, as in quantize_groups32, so q, s and t are
-// identical. A quarter of the lanes per group makes the per-group work (the
-// reductions, the division) four times rarer per activation.
+// (quad permutes and the row half-mirror). Against 32 lanes per group the
+// per-group work -- the reductions, the division -- is four times rarer per
+// activation, which pays where the quantisation's issue is the cost (the
+// fused decode GEMV: 5.74 -> 5.02 us; the quantiser at 4096 x 5120: 20.3 ->
+// 16.7 us).
 __device__ __forceinline__ void quantize_groups8(const float4 (&v)[4], uint32_t (&word)[4],
                                                  float &scale, int &sum) {
     float a = 0.0f;

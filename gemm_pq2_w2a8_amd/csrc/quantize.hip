@@ -8,10 +8,11 @@
 // quantiser (section "Prompt processing: check configuration and launch
 // costs"); the plane layout is from its section "One token at a time".
 //
-// Mapping: 32 lanes per group, lane b loads x[4b .. 4b+3] as one float4 (the
-// 512-byte group is read fully coalesced); quantize_groups32 (shared with the
-// fused GEMV) reduces amax and t over the 32 lanes and leaves lane 4j+s with
-// the 32-bit plane word (s, j), written to byte 32*s + 4*j of the group.
+// Mapping: 32 lanes per group (lane b loads x[4b .. 4b+3]; quantize_groups32
+// leaves lane 4j+p with the plane word (p, j)) for launches of few groups, 8
+// lanes per group (lane j loads x[16j .. 16j+15]; quantize_groups8, shared
+// with the fused GEMV, leaves lane j with the four plane words (p, j)) for
+// many. Each plane word goes to bytes 32*p + 4*j of its group.
 //
 // HBM-bound: 4 bytes read and 1 + 8/128 bytes written per element.
 #include "pq2_device.hpp"
@@ -22,7 +23,6 @@ namespace pq2 {
 namespace {
 
 constexpr int kQuantThreads = 256;
-constexpr int kGroupsPerBlock = kQuantThreads / 32;
 
 // Four activations of one lane as float32: float32 input as is; bfloat16 and
 // binary16 input (FMT 1, 2) widened exactly, so the quantisation is that of
@@ -46,31 +46,74 @@ __device__ __forceinline__ float4 load4(const void *x, int64_t i) {
     }
 }
 
-template <int FMT>
+// LANES = 32 or 8 lanes per group (quantize_groups32 / quantize_groups8).
+template <int FMT, int LANES>
 __global__ __launch_bounds__(kQuantThreads) void quantize_plane_kernel(
     const void *__restrict__ x, int8_t *__restrict__ q, float *__restrict__ s,
     int32_t *__restrict__ t, int64_t MG, int64_t G, int64_t K) {
-    const int lane32 = threadIdx.x & 31;
-    const int64_t grp = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x >> 5);
+    constexpr int kGroupsPerBlock = kQuantThreads / LANES;
+    const int lane = threadIdx.x & (LANES - 1);
+    const int64_t grp = (int64_t)blockIdx.x * kGroupsPerBlock + (threadIdx.x / LANES);
     const bool valid = grp < MG;
-    const int64_t gg = valid ? grp : MG - 1;   // keep every lane in the shuffles
+    const int64_t gg = valid ? grp : MG - 1;   // keep every lane in the lane exchanges
     const int64_t m = gg / G;
     const int64_t g = gg - m * G;
     const int64_t base = m * K + g * kGroup;
 
-    const float4 v[1] = {load4<FMT>(x, base + 4 * lane32)};
-    uint32_t word[1];
-    float sc[1];
-    int sum[1];
-    quantize_groups32<1>(v, lane32, word, sc, sum);
-    const int j = lane32 >> 2;        // output word j of plane sp
-    const int sp = lane32 & 3;
-    if (valid) {
-        *reinterpret_cast<uint32_t *>(q + base + 32 * sp + 4 * j) = word[0];
-        if (lane32 == 0) {
-            s[gg] = sc[0];
-            t[gg] = sum[0];
+    if constexpr (LANES == 32) {
+        const float4 v[1] = {load4<FMT>(x, base + 4 * lane)};
+        uint32_t word[1];
+        float sc[1];
+        int sum[1];
+        quantize_groups32<1>(v, lane, word, sc, sum);
+        if (valid) {
+            // plane word (lane & 3, lane >> 2): bytes 32 (lane & 3) + 4 (lane >> 2)
+            *reinterpret_cast<uint32_t *>(q + base + 32 * (lane & 3) + 4 * (lane >> 2)) = word[0];
+            if (lane == 0) {
+                s[gg] = sc[0];
+                t[gg] = sum[0];
+            }
         }
+    } else {
+        float4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = load4<FMT>(x, base + 16 * lane + 4 * i);
+        uint32_t word[4];
+        float sc;
+        int sum;
+        quantize_groups8(v, word, sc, sum);
+        if (valid) {
+            // plane p, positions 4 lane .. 4 lane + 3: bytes 32 p + 4 lane
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                *reinterpret_cast<uint32_t *>(q + base + 32 * p + 4 * lane) = word[p];
+            if (lane == 0) {
+                s[gg] = sc;
+                t[gg] = sum;
+            }
+        }
+    }
+}
+
+// Lanes per group (MI355X, us per launch, x resident): 32 while a launch has
+// few groups, where each lane's short chain decides (K = 5120: M = 1 1.96
+// against 2.40 with 8 lanes, M = 128 2.46 against 2.80, M = 256 (10240
+// groups) 2.99 against 3.29), 8 from 16384 groups on, where the per-group work
+// is the cost (M = 512 (20480 groups) 3.87 against 4.35; M = 4096 16.7
+// against 20.3).
+constexpr int64_t kQuant8MinGroups = 16384;
+
+template <int FMT>
+void launch_fmt(const void *x, int8_t *q, float *s, int32_t *t, int64_t MG, int64_t G, int64_t K,
+                hipStream_t stream) {
+    if (MG >= kQuant8MinGroups) {
+        const int64_t blocks = (MG + kQuantThreads / 8 - 1) / (kQuantThreads / 8);
+        hipLaunchKernelGGL((quantize_plane_kernel<FMT, 8>), dim3((unsigned)blocks),
+                           dim3(kQuantThreads), 0, stream, x, q, s, t, MG, G, K);
+    } else {
+        const int64_t blocks = (MG + kQuantThreads / 32 - 1) / (kQuantThreads / 32);
+        hipLaunchKernelGGL((quantize_plane_kernel<FMT, 32>), dim3((unsigned)blocks),
+                           dim3(kQuantThreads), 0, stream, x, q, s, t, MG, G, K);
     }
 }
 
@@ -80,16 +123,12 @@ hipError_t launch_quantize(const void *x, int format, int8_t *q, float *s, int32
                            int64_t M, int64_t K, hipStream_t stream) {
     const int64_t G = K / kGroup;
     const int64_t MG = M * G;
-    const int64_t blocks = (MG + kGroupsPerBlock - 1) / kGroupsPerBlock;
     if (format == 1)
-        hipLaunchKernelGGL(quantize_plane_kernel<1>, dim3((unsigned)blocks), dim3(kQuantThreads),
-                           0, stream, x, q, s, t, MG, G, K);
+        launch_fmt<1>(x, q, s, t, MG, G, K, stream);
     else if (format == 2)
-        hipLaunchKernelGGL(quantize_plane_kernel<2>, dim3((unsigned)blocks), dim3(kQuantThreads),
-                           0, stream, x, q, s, t, MG, G, K);
+        launch_fmt<2>(x, q, s, t, MG, G, K, stream);
     else
-        hipLaunchKernelGGL(quantize_plane_kernel<0>, dim3((unsigned)blocks), dim3(kQuantThreads),
-                           0, stream, x, q, s, t, MG, G, K);
+        launch_fmt<0>(x, q, s, t, MG, G, K, stream);
     return hipGetLastError();
 }
 

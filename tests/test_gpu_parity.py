@@ -81,6 +81,16 @@ def edge_rows():
     return x
 
 
+def edge_rows_many():
+    """The edge rows repeated past 16384 groups (the launch then takes 8 lanes
+    per group instead of 32), between rows of random activations."""
+    e = edge_rows()
+    reps = 16384 // (e.shape[0] * e.shape[1] // 128) + 2
+    x = np.tile(e, (reps, 1))
+    x[1::5] = synth.activations(x[1::5].shape[0], x.shape[1], 11, outlier_frac=0.01)
+    return x
+
+
 QUANT_CASES = {
     "tiny": lambda: synth.activations(1, 512, 0),
     "decode": lambda: synth.activations(1, 6144, 0),
@@ -88,6 +98,9 @@ QUANT_CASES = {
     "ragged": lambda: synth.activations(3, 640, 5, outlier_frac=0.01),
     "prefill": lambda: synth.activations(4096, 5120, 0),
     "edge": edge_rows,
+    "edge_many": edge_rows_many,
+    "layouts_boundary": lambda: synth.activations(409, 5120, 3),   # 16360 groups: 32 lanes
+    "layouts_boundary_8": lambda: synth.activations(410, 5120, 3), # 16400 groups: 8 lanes
 }
 
 
@@ -118,7 +131,7 @@ def edge_rows_16(dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
-@pytest.mark.parametrize("case", ["decode", "small_outliers", "ragged", "edge"])
+@pytest.mark.parametrize("case", ["decode", "small_outliers", "ragged", "edge", "prefill"])
 def test_quantize_16bit_bitexact(pq2, dtype, case):
     """bfloat16 / float16 activations: q, s, t bit for bit those the oracle gives
     for the same values widened to float32 (the widening is exact)."""
