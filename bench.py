@@ -60,11 +60,12 @@ def linear_bytes(M, N, K):
 def one_launch(M, N, K):
     """Where the one-launch pq2_linear (quantisation inside the GEMV) measured
     faster than pq2_quantize_act + pq2_gemm on MI355X: one token row with
-    K <= 6144 and N * K <= 2^25 (decode 5120 x 6144: 6.57 against 7.29 us;
-    6144 x 5120: 6.93 against 7.24; the stacked 34816 x 5120 gate and up:
-    14.53 against 14.23; at K = 17408 and from two rows on, quantising in
-    every block costs more than the separate launch). The 64-layer step takes
-    it there; the bench line reports it beside its two-launch step."""
+    K <= 6144 and N * K <= 2^25 (decode 5120 x 6144: 5.07 against 6.57 us).
+    The 64-layer step takes it there: with it on every GEMM of a layer, or
+    on the stacked 34816 x 5120 gate and up too, the step measured slower.
+    From two rows on it is slower than the two launches except on the
+    decode shape (7.21 against 7.53 us at two rows). The bench line reports
+    it beside the two-launch step."""
     return M == 1 and K <= 6144 and N * K <= (1 << 25)
 
 

@@ -245,8 +245,9 @@ pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t,
  *     second, summing launch).
  * Every compute unit quantises the activations it consumes, so the work of
  * the quantiser is repeated once per unit: on MI355X this pays at one token
- * row (decode 5120 x 6144: 6.57 against 7.29 us for the two launches) and
- * costs more than the launch it saves from two rows on (see the bench's
+ * row (decode 5120 x 6144: 5.07 against 6.57 us for the two launches) and
+ * at two rows of that shape (7.21 against 7.53 us), and costs more than the
+ * launch it saves on longer K or from four rows on (see the bench's
  * fused_step_us).
  *   x  float32 [M][K], 16-byte aligned; codes, wscale, y as for pq2_gemm.
  *   workspace, workspace_bytes  as for pq2_gemm, sized by
