@@ -246,9 +246,9 @@ pq2_status pq2_gemm_bf16(const int8_t *q, const float *s, const int32_t *t,
  * Every compute unit quantises the activations it consumes, so the work of
  * the quantiser is repeated once per unit: on MI355X this pays at one token
  * row (decode 5120 x 6144: 5.07 against 6.57 us for the two launches) and
- * at two rows of that shape (7.21 against 7.53 us), and costs more than the
- * launch it saves on longer K or from four rows on (see the bench's
- * fused_step_us).
+ * at two rows of that shape (7.21 against 7.53 us); on the larger shapes
+ * and from four rows on it costs more than the launch it saves (see the
+ * bench's fused_step_us).
  *   x  float32 [M][K], 16-byte aligned; codes, wscale, y as for pq2_gemm.
  *   workspace, workspace_bytes  as for pq2_gemm, sized by
  *      pq2_linear_workspace_bytes (0 for M <= 2 and for K <= 6144).
