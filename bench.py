@@ -336,6 +336,21 @@ class Probes:
         return {"bytes": n16, "us": best[0], "GB/s": n16 / (best[0] * 1e-6) / 1e9,
                 "blocks": best[1], "rotating_bytes": slices * n16}
 
+    def launch_floor(self, calls=400, trials=5):
+        """Time per launch of a one-block kernel that reads 16 bytes, launched
+        back to back: the fixed cost of every launch on this stack (dispatch,
+        the in-order wait for the previous kernel, its cache write-back)."""
+        torch = self.torch
+        buf = torch.ones(16, dtype=torch.uint8, device="cuda:0")
+        stream = torch.cuda.current_stream().cuda_stream
+        tm = Timer(torch, calls)
+
+        def body():
+            self._ok(self.lib.pq2_probe_stream_read(buf.data_ptr(), 16, self.sink.data_ptr(), 1,
+                                                    stream), "stream_read")
+        h = tm.host_ms(body)
+        return median([tm.run(body, h) for _ in range(trials)]) / calls * 1e3
+
     def mfma_i8(self, trials=5):
         torch = self.torch
         stream = torch.cuda.current_stream().cuda_stream
@@ -458,6 +473,16 @@ def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
                bytes_between_reuse=(R - 1) * wbytes if R > 1 else None,
                rotate=R)
     out["kernel_ms"] = out["gemm_ms"]
+    if probes is not None and M <= LINEAR_MAX_M:
+        # the same launches on one matrix, whose bytes then stay in the caches:
+        # what the kernel takes when no byte has to come from HBM
+        def resident():
+            st = gemm(qp, sp, tp, cps[0], wps[0], yp, M, N, K, wkp, wsz, stream)
+            if st:
+                raise pq2.PQ2Error(st)
+        resident()
+        h_res = tm.host_ms(resident)
+        out["resident_gemm_ms"] = per([tm.run(resident, h_res) for _ in range(trials)])
     if sclk and all(v is not None for v in sclk):
         out["sclk_mhz"] = median(sclk)
     if fused:
@@ -506,6 +531,8 @@ def report_gemm(args, wl, r, torch):
            "pq2_gemm_us": r["gemm_ms"] * 1e3}
     if "sclk_mhz" in r:
         cfg["sclk_mhz_during_pq2_gemm"] = r["sclk_mhz"]
+    if "resident_gemm_ms" in r:
+        cfg["pq2_gemm_cache_resident_us"] = r["resident_gemm_ms"] * 1e3
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": r["steps"],
         "warmup": args.warmup, "ms_per_step": r["ms_step"], "higher_is_better": True,
@@ -547,12 +574,10 @@ def layer_step(m, torch, pq2, stream):
     work = torch.empty(max(wsz, 16), dtype=torch.uint8, device=dev)
     wkp = work.data_ptr() if wsz else None
     lib = pq2.lib
-    # one launch (pq2_linear, quantisation inside the GEMV) where that measured
-    # faster than pq2_quantize_act + pq2_gemm on MI355X: one token row with
-    # K <= 6144 and N * K <= 2^25 (6144 x 5120: 6.93 against 7.24 us; 5120 x
-    # 6144: 6.48 against 7.28; the stacked 34816 x 5120 gate and up: 14.53
-    # against 14.23); the two-launch step elsewhere (at K = 17408 and from two
-    # rows on, quantising in every block costs more than the separate launch)
+    # one launch (pq2_linear, quantisation inside the GEMV) where one_launch
+    # says it measured faster; the two-launch step elsewhere (MI355X, M = 1
+    # step: 2.28 ms this way, 2.34 with every projection in one launch, 2.39
+    # with the down projection's as well as the two K <= 6144 ones)
     fused = tuple(one_launch(m, n, k) for (n, k) in synth.LAYER_SHAPES)
     calls = []
     for projs in layers:
@@ -722,7 +747,8 @@ def layer_read_floor(torch, probes, m, steps=5, trials=5):
 def run_ceiling(torch):
     """Practical ceilings of one MI355X: a plain streaming read at several
     sizes (slices cycling through 1 GiB), the 64-layer step's launches as
-    plain reads, the int8 MFMA loop and the exact-epilogue instruction mix."""
+    plain reads, the launch floor, the int8 MFMA loop and the exact-epilogue
+    instruction mix."""
     probes = Probes(torch)
     reads = []
     for mib in (8, 24, 64, 256):
@@ -734,11 +760,14 @@ def run_ceiling(torch):
         print(f"# 64-layer step read floor, M = {m}", file=sys.stderr, flush=True)
         floors[f"layer64_m{m}"] = layer_read_floor(torch, probes, m)
         torch.cuda.empty_cache()
+    print("# launch floor", file=sys.stderr, flush=True)
+    lf = probes.launch_floor()
     print("# int8 MFMA loop", file=sys.stderr, flush=True)
     mf = probes.mfma_i8()
     print("# int8 MFMA with the float32 epilogue mix", file=sys.stderr, flush=True)
     em = probes.epilogue_mix()
-    return {"ceiling": {"stream_read": reads, "layer_read_floor": floors, "mfma_i8": mf,
+    return {"ceiling": {"stream_read": reads, "layer_read_floor": floors, "launch_floor_us": lf,
+                        "mfma_i8": mf,
                         "epilogue_mix": em,
                         "hbm_peak_GB/s": HBM_PEAK_GBS, "i8_peak_TOP/s": I8_PEAK_TOPS}}
 
@@ -780,6 +809,7 @@ def extras(args, wl, r, torch, pq2, probes):
         sr = probes.stream_read(nb, 1 << 30, calls=max(20, min(args.steps, 200)))
         sr["pq2_gemm_time_over_read_time"] = r["kernel_ms"] * 1e3 / sr["us"]
         out["stream_read_same_bytes"] = sr
+        out["launch_floor_us"] = probes.launch_floor()
     out["mfma_i8_loop"] = probes.mfma_i8()
     out["mfma_i8_with_epilogue_mix"] = probes.epilogue_mix()
     return out
