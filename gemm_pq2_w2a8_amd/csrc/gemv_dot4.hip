@@ -78,6 +78,8 @@ constexpr int64_t kMaxStage = 40960;              // activations staged per wind
 constexpr int64_t kPersistBlocks = 512;           // two blocks per CU
 constexpr int kXRound = 2;                        // groups per 8-lane slot and pass (fused)
 
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+
 // NW waves per block (4 by default; 5 to 10 for the one-block-per-CU plans
 // of the decode shapes, see launch_mt), IB0 chunk iterations per batch (0:
 // kLoadsPerBatch / RP; those plans take a row's whole iteration count).
@@ -130,21 +132,54 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
     // (native vectors: copies of the HIP uint4 struct can leave arrays in scratch)
     v4i bufa[IB][RP], bufb[IB][RP];
     uint16_t wsa[IB][RP], wsb[IB][RP];
+    // Byte offsets of this lane's rows (local0 + r * RL) inside a row group's
+    // codes and weight scales. For one token row (not fused) the loads are
+    // buffer loads over the row group: the per-lane part is this fixed offset,
+    // the chunk iteration and window are a wave-uniform offset, so a load
+    // costs no address arithmetic; rows past N lie outside the resource and
+    // read zeros (their sums are never stored). Every offset stays below 2^30
+    // (K <= 2^24, at most 128 rows).
+    int voff_c[RP], voff_w[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+        const int lr = local0 + r * RL;
+        voff_c[r] = lr * (int)(K / 4) + 16 * cs;
+        voff_w[r] = 2 * (lr * (int)G + (cs >> 1));
+    }
     // code chunks of row group rg, window starting at k0, iterations it0..
     // (never predicated: past the window the last chunk is re-read, unused)
     auto load_batch = [&](v4i (&buf)[IB][RP], uint16_t (&wsv)[IB][RP], int64_t rg, int64_t k0,
                           int iters, int it0) __attribute__((always_inline)) {
+        const int64_t rbase = rg * S::ROWS_PER_BLOCK;
+        const int64_t nr = N - rbase < S::ROWS_PER_BLOCK ? N - rbase : S::ROWS_PER_BLOCK;
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + rbase * (K / 4), nr * (K / 4));
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(ws + rbase * G, nr * G * 2);
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-            const int64_t row = rg * S::ROWS_PER_BLOCK + local0 + (int64_t)r * RL;
-            const int64_t rc = row < N ? row : N - 1;
-            const v4i *cp = reinterpret_cast<const v4i *>(codes + rc * (K / 4)) + k0 / 64 + cs;
-            const uint16_t *wp = ws + rc * G + k0 / kGroup;
+            if constexpr (FUSED || MT > 1) {
+                // (the fused variant and two or four token rows measured as
+                // fast or faster with plain loads)
+                const int64_t row = rbase + local0 + (int64_t)r * RL;
+                const int64_t rcl = row < N ? row : N - 1;
+                const v4i *cp = reinterpret_cast<const v4i *>(codes + rcl * (K / 4)) + k0 / 64 + cs;
+                const uint16_t *wp = ws + rcl * G + k0 / kGroup;
 #pragma unroll
-            for (int b = 0; b < IB; ++b) {
-                const int it = min(it0 + b, iters - 1);
-                buf[b][r] = cp[CL * it];
-                if (!DOTS) wsv[b][r] = wp[(cs + CL * it) >> 1];
+                for (int b = 0; b < IB; ++b) {
+                    const int it = min(it0 + b, iters - 1);
+                    buf[b][r] = cp[CL * it];
+                    wsv[b][r] = wp[(cs + CL * it) >> 1];
+                }
+            } else {
+#pragma unroll
+                for (int b = 0; b < IB; ++b) {
+                    const int it = min(it0 + b, iters - 1);
+                    buf[b][r] = __builtin_bit_cast(
+                        v4i, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_c[r],
+                                                                   (int)(k0 / 4) + 16 * CL * it, 0));
+                    if (!DOTS)
+                        wsv[b][r] = __builtin_amdgcn_raw_buffer_load_b16(
+                            rw, voff_w[r], (int)(k0 / 64) + CL * it, 0);
+                }
             }
         }
     };
@@ -298,11 +333,25 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
         const float *s_l = reinterpret_cast<const float *>(smem + 4 * MT * wchunks);
         const int32_t *t_l = reinterpret_cast<const int32_t *>(s_l + MT * wg);
         const int64_t row0 = rg * S::ROWS_PER_BLOCK + local0;
+        // this lane's chunk and group at b = 0; chunk b of the batch is CL * b
+        // chunks and CL / 2 groups further (constant LDS offsets)
+        const int cb = cs + CL * it0;
+        const int32_t *t_b = t_l + (cb >> 1);
+        const float *s_b = s_l + (cb >> 1);
+        // the LDS address of each token's planes at b = 0, opaque to the
+        // compiler: it would otherwise fold the constant b offsets into the
+        // wave-uniform plane offsets and add both to the lane address per chunk
+        lds_v4i *q_b[MT][4];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                q_b[m][p] = (lds_v4i *)smem + (m * 4 + p) * wchunks + cb;
+                asm volatile("" : "+v"(q_b[m][p]));
+            }
 #pragma unroll
         for (int b = 0; b < IB; ++b) {
             if (it0 + b >= iters) break;
-            const int c = cs + CL * (it0 + b);    // chunk within window
-            const int g = c >> 1;                 // group within window
             // the planes of every code word of the RP rows, shared by the tokens
             uint32_t pa0[RP][4], pa1[RP][4], pa2[RP][4], pa3[RP][4];
 #pragma unroll
@@ -328,11 +377,10 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
             for (int m = 0; m < MT; ++m) {
                 v4i qv[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    qv[p] = reinterpret_cast<const v4i *>(smem)[(m * 4 + p) * wchunks + c];
-                const int tg = t_l[m * wg + g];
+                for (int p = 0; p < 4; ++p) qv[p] = q_b[m][p][CL * b];
+                const int tg = t_b[m * wg + (CL / 2) * b];
                 float sg = 0.0f;
-                if (!DOTS) sg = s_l[m * wg + g];
+                if (!DOTS) sg = s_b[m * wg + (CL / 2) * b];
                 uint32_t p0[4], p1[4], p2[4], p3[4];
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
@@ -356,6 +404,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
                     const int dot = half_dot + dpp_xor1(half_dot);  // exact group dot
                     if (DOTS) {
                         const int64_t row = row0 + (int64_t)r * RL;
+                        const int g = (cb >> 1) + (CL / 2) * b;   // group within window
                         if (!h && m < M && row < N) d[(m * N + row) * G + k0 / kGroup + g] = dot;
                     } else {
                         facc[r][m] = fmaf((float)dot, h ? 0.0f : sg * cw[r], facc[r][m]);
