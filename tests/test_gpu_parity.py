@@ -149,8 +149,10 @@ def test_quantize_16bit_bitexact(pq2, dtype, case):
     np.testing.assert_array_equal(host(t), to)
 
 
+# the last three span several LDS windows of one token row (40960 activations):
+# 32 or 2 chunk lanes per row, the windows' offsets in the loads' uniform part
 GEMV_SHAPES = [(1, 128), (7, 384), (64, 512), (300, 640), (33, 2048), (130, 5120), (257, 6144),
-               (65, 8192)]
+               (65, 8192), (33, 45056), (5, 42368), (2, 90112)]
 
 
 @pytest.mark.parametrize("N,K", GEMV_SHAPES)
@@ -320,7 +322,7 @@ PATH_Y = [(1, 3, 300, 1024), (2, 5, 130, 1024), (4, 5, 4100, 2176), (4, 16, 8200
           (4, 8, 300, 8192), (4, 16, 5000, 7168), (4, 5, 700, 17408), (4, 16, 1000, 17408),
           (4, 12, 5120, 18432), (4, 1, 33, 2048), (3, 16, 130, 640), (3, 40, 700, 5120),
           (3, 200, 520, 2048), (4, 17, 300, 2048), (4, 32, 1000, 5120), (4, 48, 700, 17408),
-          (4, 64, 4100, 6144)]
+          (4, 64, 4100, 6144), (1, 1, 33, 45056), (1, 1, 70, 42368)]
 
 
 @pytest.mark.parametrize("path,M,N,K", PATH_Y)
