@@ -129,7 +129,8 @@ def make_layer_set(torch, dev, n_layers, gen):
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl, budget_s=10.0):
-    """The oracle (as is) on a bounded sample of the workload, all host cores."""
+    """The oracle (as is) on a bounded sample of the workload: all host cores
+    for budget_s, then one core for half of that."""
     import oracle
     import pq2_synth as synth
     oracle.build(force=False)
@@ -137,16 +138,20 @@ def cpu_baseline(wl, budget_s=10.0):
     x = synth.activations(wl.m, wl.k, 0, wl.outlier_frac)
     n_mats = min(wl.rotate, 4)
     mats = [synth.weights(wl.n, wl.k, synth.matrix_seed(i), wl.probs) for i in range(n_mats)]
-    calls = 0
-    t0 = time.perf_counter()
-    while True:
-        w = mats[calls % n_mats]
-        oracle.forward(x, w.codes, w.wscale, threads=threads)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_call = el / calls
+
+    def timed(nthreads, budget):
+        calls = 0
+        t0 = time.perf_counter()
+        while True:
+            w = mats[calls % n_mats]
+            oracle.forward(x, w.codes, w.wscale, threads=nthreads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return calls, el
+    calls, el = timed(threads, budget_s)
+    calls1, el1 = timed(1, budget_s / 2)
+    per_call, per_call1 = el / calls, el1 / calls1
     return {
         "value": step_bytes(wl.m, wl.n, wl.k) / per_call / 1e9,
         "unit": "GB/s",
@@ -154,6 +159,8 @@ def cpu_baseline(wl, budget_s=10.0):
         "kind": "oracle",
         "sample": f"{calls} full calls (quantise + all {wl.m}x{wl.n} outputs) over {n_mats} "
                   f"of the workload's matrices, {el:.1f} s, {per_call * 1e3:.1f} ms/call",
+        "one_core_value": step_bytes(wl.m, wl.n, wl.k) / per_call1 / 1e9,
+        "one_core_sample": f"{calls1} calls on one core, {el1:.1f} s, {per_call1 * 1e3:.1f} ms/call",
     }
 
 
@@ -166,17 +173,23 @@ def cpu_baseline_prefill(wl, budget_s=10.0):
     w = synth.weights(wl.n, wl.k, synth.matrix_seed(0), wl.probs)
     q, s, t = oracle.quantize(x)
     rng = np.random.default_rng(0)
-    P = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        mm = rng.integers(0, wl.m, 4096)
-        nn = rng.integers(0, wl.n, 4096)
-        oracle.gemm_f64_sampled(q, s, w.codes, w.wscale, mm, nn, threads=threads)
-        P += 4096
-    el = time.perf_counter() - t0
+
+    def timed(nthreads, budget):
+        P = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget:
+            mm = rng.integers(0, wl.m, 4096)
+            nn = rng.integers(0, wl.n, 4096)
+            oracle.gemm_f64_sampled(q, s, w.codes, w.wscale, mm, nn, threads=nthreads)
+            P += 4096
+        return P, time.perf_counter() - t0
+    P, el = timed(threads, budget_s)
+    P1, el1 = timed(1, budget_s / 2)
     return {"value": 2 * P * wl.k / el / 1e12, "unit": "TOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{P} sampled outputs of the {wl.m}x{wl.n} product, {el:.1f} s"}
+            "sample": f"{P} sampled outputs of the {wl.m}x{wl.n} product, {el:.1f} s",
+            "one_core_value": 2 * P1 * wl.k / el1 / 1e12,
+            "one_core_sample": f"{P1} sampled outputs on one core, {el1:.1f} s"}
 
 
 # ---------------------------------------------------------------- GPU timing

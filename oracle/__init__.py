@@ -79,8 +79,15 @@ def _check_k(K: int) -> None:
         raise ValueError("K must be a positive multiple of 128")
 
 
+_MAX_THREADS = []
+
+
 def max_threads() -> int:
-    return int(_load().oracle_max_threads())
+    """OpenMP's thread count as the process started (read once: a call with
+    threads = n sets OpenMP's count for the calls after it)."""
+    if not _MAX_THREADS:
+        _MAX_THREADS.append(int(_load().oracle_max_threads()))
+    return _MAX_THREADS[0]
 
 
 def half_to_double(bits: int) -> float:
