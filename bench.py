@@ -669,6 +669,27 @@ def proxy_spin_us(m):
     return cycles / 1.5 / 1000.0
 
 
+def power_sampler(stop, out):
+    """(start, end, socket power W, first graphics clock MHz) read with
+    amd-smi, a child process per sample, until stop is set (nothing if it is
+    missing)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    while exe and not stop.is_set():
+        try:
+            t0 = time.perf_counter()
+            r = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True,
+                               text=True, timeout=10)
+            d = json.loads(r.stdout)
+            g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+            out.append((t0, time.perf_counter(), float(g["power"]["socket_power"]["value"]),
+                        float(g["clock"]["gfx_0"]["clk"]["value"])))
+        except (OSError, ValueError, KeyError, IndexError, TypeError,
+                subprocess.SubprocessError):
+            return
+
+
 def run_proxy(args, m, torch, pq2):
     """The 64-layer step with a spin after every GEMM, captured once in a
     HIP graph and replayed back to back for --proxy-seconds. Kernel durations
@@ -694,6 +715,10 @@ def run_proxy(args, m, torch, pq2):
     b = torch.cuda.Event(enable_timing=True)
     g.replay()
     torch.cuda.synchronize()
+    import threading
+    stop, samples = threading.Event(), []
+    sampler = threading.Thread(target=power_sampler, args=(stop, samples), daemon=True)
+    sampler.start()
     replays, t0 = 0, time.perf_counter()
     a.record()
     while time.perf_counter() - t0 < args.proxy_seconds:
@@ -703,11 +728,20 @@ def run_proxy(args, m, torch, pq2):
         torch.cuda.synchronize()
     b.record()
     torch.cuda.synchronize()
+    t1 = time.perf_counter()
     ms = a.elapsed_time(b) / replays
+    stop.set()
+    sampler.join()
+    inside = [(p, c) for (s0, s1, p, c) in samples if s0 >= t0 and s1 <= t1]
+    power = None
+    if inside:
+        power = {"samples": len(inside), "socket_W_median": median([p for p, _ in inside]),
+                 "gfx_MHz_median": median([c for _, c in inside]),
+                 "source": "amd-smi metric -p -c, polled during the replay"}
     return {"proxy": {"workload": f"layer64_m{m}", "M": m, "spin_us_per_gemm": spin_us,
                       "spin_cycles": spin,
                       "gemms_per_step": len(synth.LAYER_SHAPES) * synth.N_LAYERS,
-                      "replays": replays, "ms_per_replay": ms,
+                      "replays": replays, "ms_per_replay": ms, "power": power,
                       "note": "HIP-graph replay of the 64-layer step with a spin after every "
                               "GEMM; GEMM kernel durations from a kernel trace of this run"}}
 
