@@ -54,3 +54,32 @@ def test_bad_counts_are_rejected():
         r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags],
                            capture_output=True, text=True, timeout=120)
         assert r.returncode == 2, flags
+
+
+def test_power_sampler_parses_and_stops(tmp_path, monkeypatch):
+    """The proxy's power sampler reads socket power and the first graphics
+    clock from amd-smi's JSON (a stand-in script here), and returns when the
+    tool's output is not what it expects."""
+    import threading
+    import time
+
+    import bench
+    tool = tmp_path / "amd-smi"
+    tool.write_text("#!/bin/sh\n"
+                    "echo '{\"gpu_data\": [{\"gpu\": 0, \"power\": {\"socket_power\": "
+                    "{\"value\": 321, \"unit\": \"W\"}}, \"clock\": {\"gfx_0\": {\"clk\": "
+                    "{\"value\": 2100, \"unit\": \"MHz\"}}}}]}'\n")
+    tool.chmod(0o755)
+    monkeypatch.setenv("PATH", f"{tmp_path}{os.pathsep}{os.environ['PATH']}")
+    stop, out = threading.Event(), []
+    th = threading.Thread(target=bench.power_sampler, args=(stop, out), daemon=True)
+    th.start()
+    time.sleep(0.5)
+    stop.set()
+    th.join(timeout=20)
+    assert not th.is_alive() and out
+    assert all(p == 321.0 and c == 2100.0 and s0 <= s1 for (s0, s1, p, c) in out)
+    tool.write_text("#!/bin/sh\necho not json\n")
+    stop2, out2 = threading.Event(), []
+    bench.power_sampler(stop2, out2)          # returns at the first bad sample
+    assert out2 == []
