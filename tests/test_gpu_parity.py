@@ -749,6 +749,10 @@ def test_full_size_sampled(pq2, name, M, N, K, probs, outl):
 
 
 @pytest.mark.parametrize("M,N,K,path", [(1, 5120, 6144, 1), (4, 5120, 6144, 1),
+                                        # one row: the persistent plans with several
+                                        # batches per wave and a ragged last row group
+                                        (1, 34821, 5120, 1), (1, 17411, 5120, 1),
+                                        (1, 5123, 17408, 1),
                                         (2, 2048, 17408, 1), (16, 5120, 6144, 2),
                                         (16, 2048, 17408, 2), (256, 1024, 5120, 3),
                                         (16, 4100, 5120, 4), (9, 17408, 8192, 4),
