@@ -60,6 +60,8 @@
 #include "pq2_device.hpp"
 #include "pq2_launch.hpp"
 
+#include <type_traits>
+
 namespace pq2 {
 
 namespace {
@@ -130,8 +132,17 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
 
     // ---------------------------------------------------------------- loads
     // (native vectors: copies of the HIP uint4 struct can leave arrays in scratch)
+    // One row's weight scales for a whole-row batch of five 16-lane chunks
+    // (K = 5120, the four-wave plan): its 40 halves are 20 dwords, which the
+    // row's 16 lanes load in two instructions (lane i: dwords i and 16 + i % 4)
+    // and hand out by lane permutes, instead of five 2-byte loads per lane
+    // (34816 x 5120: 11.4 -> 11.1 us; the six- to ten-wave plans measured
+    // slower this way and keep the 2-byte loads).
+    constexpr bool kCoopWs =
+        MT == 1 && !FUSED && !DOTS && LOG_CL == 4 && IB == 5 && RP == 1 && NW == 4;
+    using WsT = typename std::conditional<kCoopWs, uint32_t, uint16_t>::type;
     v4i bufa[IB][RP], bufb[IB][RP];
-    uint16_t wsa[IB][RP], wsb[IB][RP];
+    WsT wsa[IB][RP], wsb[IB][RP];
     // Byte offsets of this lane's rows (local0 + r * RL) inside a row group's
     // codes and weight scales. For one token row (not fused) the loads are
     // buffer loads over the row group: the per-lane part is this fixed offset,
@@ -148,7 +159,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
     }
     // code chunks of row group rg, window starting at k0, iterations it0..
     // (never predicated: past the window the last chunk is re-read, unused)
-    auto load_batch = [&](v4i (&buf)[IB][RP], uint16_t (&wsv)[IB][RP], int64_t rg, int64_t k0,
+    auto load_batch = [&](v4i (&buf)[IB][RP], WsT (&wsv)[IB][RP], int64_t rg, int64_t k0,
                           int iters, int it0) __attribute__((always_inline)) {
         const int64_t rbase = rg * S::ROWS_PER_BLOCK;
         const int64_t nr = N - rbase < S::ROWS_PER_BLOCK ? N - rbase : S::ROWS_PER_BLOCK;
@@ -170,13 +181,21 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
                     wsv[b][r] = wp[(cs + CL * it) >> 1];
                 }
             } else {
+                if constexpr (kCoopWs) {
+                    // (this plan runs for K = 5120 only: one batch per row, it0 = 0)
+                    const int sb = (int)(k0 / 64) + CL * it0;
+                    const int rowoff = 2 * local0 * (int)G;
+                    wsv[0][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, rowoff + 4 * cs, sb, 0);
+                    wsv[1][0] = __builtin_amdgcn_raw_buffer_load_b32(rw, rowoff + 4 * (16 + (cs & 3)),
+                                                                     sb, 0);
+                }
 #pragma unroll
                 for (int b = 0; b < IB; ++b) {
                     const int it = min(it0 + b, iters - 1);
                     buf[b][r] = __builtin_bit_cast(
                         v4i, __builtin_amdgcn_raw_buffer_load_b128(rc, voff_c[r],
                                                                    (int)(k0 / 4) + 16 * CL * it, 0));
-                    if (!DOTS)
+                    if (!DOTS && !kCoopWs)
                         wsv[b][r] = __builtin_amdgcn_raw_buffer_load_b16(
                             rw, voff_w[r], (int)(k0 / 64) + CL * it, 0);
                 }
@@ -325,7 +344,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
     };
 
     // ---------------------------------------------------------------- compute
-    auto compute_batch = [&](const v4i (&buf)[IB][RP], const uint16_t (&wsv)[IB][RP],
+    auto compute_batch = [&](const v4i (&buf)[IB][RP], const WsT (&wsv)[IB][RP],
                              int64_t rg, int64_t k0, int wk, int it0) __attribute__((always_inline)) {
         const int wg = wk / kGroup;
         const int wchunks = wk / 64;
@@ -371,7 +390,17 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
             float cw[RP];
             if (!DOTS) {
 #pragma unroll
-                for (int r = 0; r < RP; ++r) cw[r] = half_bits_to_float(wsv[b][r]);
+                for (int r = 0; r < RP; ++r) {
+                    if constexpr (kCoopWs) {
+                        // half (cs >> 1) + 8 b of the row's batch: dword (cs >> 2) + 4 b
+                        const int src = rs * 16 + (b < 4 ? 4 * b : 0) + (cs >> 2);
+                        const uint32_t dw = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                            4 * src, (int)(b < 4 ? wsv[0][0] : wsv[1][0]));
+                        cw[r] = half_bits_to_float((uint16_t)(dw >> (16 * ((cs >> 1) & 1))));
+                    } else {
+                        cw[r] = half_bits_to_float(wsv[b][r]);
+                    }
+                }
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
