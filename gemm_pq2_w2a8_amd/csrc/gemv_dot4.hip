@@ -34,7 +34,10 @@
 //  * Memory-level parallelism: a lane issues the code loads (and the weight
 //    scale of each chunk's group) of IB chunk iterations x RP rows at once
 //    (one batch); the next batch -- of the same row group or the next one --
-//    is in flight while the current one is computed. The staging loads go
+//    is in flight while the current one is computed. For one token row they
+//    are buffer loads with a fixed per-lane offset (no address arithmetic
+//    per load); the four-wave K = 5120 plan loads a row's scales together
+//    and hands them out by lane permutes. The staging loads go
 //    out first and the first batch right behind them, in one memory round
 //    trip; the block computes on each code word as it arrives. Six loads
 //    per batch: the decode shapes' rows then split into whole batches
@@ -131,7 +134,6 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
         for (int m = 0; m < MT; ++m) facc[r][m] = 0.0f;
 
     // ---------------------------------------------------------------- loads
-    // (native vectors: copies of the HIP uint4 struct can leave arrays in scratch)
     // One row's weight scales for a whole-row batch of five 16-lane chunks
     // (K = 5120, the four-wave plan): its 40 halves are 20 dwords, which the
     // row's 16 lanes load in two instructions (lane i: dwords i and 16 + i % 4)
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(NW * kWave) void gemv_dot4_kernel(
     constexpr bool kCoopWs =
         MT == 1 && !FUSED && !DOTS && LOG_CL == 4 && IB == 5 && RP == 1 && NW == 4;
     using WsT = typename std::conditional<kCoopWs, uint32_t, uint16_t>::type;
+    // (native vectors: copies of the HIP uint4 struct can leave arrays in scratch)
     v4i bufa[IB][RP], bufb[IB][RP];
     WsT wsa[IB][RP], wsb[IB][RP];
     // Byte offsets of this lane's rows (local0 + r * RL) inside a row group's
