@@ -453,6 +453,11 @@ def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
         if st:
             raise pq2.PQ2Error(st)
 
+    def quant_only():
+        st = quant(xp, qp, sp, tp, M, K, stream)
+        if st:
+            raise pq2.PQ2Error(st)
+
     for _ in range(args.warmup):
         step()
         if fused:
@@ -486,6 +491,9 @@ def run_gemm(args, wl, torch, pq2, steps, trials, probes=None):
                bytes_between_reuse=(R - 1) * wbytes if R > 1 else None,
                rotate=R)
     out["kernel_ms"] = out["gemm_ms"]
+    # the quantiser alone (K1), back to back on the same activations
+    h_quant = tm.host_ms(quant_only)
+    out["quant_ms"] = per([tm.run(quant_only, h_quant) for _ in range(trials)])
     if probes is not None and M <= LINEAR_MAX_M:
         # the same launches on one matrix, whose bytes then stay in the caches:
         # what the kernel takes when no byte has to come from HBM
@@ -541,7 +549,8 @@ def report_gemm(args, wl, r, torch):
            "trial_step_us": [round(v, 3) for v in r["trial_step_us"]],
            "trial_pq2_gemm_us": [round(v, 3) for v in r["trial_gemm_us"]],
            "host_enqueue_ms": r["host_enqueue_ms"],
-           "pq2_gemm_us": r["gemm_ms"] * 1e3}
+           "pq2_gemm_us": r["gemm_ms"] * 1e3,
+           "pq2_quantize_act_us": r["quant_ms"] * 1e3}
     if "sclk_mhz" in r:
         cfg["sclk_mhz_during_pq2_gemm"] = r["sclk_mhz"]
     if "resident_gemm_ms" in r:
