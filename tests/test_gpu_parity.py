@@ -508,6 +508,47 @@ def test_random_shapes_auto_path(pq2, M, N, K):
     assert oracle.rel_err(host(y), yo, tabs) < TOL
 
 
+def random_gemv_shapes(seed, count=16, budget=2e8):
+    """One or two token rows: log-uniform N in [1, 40000], K = 128 g with g in
+    [1, 512] (up to two LDS windows of one row), at most `budget` multiply-adds."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        M = int(rng.integers(1, 3))
+        N = int(np.exp(rng.uniform(0, np.log(40000))))
+        K = 128 * int(rng.integers(1, 513))
+        if M * N * K <= budget:
+            out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", random_gemv_shapes(23))
+def test_random_gemv_shapes(pq2, M, N, K):
+    """Seeded random one- and two-row shapes through pq2_gemm's own kernel choice
+    (every GEMV launch plan: persistent and windowed, one block or two per CU,
+    ragged row groups): exact group dots, y within tolerance, and pq2_linear
+    identical to quantise + pq2_gemm."""
+    print(f"random gemv M={M} N={N} K={K} path={pq2.gemm_kernel_path(M, N, K)}", flush=True)
+    x = synth.activations(M, K, M * 11 + N, outlier_frac=0.01)
+    w = synth.weights(N, K, synth.matrix_seed(N * 5 + K))
+    qo, so, to = oracle.quantize(x)
+    qd, td, cd = dev(oracle.plane_order(qo)), dev(to), dev(w.codes)
+    wd = dev(w.wscale_bits.view(np.int16))
+    d = torch.empty((M, N, K // G), dtype=torch.int32, device="cuda")
+    pq2.pq2_gemm_group_dots(qd, td, cd, d)
+    np.testing.assert_array_equal(host(d), oracle.group_dots(qo, w.codes))
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_gemm(qd, dev(so), td, cd, wd, y)
+    yo, tabs, _ = oracle.forward(x, w.codes, w.wscale)
+    assert oracle.rel_err(host(y), yo, tabs) < TOL
+    y2 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    q, s_, t = pq2.quantize_act(dev(x))
+    pq2.pq2_gemm(q, s_, t, cd, wd, y2)
+    y3 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    pq2.pq2_linear(dev(x), cd, wd, y3)
+    np.testing.assert_array_equal(host(y3), host(y2))
+
+
 def test_tiny_workload(pq2):
     wl = synth.tiny()
     w = synth.weights(wl.n, wl.k, 0)
